@@ -1,0 +1,145 @@
+"""CPU oracle for paged decode attention (test infrastructure).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product (``paged_kv_cache_58_amd``)
+never does, and this package imports nothing from the product.
+
+The arithmetic lives in ``pa_oracle.c`` (plain C, double precision, OpenMP over
+(sequence, head)); this file only builds and calls it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH) or (
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                        "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def load_library(path: str):
+    """ctypes handle with argument types set, for liboracle.so or a rebuilt copy."""
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    lib.oracle_decode.restype = I
+    lib.oracle_decode.argtypes = [P, P, P, P, P, P, ctypes.c_double, I, I, I, I, I,
+                                  I, I, I, P, I, I]
+    lib.oracle_append.restype = I
+    lib.oracle_append.argtypes = [P, P, P, ctypes.c_int64, P, ctypes.c_int64, P, I, I,
+                                  I, I, I, I, I]
+    return lib
+
+
+def _load(lib=None):
+    global _lib
+    if lib is not None:
+        return lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or (
+                os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+            build(force=True)
+        _lib = load_library(_LIB_PATH)
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return 0
+    if a.dtype == np.uint16:
+        return 1
+    raise TypeError(f"oracle takes float32 or bf16 bit patterns (uint16), got {a.dtype}")
+
+
+def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: Optional[np.ndarray],
+           block_tables: np.ndarray, context_lens: np.ndarray, scale: float,
+           head_dim_v: Optional[int] = None, pairs: Optional[Sequence] = None,
+           threads: Optional[int] = None, lib=None) -> np.ndarray:
+    """Attention output in float64, shape [num_seqs, Hq, dv].
+
+    q [B, Hq, dk]; caches [num_blocks, bs, Hkv, d]; v_cache None = latent mode,
+    where V is the first ``head_dim_v`` values of each K row.  With ``pairs``
+    (an iterable of (b, h)) only those rows are computed; the rest stay NaN.
+    """
+    lib = _load(lib)
+    q = np.ascontiguousarray(q)
+    k_cache = np.ascontiguousarray(k_cache)
+    dtype = _dtype_code(q)
+    assert _dtype_code(k_cache) == dtype
+    if v_cache is not None:
+        v_cache = np.ascontiguousarray(v_cache)
+        assert _dtype_code(v_cache) == dtype
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    B, Hq, dk = q.shape
+    nb, bs, Hkv, dk2 = k_cache.shape
+    assert dk2 == dk
+    if v_cache is not None:
+        dv = v_cache.shape[3]
+    else:
+        dv = dk if head_dim_v is None else int(head_dim_v)
+    out = np.full((B, Hq, dv), np.nan, dtype=np.float64)
+    if pairs is not None:
+        pr = np.ascontiguousarray(np.asarray(list(pairs), dtype=np.int32).reshape(-1, 2))
+        n_pairs = pr.shape[0]
+    else:
+        pr, n_pairs = None, 0
+    n_threads = default_threads() if threads is None else int(threads)
+    rc = lib.oracle_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt),
+                           _ptr(cl), float(scale), B, Hq, Hkv, dk, dv, bs, bt.shape[1],
+                           dtype, _ptr(pr), n_pairs, n_threads)
+    if rc != 0:
+        raise RuntimeError(f"oracle_decode failed with code {rc}")
+    return out
+
+
+def decode_workload(w, pairs=None, threads=None, context_lens=None, lib=None) -> np.ndarray:
+    """Oracle decode over a ``workloads.Workload`` (optionally other lengths)."""
+    cl = w.context_lens if context_lens is None else context_lens
+    return decode(w.q, w.k_cache, w.v_cache, w.block_tables, cl, w.scale,
+                  head_dim_v=w.spec.head_dim_v, pairs=pairs, threads=threads, lib=lib)
+
+
+def append(k_cache: np.ndarray, v_cache: Optional[np.ndarray], k: np.ndarray,
+           v: Optional[np.ndarray], slot_mapping: np.ndarray, lib=None) -> None:
+    """In-place byte copy of each token's k (and v) row into its slot."""
+    lib = _load(lib)
+    assert k_cache.flags.c_contiguous and (v_cache is None or v_cache.flags.c_contiguous)
+    nb, bs, Hkv, dk = k_cache.shape
+    dv = 0 if v_cache is None else v_cache.shape[3]
+    elt = k_cache.dtype.itemsize
+    k2 = np.ascontiguousarray(k).reshape(k.shape[0], -1)
+    v2 = None if v is None else np.ascontiguousarray(v).reshape(v.shape[0], -1)
+    sm = np.ascontiguousarray(slot_mapping, dtype=np.int32)
+    rc = lib.oracle_append(_ptr(k_cache), _ptr(v_cache), _ptr(k2), k2.shape[1], _ptr(v2),
+                           0 if v2 is None else v2.shape[1], _ptr(sm), sm.shape[0], nb, bs,
+                           Hkv, dk, dv, elt)
+    if rc != 0:
+        raise RuntimeError(f"oracle_append failed with code {rc}")
