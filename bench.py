@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged decode hot path on one MI355X.
+
+A step is one pass of the whole hot path over one batch: pa_cache_append of
+each sequence's new token through the slot mapping, then pa_decode of every
+sequence over its context including that token.  Inputs are seeded synthetic
+data of the named workload, resident in HBM before timing starts.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+METRIC = "paged decode attention KV-read GB/s (% of HBM peak) + decode tokens/s"
+WORKLOAD_TEXT = {
+    "c1": "tiny paged decode fp32: 4 seqs ctx {17,64,100,255}, 4 q / 2 kv heads, d 64, block 16",
+    "c2": "7B-style MHA decode layer bf16: batch 32, 32 q = 32 kv heads, d 128, block 16, "
+          "ctx U[512,4096]",
+    "c3": "Llama-3-70B-style GQA decode layer bf16: batch 100, 64 q / 8 kv heads, d 128, "
+          "block 16, ctx U[1024,8192], shuffled blocks",
+    "c4": "long-context GQA decode bf16: batch 4 x ctx 131072, 64 q / 8 kv heads, d 128, block 16",
+    "c5": "MLA-style latent decode bf16: batch 64, 128 heads over one 576-dim latent "
+          "(V = first 512), block 64, ctx U[2048,8192]",
+}
+KERNEL_SOURCES = ["grouped_decode.hip", "latent_decode.hip", "append.hip", "plan.cpp"]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_58_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(cfg: str, decode_bytes: int):
+    """HBM traffic per decode from committed rocprofv3 --pmc summaries, or None
+    when they are missing or were taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{cfg}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_decode")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c3", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode path shards by KV head or sequence with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_58_amd as pa
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    spec = workloads.CONFIGS[args.config]
+
+    t0 = time.time()
+    w = workloads.make_workload(args.config)
+    log(f"[bench] generated {args.config} in {time.time() - t0:.1f}s: "
+        f"{w.num_blocks} blocks, sum ctx {int(w.context_lens.sum())}")
+
+    def to_dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    q, kc, vc = to_dev(w.q), to_dev(w.k_cache), to_dev(w.v_cache)
+    k_new, v_new = to_dev(w.k_new), to_dev(w.v_new)
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    L1 = (w.context_lens + 1).astype(np.int32)  # context after the append
+    cl = torch.from_numpy(L1).to(dev)
+    sm = torch.from_numpy(w.slot_mapping).to(dev)
+    ws = pa.alloc_workspace(q, kc, bt, head_dim_v=spec.head_dim_v)
+    out = torch.empty((spec.num_seqs, spec.num_q_heads, spec.head_dim_v), dtype=q.dtype,
+                      device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        pa.cache_append(kc, vc, k_new, v_new, sm)
+        pa.decode(out, q, kc, vc, bt, cl, w.scale, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: K steps; events on torch's current stream, which is the
+    # stream the binding hands to the library.
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(K):
+        ev[i][0].record()
+        pa.cache_append(kc, vc, k_new, v_new, sm)
+        ev[i][1].record()
+        pa.decode(out, q, kc, vc, bt, cl, w.scale, ws)
+        ev[i][2].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+    t_append = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    t_decode = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    ms_per_step = total_ms / K
+
+    # accounting over the context actually attended (ctx + 1)
+    w_after = workloads.Workload(**{**w.__dict__, "context_lens": L1})
+    decode_bytes = workloads.algorithmic_bytes(w_after)
+    append_bytes = workloads.append_bytes(w)
+    flops = workloads.algorithmic_flops(w_after)
+    step_bytes = decode_bytes + append_bytes
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    dec_ms = float(np.mean(t_decode))
+    achieved = decode_bytes / (dec_ms * 1e-3) / 1e9
+    log(f"[bench] {K} steps: {ms_per_step * 1e3:.1f} us/step (append {np.mean(t_append) * 1e3:.1f}"
+        f" us, decode {dec_ms * 1e3:.1f} us); decode {achieved:.0f} GB/s = "
+        f"{achieved / HBM_PEAK_GBS:.1%} of HBM peak")
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {args.copy_probe_mib} MiB read + written once")
+        del src, dst
+
+    # correctness of the timed output against the oracle (also the CPU leg)
+    import oracle
+
+    got = out.float().cpu().numpy().astype(np.float64)
+    hk = w.k_cache.copy()
+    hv = None if w.v_cache is None else w.v_cache.copy()
+    oracle.append(hk, hv, w.k_new, w.v_new, w.slot_mapping)
+    cpu = None
+    if args.no_cpu_baseline:
+        rng = np.random.default_rng(0)
+        rows = [(int(b), int(h)) for b, h in zip(rng.integers(0, spec.num_seqs, 128),
+                                                 rng.integers(0, spec.num_q_heads, 128))]
+        ref = oracle.decode(w.q, hk, hv, w.block_tables, L1, w.scale, pairs=rows,
+                            head_dim_v=spec.head_dim_v)
+        sel = np.array(rows)
+        d = np.abs(got[sel[:, 0], sel[:, 1]] - ref[sel[:, 0], sel[:, 1]])
+    else:
+        threads = oracle.default_threads()
+        t_c = time.perf_counter()
+        ref = oracle.decode(w.q, hk, hv, w.block_tables, L1, w.scale, threads=threads,
+                            head_dim_v=spec.head_dim_v)
+        cpu_s = time.perf_counter() - t_c
+        d = np.abs(got - ref)
+        cpu = {"value": round(decode_bytes / cpu_s / 1e9, 3), "unit": "GB/s",
+               "cores": threads, "kind": "oracle",
+               "sample": f"one full decode of the {args.config} batch "
+                         f"({spec.num_seqs} seqs x {spec.num_q_heads} heads), fp64, "
+                         f"{cpu_s:.2f} s wall",
+               "tokens_per_s": round(spec.num_seqs / cpu_s, 3)}
+        log(f"[bench] oracle: {cpu_s:.2f}s on {threads} threads")
+    max_err = float(d.max())
+
+    traffic = load_traffic(args.config, decode_bytes)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[args.config], "name": spec.name,
+                   "global_batch": spec.num_seqs, "seq_len": int(L1.max()),
+                   "mean_context": float(L1.mean()), "parallelism": "single GPU"},
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "decode_tokens_per_s": round(spec.num_seqs / (ms_per_step * 1e-3), 1),
+        "us_append": round(float(np.mean(t_append)) * 1e3, 2),
+        "us_decode": round(dec_ms * 1e3, 2),
+        "us_decode_p10_p90": [round(float(np.percentile(t_decode, 10)) * 1e3, 2),
+                              round(float(np.percentile(t_decode, 90)) * 1e3, 2)],
+        "decode_tflops": round(flops / (dec_ms * 1e-3) / 1e12, 3),
+        "roofline": {"bound": "hbm", "kernel": "pa_decode (partition + log-sum-exp reduce)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": decode_bytes},
+        "cpu_baseline": cpu,
+        "max_abs_err_vs_oracle": max_err,
+        "wall_s_timed": round(wall, 4),
+    }
+    print(json.dumps(result), flush=True)
+    tol = 2e-3 if spec.dtype == "f32" else 1.5e-2
+    if not max_err <= tol:
+        log(f"[bench] PARITY FAILURE: max |delta| {max_err} > {tol}")
+        return 1
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,163 @@
+/*
+ * pa.h — C ABI of libpa.so: decode-phase attention over a paged KV cache on
+ * AMD Instinct MI355X (gfx950), plus the slot-mapped append that fills it.
+ *
+ * The operations follow the pages this library is built from:
+ *
+ *  - The KV cache is a pool of fixed-size blocks ("pages" of block_size
+ *    tokens) that may sit anywhere in device memory; each sequence reaches
+ *    its tokens through a block table mapping logical block index ->
+ *    physical block ("PagedAttention" in "Optimisation de l'inférence";
+ *    "PagedAttention KV cache comme mémoire virtuelle" in "Cache KV,
+ *    attention et optimisation de l'inference").
+ *  - One layer's cache is a tensor [num_blocks, block_size, num_kv_heads,
+ *    head_dim], one for K and one for V (the pool of "Implémentation du
+ *    cache" in the nano-vLLM article, sliced per layer).
+ *  - New K/V rows are written through a slot mapping, slot = physical block *
+ *    block_size + offset, with -1 meaning "skip this token" ("Écriture dans
+ *    le cache", same article).
+ *  - Decode attention is one query token per sequence attending to all of its
+ *    cached tokens: O = softmax(q K^T * scale) V, max-subtracted, with no mask
+ *    ("Étape 2: Attention avec KV Cache", "Optimisation de l'inférence"),
+ *    where query head h reads KV head h / (num_q_heads / num_kv_heads)
+ *    (grouped-query attention, CS336 lecture 10 notes, "核心概念与定义").
+ *  - Latent mode (v_cache == NULL): one cached 576-wide latent row per token
+ *    serves as the key, and its first head_dim_v = 512 values serve as the
+ *    value (the MLA bullet of the same notes: 512 latent + 64 RoPE dims).
+ *
+ * Conventions for every call:
+ *  - All array pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or keeps them after returning.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    enqueue work on it; they never synchronise and never read device arrays
+ *    from the host, so slot_mapping, block_tables and context_lens are
+ *    trusted (see "Undefined" below).
+ *  - Errors: host-checkable faults return a status and enqueue nothing.
+ *    pa_last_error() then holds a message for the calling thread.  A failed
+ *    kernel launch returns PA_ERR_HIP.  No call prints or throws.
+ *  - Undefined (not checked, the contract is the caller's): a slot or block id
+ *    outside the pool, a context longer than max_blocks_per_seq * block_size,
+ *    duplicate non-negative slots in one append, negative context lengths.
+ *  - Results are deterministic: no atomics, bitwise identical run to run and
+ *    independent of where the physical blocks sit in the pool.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_NULL = 1,        /* a required pointer is NULL */
+    PA_ERR_SHAPE = 2,       /* sizes inconsistent or out of range */
+    PA_ERR_DTYPE = 3,       /* unknown dtype */
+    PA_ERR_UNSUPPORTED = 4, /* valid but outside the shapes this build runs */
+    PA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
+    PA_ERR_HIP = 6,         /* the HIP runtime reported an error */
+    PA_ERR_ALIGN = 7        /* a pointer or stride breaks the 16-byte alignment rule */
+} pa_status;
+
+typedef enum pa_dtype {
+    PA_F32 = 0,  /* IEEE binary32 */
+    PA_BF16 = 1  /* bfloat16 (upper 16 bits of binary32), round-to-nearest-even */
+} pa_dtype;
+
+/*
+ * pa_cache_append — write each new token's K (and V) row into its cache slot.
+ *
+ * For i in [0, num_tokens): s = slot_mapping[i]; if s == -1 the token is
+ * skipped, otherwise row s of k_cache viewed as [num_blocks * block_size,
+ * num_kv_heads * head_dim_k] becomes a bitwise copy of k[i], and likewise for
+ * v_cache / v with head_dim_v.  No other byte of either cache changes.
+ *
+ *   k_cache, v_cache  [num_blocks, block_size, num_kv_heads, head_dim_{k,v}],
+ *                     contiguous, element type `dtype`.  v_cache == NULL
+ *                     selects latent mode: only k is written, and v must be NULL.
+ *   k, v              token i's row starts at element i * {k,v}_token_stride;
+ *                     the num_kv_heads * head_dim elements of a row are
+ *                     contiguous.  Strides are in elements, >= the row length.
+ *   slot_mapping      int32 [num_tokens]; -1 = skip.  Non-negative slots must be
+ *                     distinct and < num_blocks * block_size.
+ *   dtype             element type of k, v and both caches (the copy never
+ *                     converts).
+ * num_tokens == 0 is a no-op.  Returns PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE
+ * or PA_ERR_HIP as described above.
+ */
+pa_status pa_cache_append(void *k_cache, void *v_cache,
+                          const void *k, int64_t k_token_stride,
+                          const void *v, int64_t v_token_stride,
+                          const int32_t *slot_mapping, int32_t num_tokens,
+                          int32_t num_blocks, int32_t block_size,
+                          int32_t num_kv_heads, int32_t head_dim_k,
+                          int32_t head_dim_v, pa_dtype dtype, void *stream);
+
+/*
+ * pa_decode_workspace_size — bytes of device workspace pa_decode needs for
+ * these sizes (the split-context partial results: an fp32 accumulator of
+ * head_dim_v values plus a running max and a running sum per sequence, query
+ * head and context partition).  Returns 0 when the sizes are not valid.
+ * pa_decode must be called with the same sizes.
+ */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim_k,
+                                int32_t head_dim_v, int32_t block_size,
+                                int32_t max_blocks_per_seq);
+
+/*
+ * pa_decode — decode attention for one query token per sequence.
+ *
+ * For b < num_seqs, h < num_q_heads, with G = num_q_heads / num_kv_heads,
+ * g = h / G and L = context_lens[b]: token t < L sits at row t % block_size of
+ * physical block block_tables[b * max_blocks_per_seq + t / block_size];
+ *   s_t = scale * dot(q[b,h,:], K[t, g, :])
+ *   out[b,h,:] = sum_t exp(s_t - max s) V[t, g, :] / sum_t exp(s_t - max s)
+ * and out[b,h,:] = 0 when L == 0.  Cache slots at or beyond L are never used,
+ * whatever they hold (NaN included).
+ *
+ *   out            [num_seqs, num_q_heads, head_dim_v], element type dtype
+ *                  (fp32 accumulation, rounded once to nearest-even for bf16).
+ *   q              [num_seqs, num_q_heads, head_dim_k], dtype, contiguous.
+ *   k_cache        [num_blocks, block_size, num_kv_heads, head_dim_k], dtype.
+ *   v_cache        [num_blocks, block_size, num_kv_heads, head_dim_v], dtype,
+ *                  or NULL for latent mode (V = first head_dim_v values of
+ *                  each k_cache row).
+ *   block_tables   int32 [num_seqs, max_blocks_per_seq]; entries past the
+ *                  blocks a sequence uses are never read.
+ *   context_lens   int32 [num_seqs], each in [0, max_blocks_per_seq*block_size].
+ *   scale          softmax scale (finite), e.g. 1/sqrt(head_dim_k).
+ *   workspace      device buffer of at least pa_decode_workspace_size(...)
+ *                  bytes, 256-byte aligned; its contents on entry do not matter
+ *                  and on return are scratch.
+ *
+ * Shapes this build runs (anything else returns PA_ERR_UNSUPPORTED):
+ *   - head_dim_k == head_dim_v in {64, 128}, block_size 16,
+ *     num_q_heads / num_kv_heads in {1, 2, 4, 8}, dtype PA_F32 or PA_BF16;
+ *   - latent mode: head_dim_k 576, head_dim_v 512, num_kv_heads 1,
+ *     block_size 64, PA_BF16, num_q_heads a multiple of 16 up to 128.
+ * q, caches, out and workspace must be 16-byte aligned (PA_ERR_ALIGN).
+ */
+pa_status pa_decode(void *out, const void *q, const void *k_cache,
+                    const void *v_cache, const int32_t *block_tables,
+                    const int32_t *context_lens, float scale, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t num_kv_heads,
+                    int32_t head_dim_k, int32_t head_dim_v, int32_t block_size,
+                    int32_t num_blocks, int32_t max_blocks_per_seq,
+                    pa_dtype dtype, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/* Static text for a status code ("PA_OK", ...); never NULL. */
+const char *pa_status_string(pa_status status);
+
+/* Detail of the calling thread's last failed call ("" if none). */
+const char *pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -107,7 +107,9 @@ def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: Optional[np.ndarray],
         dv = dk if head_dim_v is None else int(head_dim_v)
     out = np.full((B, Hq, dv), np.nan, dtype=np.float64)
     if pairs is not None:
-        pr = np.ascontiguousarray(np.asarray(list(pairs), dtype=np.int32).reshape(-1, 2))
+        # each (b, h) once: rows are independent, duplicates would only repeat work
+        pr = np.ascontiguousarray(
+            np.unique(np.asarray(list(pairs), dtype=np.int32).reshape(-1, 2), axis=0))
         n_pairs = pr.shape[0]
     else:
         pr, n_pairs = None, 0

@@ -63,11 +63,16 @@ static int decode_row(double *out_row, const void *q, const void *k_cache,
     const int G = Hq / Hkv;
     const int g = h / G;
     const int L = context_lens[b];
-    for (int j = 0; j < dv; ++j) out_row[j] = 0.0;
-    if (L <= 0) return ORACLE_OK;
+    if (L <= 0) {
+        for (int j = 0; j < dv; ++j) out_row[j] = 0.0;
+        return ORACLE_OK;
+    }
 
-    double *s = (double *)malloc(sizeof(double) * (size_t)L);
+    /* scores and the output are built in private buffers and stored once */
+    double *s = (double *)malloc(sizeof(double) * ((size_t)L + (size_t)dv));
     if (!s) return ORACLE_NO_MEM;
+    double *o = s + L;
+    for (int j = 0; j < dv; ++j) o[j] = 0.0;
 
     const int64_t q_off = ((int64_t)b * Hq + h) * dk;
     for (int t = 0; t < L; ++t) {
@@ -99,9 +104,9 @@ static int decode_row(double *out_row, const void *q, const void *k_cache,
             v_off = ((p * bs + r) * Hkv + g) * (int64_t)dk;
             vbase = k_cache;
         }
-        for (int j = 0; j < dv; ++j) out_row[j] += w * widen(vbase, v_off + j, dtype);
+        for (int j = 0; j < dv; ++j) o[j] += w * widen(vbase, v_off + j, dtype);
     }
-    for (int j = 0; j < dv; ++j) out_row[j] /= denom;
+    for (int j = 0; j < dv; ++j) out_row[j] = o[j] / denom;
     free(s);
     return ORACLE_OK;
 }

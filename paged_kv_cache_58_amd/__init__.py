@@ -1,0 +1,148 @@
+"""Python binding of libpa.so: paged decode attention for MI355X (gfx950).
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of ``libpa.so``; there is no fallback.  If the library has not been
+built (``python -m paged_kv_cache_58_amd.build``) importing the functions below
+raises ``ImportError`` at first use.
+
+Tensors are torch tensors on the GPU (PyTorch supplies device memory and
+streams); the C ABI in ``include/pa.h`` takes the raw device pointers.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_F32, PA_BF16 = 0, 1
+STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_DTYPE",
+          4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP", 7: "PA_ERR_ALIGN"}
+
+EXPORTS = ("pa_cache_append", "pa_decode_workspace_size", "pa_decode", "pa_status_string",
+           "pa_last_error")
+
+_lib = None
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+def lib():
+    """The loaded ctypes library (built in-tree); raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run python -m paged_kv_cache_58_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        L.pa_cache_append.restype = ctypes.c_int
+        L.pa_cache_append.argtypes = [P, P, P, I64, P, I64, P, I32, I32, I32, I32, I32, I32,
+                                      ctypes.c_int, P]
+        L.pa_decode_workspace_size.restype = ctypes.c_size_t
+        L.pa_decode_workspace_size.argtypes = [I32] * 7
+        L.pa_decode.restype = ctypes.c_int
+        L.pa_decode.argtypes = [P, P, P, P, P, P, ctypes.c_float, I32, I32, I32, I32, I32,
+                                I32, I32, I32, ctypes.c_int, P, ctypes.c_size_t, P]
+        L.pa_status_string.restype = ctypes.c_char_p
+        L.pa_status_string.argtypes = [ctypes.c_int]
+        L.pa_last_error.restype = ctypes.c_char_p
+        L.pa_last_error.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise PAError(status, lib().pa_last_error().decode())
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def cache_append(k_cache, v_cache, k, v, slot_mapping, stream=None) -> None:
+    """Write k[i] (and v[i]) into slot slot_mapping[i] of the caches (-1 skips).
+
+    k_cache, v_cache: [num_blocks, block_size, kv_heads, head_dim]; v_cache None
+    selects latent mode (k only).  k, v: [num_tokens, kv_heads, head_dim] with
+    contiguous rows.  slot_mapping: int32 [num_tokens].
+    """
+    nb, bs, hkv, dk = k_cache.shape
+    dv = 0 if v_cache is None else v_cache.shape[3]
+    n = slot_mapping.shape[0]
+    k2 = k.reshape(n, -1) if n else k
+    v2 = None if v is None else (v.reshape(n, -1) if n else v)
+    if n and k2.stride(1) != 1:
+        raise ValueError("k rows must be contiguous")
+    if n and v2 is not None and v2.stride(1) != 1:
+        raise ValueError("v rows must be contiguous")
+    _check(lib().pa_cache_append(
+        _ptr(k_cache), _ptr(v_cache), _ptr(k2), k2.stride(0) if n else hkv * dk,
+        _ptr(v2), (v2.stride(0) if n else hkv * dv) if v2 is not None else 0,
+        _ptr(slot_mapping), n, nb, bs, hkv, dk, dv, _dtype_code(k_cache), _stream(stream)))
+
+
+def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim_k, head_dim_v,
+                          block_size, max_blocks_per_seq) -> int:
+    return int(lib().pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim_k,
+                                              head_dim_v, block_size, max_blocks_per_seq))
+
+
+def alloc_workspace(q, k_cache, block_tables, head_dim_v=None):
+    """A uint8 device tensor of the size pa_decode needs for these inputs."""
+    import torch
+
+    B, hq, dk = q.shape
+    hkv, bs = k_cache.shape[2], k_cache.shape[1]
+    dv = dk if head_dim_v is None else head_dim_v
+    n = decode_workspace_size(B, hq, hkv, dk, dv, bs, block_tables.shape[1])
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+
+
+def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, workspace,
+           stream=None) -> None:
+    """out[b, h] = softmax(q[b, h] . K^T * scale) . V over the paged context of b.
+
+    q [B, Hq, dk]; caches [num_blocks, block_size, Hkv, d] (v_cache None =
+    latent mode, V = first out.shape[-1] values of each K row); block_tables
+    int32 [B, max_blocks]; context_lens int32 [B]; out [B, Hq, dv] in q's dtype.
+    """
+    B, hq, dk = q.shape
+    nb, bs, hkv, _ = k_cache.shape
+    dv = out.shape[2]
+    for name, t in (("q", q), ("k_cache", k_cache), ("out", out), ("block_tables", block_tables),
+                    ("context_lens", context_lens)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if v_cache is not None and not v_cache.is_contiguous():
+        raise ValueError("v_cache must be contiguous")
+    _check(lib().pa_decode(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        _ptr(context_lens), float(scale), B, hq, hkv, dk, dv, bs, nb, block_tables.shape[1],
+        _dtype_code(q), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))

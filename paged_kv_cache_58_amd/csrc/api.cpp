@@ -1,0 +1,111 @@
+// C ABI of libpa.so (declared in include/pa.h): argument checks, planning and
+// kernel launches on the caller's stream.  Only the pa_* symbols are exported.
+#include <hip/hip_runtime.h>
+
+#include <string>
+
+#include "launch.h"
+#include "pa.h"
+#include "plan.h"
+
+#define PA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pa_status finish(pa_status st, const std::string &why) {
+    g_last_error = st == PA_OK ? std::string() : why;
+    return st;
+}
+
+pa::DecodeShape make_shape(bool latent, int32_t num_seqs, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim_k, int32_t head_dim_v,
+                           int32_t block_size, int32_t max_blocks_per_seq, pa_dtype dtype) {
+    pa::DecodeShape s{};
+    s.num_seqs = num_seqs;
+    s.num_q_heads = num_q_heads;
+    s.num_kv_heads = num_kv_heads;
+    s.head_dim_k = head_dim_k;
+    s.head_dim_v = head_dim_v;
+    s.block_size = block_size;
+    s.max_blocks_per_seq = max_blocks_per_seq;
+    s.latent = latent;
+    s.dtype = dtype;
+    return s;
+}
+
+}  // namespace
+
+PA_EXPORT pa_status pa_cache_append(void *k_cache, void *v_cache, const void *k,
+                                    int64_t k_token_stride, const void *v,
+                                    int64_t v_token_stride, const int32_t *slot_mapping,
+                                    int32_t num_tokens, int32_t num_blocks, int32_t block_size,
+                                    int32_t num_kv_heads, int32_t head_dim_k,
+                                    int32_t head_dim_v, pa_dtype dtype, void *stream) {
+    pa::AppendArgs a{k_cache, v_cache, k, k_token_stride, v, v_token_stride, slot_mapping,
+                     num_tokens, num_blocks, block_size, num_kv_heads, head_dim_k,
+                     head_dim_v, dtype};
+    std::string why;
+    pa::AppendPlan plan{};
+    pa_status st = pa::check_append(a, &plan, &why);
+    if (st != PA_OK) return finish(st, why);
+    st = pa::launch_append(a, plan, static_cast<hipStream_t>(stream), &why);
+    return finish(st, why);
+}
+
+PA_EXPORT size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                          int32_t num_kv_heads, int32_t head_dim_k,
+                                          int32_t head_dim_v, int32_t block_size,
+                                          int32_t max_blocks_per_seq) {
+    // Latent mode is the only shape with head_dim_v != head_dim_k.
+    const bool latent = head_dim_k != head_dim_v;
+    const pa::DecodeShape s = make_shape(latent, num_seqs, num_q_heads, num_kv_heads,
+                                         head_dim_k, head_dim_v, block_size,
+                                         max_blocks_per_seq, PA_BF16);
+    pa::DecodePlan plan{};
+    if (pa::plan_decode(s, &plan, nullptr) != PA_OK) return 0;
+    return plan.bytes;
+}
+
+PA_EXPORT pa_status pa_decode(void *out, const void *q, const void *k_cache,
+                              const void *v_cache, const int32_t *block_tables,
+                              const int32_t *context_lens, float scale, int32_t num_seqs,
+                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim_k,
+                              int32_t head_dim_v, int32_t block_size, int32_t num_blocks,
+                              int32_t max_blocks_per_seq, pa_dtype dtype, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+    const pa::DecodeShape s =
+        make_shape(v_cache == nullptr, num_seqs, num_q_heads, num_kv_heads, head_dim_k,
+                   head_dim_v, block_size, max_blocks_per_seq, dtype);
+    std::string why;
+    pa::DecodePlan plan{};
+    pa_status st = pa::plan_decode(s, &plan, &why);
+    if (st != PA_OK) return finish(st, why);
+    const pa::DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                           num_blocks, workspace, workspace_bytes};
+    st = pa::check_decode(s, a, plan, &why);
+    if (st != PA_OK || num_seqs == 0) return finish(st, why);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (plan.path == pa::DecodePath::kLatent)
+        st = pa::launch_latent_decode(s, a, plan, hs, &why);
+    else
+        st = pa::launch_grouped_decode(s, a, plan, hs, &why);
+    return finish(st, why);
+}
+
+PA_EXPORT const char *pa_status_string(pa_status status) {
+    switch (status) {
+        case PA_OK: return "PA_OK";
+        case PA_ERR_NULL: return "PA_ERR_NULL";
+        case PA_ERR_SHAPE: return "PA_ERR_SHAPE";
+        case PA_ERR_DTYPE: return "PA_ERR_DTYPE";
+        case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+        case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+        case PA_ERR_HIP: return "PA_ERR_HIP";
+        case PA_ERR_ALIGN: return "PA_ERR_ALIGN";
+    }
+    return "PA_ERR_UNKNOWN";
+}
+
+PA_EXPORT const char *pa_last_error(void) { return g_last_error.c_str(); }

@@ -1,0 +1,35 @@
+// Internal launchers shared by the C ABI (api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <string>
+
+#include "plan.h"
+
+namespace pa {
+
+// Slot-mapped K/V row copy.  Enqueues on `stream`; returns PA_OK or PA_ERR_HIP.
+pa_status launch_append(const AppendArgs &a, const AppendPlan &plan, hipStream_t stream,
+                        std::string *why);
+
+// Grouped-query (and MHA) decode: split-context partition kernel followed by
+// the log-sum-exp reduce.
+pa_status launch_grouped_decode(const DecodeShape &s, const DecodeArgs &a,
+                                const DecodePlan &plan, hipStream_t stream, std::string *why);
+
+// Latent (576/512) decode on MFMA, followed by the same reduce.
+pa_status launch_latent_decode(const DecodeShape &s, const DecodeArgs &a,
+                               const DecodePlan &plan, hipStream_t stream, std::string *why);
+
+// Log-sum-exp merge of the partition results into `out` (shared by both paths).
+pa_status launch_lse_reduce(const DecodeShape &s, const DecodeArgs &a, const DecodePlan &plan,
+                            int part_tokens, hipStream_t stream, std::string *why);
+
+inline pa_status hip_status(hipError_t e, std::string *why, const char *where) {
+    if (e == hipSuccess) return PA_OK;
+    if (why) *why = std::string(where) + ": " + hipGetErrorString(e);
+    return PA_ERR_HIP;
+}
+
+}  // namespace pa

@@ -1,0 +1,160 @@
+// Host-side argument checks and launch planning (no HIP headers).
+#include "plan.h"
+
+#include <cmath>
+#include <cstdlib>
+
+namespace pa {
+namespace {
+
+constexpr size_t kWorkspaceAlign = 256;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int elt_bytes(pa_dtype d) { return d == PA_F32 ? 4 : 2; }
+
+bool valid_dtype(pa_dtype d) { return d == PA_F32 || d == PA_BF16; }
+
+pa_status fail(pa_status st, std::string *why, const std::string &msg) {
+    if (why) *why = msg;
+    return st;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Blocks per partition for the grouped path.  512 tokens keeps every
+// partition long enough to stream at full rate while a batch-4, 128K-token
+// workload still yields thousands of work-groups.  PA_PARTITION_BLOCKS (1..64)
+// overrides it for tuning.
+int grouped_part_blocks() {
+    const char *env = std::getenv("PA_PARTITION_BLOCKS");
+    if (env && *env) {
+        int v = std::atoi(env);
+        if (v >= 1 && v <= 64) return v;
+    }
+    return 32;
+}
+
+// Latent path: 64-token blocks; 8 blocks (512 tokens) per partition.
+int latent_part_blocks() {
+    const char *env = std::getenv("PA_LATENT_PARTITION_BLOCKS");
+    if (env && *env) {
+        int v = std::atoi(env);
+        if (v >= 1 && v <= 64) return v;
+    }
+    return 8;
+}
+
+}  // namespace
+
+pa_status check_append(const AppendArgs &a, AppendPlan *plan, std::string *why) {
+    if (!valid_dtype(a.dtype)) return fail(PA_ERR_DTYPE, why, "append: unknown dtype");
+    if (a.num_tokens < 0) return fail(PA_ERR_SHAPE, why, "append: num_tokens < 0");
+    if (a.num_blocks <= 0 || a.block_size <= 0 || a.num_kv_heads <= 0 || a.head_dim_k <= 0)
+        return fail(PA_ERR_SHAPE, why,
+                    "append: num_blocks, block_size, num_kv_heads and head_dim_k must be > 0");
+    const bool latent = a.v_cache == nullptr;
+    if (latent != (a.v == nullptr))
+        return fail(PA_ERR_NULL, why, "append: v_cache and v must both be NULL or both set");
+    if (!latent && a.head_dim_v <= 0)
+        return fail(PA_ERR_SHAPE, why, "append: head_dim_v must be > 0 with a V cache");
+    if (a.num_tokens > 0 && (!a.k_cache || !a.k || !a.slot_mapping))
+        return fail(PA_ERR_NULL, why, "append: k_cache, k and slot_mapping must be non-NULL");
+    if ((int64_t)a.num_blocks * a.block_size > INT32_MAX)
+        return fail(PA_ERR_SHAPE, why, "append: more than 2^31-1 slots");
+    const int eb = elt_bytes(a.dtype);
+    const int64_t k_row = (int64_t)a.num_kv_heads * a.head_dim_k;
+    const int64_t v_row = latent ? 0 : (int64_t)a.num_kv_heads * a.head_dim_v;
+    if (a.k_token_stride < k_row)
+        return fail(PA_ERR_SHAPE, why, "append: k_token_stride smaller than a K row");
+    if (!latent && a.v_token_stride < v_row)
+        return fail(PA_ERR_SHAPE, why, "append: v_token_stride smaller than a V row");
+    int vec = 16;
+    auto fits = [&](int64_t bytes) { return bytes % vec == 0; };
+    auto ptr_fits = [&](const void *p) { return p == nullptr || aligned(p, vec); };
+    while (vec > eb) {
+        bool ok = fits(k_row * eb) && fits(a.k_token_stride * eb) && ptr_fits(a.k_cache) &&
+                  ptr_fits(a.k);
+        if (!latent)
+            ok = ok && fits(v_row * eb) && fits(a.v_token_stride * eb) && ptr_fits(a.v_cache) &&
+                 ptr_fits(a.v);
+        if (ok) break;
+        vec /= 2;
+    }
+    if (!ptr_fits(a.k_cache) || !ptr_fits(a.k) || !ptr_fits(a.v_cache) || !ptr_fits(a.v))
+        return fail(PA_ERR_ALIGN, why, "append: pointers not aligned to the element size");
+    if (plan) {
+        plan->vec_bytes = vec;
+        plan->k_row_bytes = k_row * eb;
+        plan->v_row_bytes = v_row * eb;
+    }
+    return PA_OK;
+}
+
+pa_status plan_decode(const DecodeShape &s, DecodePlan *plan, std::string *why) {
+    if (!valid_dtype(s.dtype)) return fail(PA_ERR_DTYPE, why, "decode: unknown dtype");
+    if (s.num_seqs < 0) return fail(PA_ERR_SHAPE, why, "decode: num_seqs < 0");
+    if (s.num_q_heads <= 0 || s.num_kv_heads <= 0 || s.head_dim_k <= 0 || s.head_dim_v <= 0 ||
+        s.block_size <= 0 || s.max_blocks_per_seq <= 0)
+        return fail(PA_ERR_SHAPE, why, "decode: head counts, head dims, block_size and "
+                                       "max_blocks_per_seq must be > 0");
+    if (s.num_q_heads % s.num_kv_heads != 0)
+        return fail(PA_ERR_SHAPE, why, "decode: num_q_heads is not a multiple of num_kv_heads");
+    if ((int64_t)s.max_blocks_per_seq * s.block_size > INT32_MAX)
+        return fail(PA_ERR_SHAPE, why, "decode: max context exceeds 2^31-1 tokens");
+    if (s.num_seqs > 65535 || s.num_kv_heads > 65535)
+        return fail(PA_ERR_UNSUPPORTED, why, "decode: runs at most 65535 sequences and KV heads");
+    const int G = s.num_q_heads / s.num_kv_heads;
+    DecodePlan p{};
+    p.group = G;
+    if (s.latent) {
+        if (s.head_dim_k != 576 || s.head_dim_v != 512 || s.num_kv_heads != 1 ||
+            s.block_size != 64 || s.dtype != PA_BF16 || s.num_q_heads % 16 != 0 ||
+            s.num_q_heads > 128)
+            return fail(PA_ERR_UNSUPPORTED, why,
+                        "decode (latent): runs head_dim_k 576, head_dim_v 512, one KV head, "
+                        "block_size 64, bf16, num_q_heads a multiple of 16 up to 128");
+        p.path = DecodePath::kLatent;
+        p.part_blocks = latent_part_blocks();
+    } else {
+        if (s.head_dim_k != s.head_dim_v || (s.head_dim_k != 64 && s.head_dim_k != 128))
+            return fail(PA_ERR_UNSUPPORTED, why,
+                        "decode: runs head_dim_k == head_dim_v in {64, 128}");
+        if (s.block_size != 16)
+            return fail(PA_ERR_UNSUPPORTED, why, "decode: runs block_size 16");
+        if (G != 1 && G != 2 && G != 4 && G != 8)
+            return fail(PA_ERR_UNSUPPORTED, why,
+                        "decode: runs num_q_heads / num_kv_heads in {1, 2, 4, 8}");
+        p.path = DecodePath::kGrouped;
+        p.part_blocks = grouped_part_blocks();
+    }
+    p.num_parts = (s.max_blocks_per_seq + p.part_blocks - 1) / p.part_blocks;
+    const size_t rows = (size_t)s.num_seqs * s.num_q_heads * (size_t)p.num_parts;
+    p.acc_offset = 0;
+    p.ml_offset = round_up(rows * s.head_dim_v * sizeof(float), kWorkspaceAlign);
+    p.bytes = round_up(p.ml_offset + rows * 2 * sizeof(float), kWorkspaceAlign);
+    if (plan) *plan = p;
+    return PA_OK;
+}
+
+pa_status check_decode(const DecodeShape &s, const DecodeArgs &a, const DecodePlan &plan,
+                       std::string *why) {
+    if (s.num_seqs == 0) return PA_OK;
+    if (!a.out || !a.q || !a.k_cache || !a.block_tables || !a.context_lens)
+        return fail(PA_ERR_NULL, why,
+                    "decode: out, q, k_cache, block_tables and context_lens must be non-NULL");
+    if (a.num_blocks <= 0) return fail(PA_ERR_SHAPE, why, "decode: num_blocks must be > 0");
+    if (!std::isfinite(a.scale)) return fail(PA_ERR_SHAPE, why, "decode: scale is not finite");
+    if (!aligned(a.out, 16) || !aligned(a.q, 16) || !aligned(a.k_cache, 16) ||
+        (a.v_cache && !aligned(a.v_cache, 16)) || !aligned(a.block_tables, 4) ||
+        !aligned(a.context_lens, 4))
+        return fail(PA_ERR_ALIGN, why, "decode: q, caches and out must be 16-byte aligned");
+    if (!a.workspace || a.workspace_bytes < plan.bytes)
+        return fail(PA_ERR_WORKSPACE, why,
+                    "decode: workspace missing or smaller than pa_decode_workspace_size()");
+    if (!aligned(a.workspace, kWorkspaceAlign))
+        return fail(PA_ERR_ALIGN, why, "decode: workspace must be 256-byte aligned");
+    return PA_OK;
+}
+
+}  // namespace pa

@@ -1,0 +1,129 @@
+"""The C-ABI library loads, exports what include/pa.h declares, and rejects bad
+arguments on the host (no GPU needed: every call here fails validation before
+any device work)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import paged_kv_cache_58_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+FAKE = 0x100000  # a 256-byte aligned non-NULL address; never dereferenced here
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared() == sorted(pa.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = pa.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (pa_\w+)", out))
+    assert exported == set(_declared())
+
+
+def test_status_strings():
+    L = pa.lib()
+    for code, name in pa.STATUS.items():
+        assert L.pa_status_string(code).decode() == name
+
+
+def _decode(**kw):
+    args = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, scale=0.125, B=4, hq=64,
+                hkv=8, dk=128, dv=128, bs=16, nb=100, mb=16, dtype=pa.PA_BF16, ws=FAKE,
+                wsb=1 << 30)
+    args.update(kw)
+    L = pa.lib()
+    return L.pa_decode(args["out"], args["q"], args["k"], args["v"], args["bt"], args["cl"],
+                       args["scale"], args["B"], args["hq"], args["hkv"], args["dk"], args["dv"],
+                       args["bs"], args["nb"], args["mb"], args["dtype"], args["ws"],
+                       args["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1),
+    (dict(out=None), 1),
+    (dict(bt=None), 1),
+    (dict(hq=60), 2),            # not a multiple of kv heads
+    (dict(hkv=0), 2),
+    (dict(B=-1), 2),
+    (dict(dtype=7), 3),
+    (dict(dk=96, dv=96), 4),
+    (dict(bs=32), 4),
+    (dict(hq=24, hkv=8), 4),     # group of 3
+    (dict(dk=128, dv=64), 4),
+    (dict(v=None), 4),           # latent mode needs the 576/512 shape
+    (dict(wsb=1024), 5),
+    (dict(ws=None), 5),
+    (dict(q=FAKE + 8), 7),
+    (dict(ws=FAKE + 16), 7),
+    (dict(scale=float("nan")), 2),
+    (dict(nb=0), 2),
+])
+def test_decode_rejects(kw, status):
+    assert _decode(**kw) == status
+    assert pa.lib().pa_last_error().decode() != ""
+
+
+def test_decode_with_no_sequences_is_a_noop():
+    assert _decode(B=0, out=None, q=None, ws=None, wsb=0) == 0
+
+
+def test_latent_shape_checks():
+    lat = dict(v=None, dk=576, dv=512, hkv=1, hq=128, bs=64)
+    assert _decode(**{**lat, "hq": 136}) == 4
+    assert _decode(**{**lat, "dtype": pa.PA_F32}) == 4
+    assert _decode(**{**lat, "bs": 16}) == 4
+
+
+def test_workspace_size():
+    n = pa.decode_workspace_size(100, 64, 8, 128, 128, 16, 513)
+    parts = -(-513 // 32)
+    assert n >= 100 * 64 * parts * (128 + 2) * 4 and n % 256 == 0
+    assert pa.decode_workspace_size(100, 60, 8, 128, 128, 16, 513) == 0
+    assert pa.decode_workspace_size(64, 128, 1, 576, 512, 64, 129) > 0
+
+
+def _append(**kw):
+    a = dict(kc=FAKE, vc=FAKE, k=FAKE, ks=1024, v=FAKE, vs=1024, sm=FAKE, n=4, nb=10, bs=16,
+             hkv=8, dk=128, dv=128, dtype=pa.PA_BF16)
+    a.update(kw)
+    return pa.lib().pa_cache_append(a["kc"], a["vc"], a["k"], a["ks"], a["v"], a["vs"], a["sm"],
+                                    a["n"], a["nb"], a["bs"], a["hkv"], a["dk"], a["dv"],
+                                    a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=9), 3),
+    (dict(k=None), 1),
+    (dict(sm=None), 1),
+    (dict(v=None), 1),          # v_cache set but v missing
+    (dict(vc=None), 1),
+    (dict(ks=100), 2),          # stride below the row length
+    (dict(vs=10), 2),
+    (dict(n=-1), 2),
+    (dict(nb=0), 2),
+    (dict(dv=0), 2),
+])
+def test_append_rejects(kw, status):
+    assert _append(**kw) == status
+
+
+def test_append_zero_tokens_is_a_noop():
+    assert _append(n=0, kc=None, k=None, sm=None, vc=None, v=None) == 0

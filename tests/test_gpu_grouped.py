@@ -1,0 +1,179 @@
+"""GPU parity of pa_cache_append and the grouped-query pa_decode path against
+the CPU oracle (runs on an MI355X through the C ABI)."""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import compare, host_array, say, to_device, widen
+from workloads import custom_spec, make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def _append_bitwise(d, slots=None):
+    w = d.w
+    sm = w.slot_mapping if slots is None else slots
+    hk = w.k_cache.copy()
+    hv = None if w.v_cache is None else w.v_cache.copy()
+    oracle.append(hk, hv, w.k_new, w.v_new, sm)
+    d.append(None if slots is None else torch.from_numpy(sm).to(d.q.device))
+    torch.cuda.synchronize()
+    gk = host_array(d.k_cache)
+    assert np.array_equal(gk.view(np.uint8), hk.view(np.uint8)), "K pool differs after append"
+    if hv is not None:
+        gv = host_array(d.v_cache)
+        assert np.array_equal(gv.view(np.uint8), hv.view(np.uint8)), "V pool differs after append"
+    return hk, hv
+
+
+def test_config1_append_and_decode(dev):
+    say("case: c1 tiny fp32, decode(ctx), append, decode(ctx+1)")
+    w = make_workload("c1")
+    d = to_device(w, dev)
+    stats = compare(d.decode(), oracle.decode_workload(w), "f32")
+    say(f"  decode(ctx): {stats}")
+    hk, hv = _append_bitwise(d)
+    L1 = w.context_lens + 1
+    out = d.decode(context_lens=torch.from_numpy(L1).to(dev))
+    ref = oracle.decode(w.q, hk, hv, w.block_tables, L1, w.scale)
+    say(f"  decode(ctx+1): {compare(out, ref, 'f32')}")
+
+
+CASES = [
+    # dtype, head_dim, q heads, kv heads, context lengths
+    ("f32", 64, 4, 2, [17, 64, 100, 255]),
+    ("f32", 64, 8, 1, [1, 16, 513, 1029]),
+    ("f32", 128, 4, 4, [0, 33, 700]),
+    ("bf16", 128, 16, 2, [1, 15, 16, 17, 511, 512, 513, 1300]),
+    ("bf16", 128, 4, 4, [2, 31, 1025, 2049]),
+    ("bf16", 128, 8, 4, [0, 100, 600]),
+    ("bf16", 64, 16, 4, [3, 17, 520, 1100]),
+    ("bf16", 64, 2, 2, [1, 48, 1500]),
+]
+
+
+@pytest.mark.parametrize("dtype,D,hq,hkv,ctx", CASES)
+def test_decode_parity_small(dev, dtype, D, hq, hkv, ctx):
+    say(f"case: {dtype} D={D} Hq={hq} Hkv={hkv} ctx={ctx}")
+    w = make_workload(custom_spec(len(ctx), hq, hkv, D, 16, dtype, ctx=ctx), seed=7 + D + hq)
+    d = to_device(w, dev)
+    say(f"  {compare(d.decode(), oracle.decode_workload(w), dtype)}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_wide_score_range_exercises_rescale(dev, dtype):
+    """scale = 1 on unit-variance data: scores spread over tens of units, so the
+    running max is raised many times inside a partition."""
+    say(f"case: rescale-heavy {dtype}")
+    spec = custom_spec(3, 16, 2, 128, 16, dtype, ctx=[700, 2000, 64], scale=1.0)
+    w = make_workload(spec, seed=3)
+    d = to_device(w, dev)
+    say(f"  {compare(d.decode(), oracle.decode_workload(w), dtype)}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_context_one_returns_v_bitwise(dev, dtype):
+    say(f"case: ctx=1 {dtype}")
+    w = make_workload(custom_spec(4, 16, 2, 128, 16, dtype, ctx=[1, 1, 1, 1]), seed=5)
+    d = to_device(w, dev)
+    got = host_array(d.decode())
+    for b in range(4):
+        v0 = w.v_cache[w.block_tables[b, 0], 0]  # [Hkv, D]
+        want = np.repeat(v0, 8, axis=0)
+        assert np.array_equal(got[b].view(np.uint8), want.view(np.uint8))
+
+
+def test_deterministic_and_permutation_invariant(dev):
+    say("case: determinism + block permutation")
+    w = make_workload(custom_spec(3, 64, 8, 128, 16, "bf16", ctx=[900, 3000, 17]), seed=11)
+    d = to_device(w, dev)
+    a = host_array(d.decode())
+    b = host_array(d.decode())
+    assert np.array_equal(a, b)
+    rng = np.random.default_rng(1)
+    pi = rng.permutation(w.num_blocks).astype(np.int32)
+    kp = np.empty_like(w.k_cache)
+    vp = np.empty_like(w.v_cache)
+    kp[pi] = w.k_cache
+    vp[pi] = w.v_cache
+    bt = np.where(w.block_tables >= 0, pi[np.maximum(w.block_tables, 0)], -1).astype(np.int32)
+    w2 = make_workload(custom_spec(3, 64, 8, 128, 16, "bf16", ctx=[900, 3000, 17]), seed=11)
+    w2.k_cache, w2.v_cache, w2.block_tables = kp, vp, bt
+    c = host_array(to_device(w2, dev).decode())
+    assert np.array_equal(a, c)
+
+
+def test_nan_poison_equals_zero_fill(dev):
+    say("case: NaN poison vs zero fill")
+    w = make_workload(custom_spec(3, 16, 2, 128, 16, "bf16", ctx=[5, 250, 1000]), seed=2)
+    a = host_array(to_device(w, dev).decode())
+    z = np.where(np.isnan(widen(w.k_cache)), 0, 1).astype(bool)
+    w.k_cache = np.where(z, w.k_cache, np.uint16(0))
+    w.v_cache = np.where(np.isnan(widen(w.v_cache)), np.uint16(0), w.v_cache)
+    assert not np.isnan(widen(w.k_cache)).any()
+    b = host_array(to_device(w, dev).decode())
+    assert np.array_equal(a, b)
+    assert np.isfinite(widen(a)).all()
+
+
+def test_gqa_equals_mha_on_expanded_cache(dev):
+    say("case: GQA vs MHA with repeated KV heads")
+    w = make_workload(custom_spec(2, 16, 2, 128, 16, "bf16", ctx=[400, 1500]), seed=9)
+    gqa = widen(host_array(to_device(w, dev).decode()))
+    w.k_cache = np.ascontiguousarray(np.repeat(w.k_cache, 8, axis=2))
+    w.v_cache = np.ascontiguousarray(np.repeat(w.v_cache, 8, axis=2))
+    mha = widen(host_array(to_device(w, dev).decode()))
+    assert np.abs(gqa - mha).max() <= 2e-2
+
+
+@pytest.mark.parametrize("blocks", ["1", "7", "64"])
+def test_partition_size_does_not_change_result(dev, blocks, monkeypatch):
+    say(f"case: partition of {blocks} blocks")
+    monkeypatch.setenv("PA_PARTITION_BLOCKS", blocks)
+    w = make_workload(custom_spec(3, 16, 2, 128, 16, "bf16", ctx=[1, 333, 2100]), seed=4)
+    d = to_device(w, dev)
+    say(f"  {compare(d.decode(), oracle.decode_workload(w), 'bf16')}")
+
+
+def test_append_skip_and_latent(dev):
+    say("case: append with -1 slots; latent-mode append")
+    w = make_workload(custom_spec(4, 8, 2, 64, 16, "bf16", ctx=[3, 16, 40, 0]), seed=6)
+    d = to_device(w, dev)
+    sm = w.slot_mapping.copy()
+    sm[1] = -1
+    _append_bitwise(d, sm)
+    spec = custom_spec(3, 16, 1, 576, 64, "bf16", ctx=[63, 64, 300], head_dim_v=512, mla=True)
+    wl = make_workload(spec, seed=8)
+    _append_bitwise(to_device(wl, dev))
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c4"])
+def test_full_config_parity(dev, name):
+    say(f"case: full config {name}: generate")
+    w = make_workload(name)
+    d = to_device(w, dev)
+    say(f"  {name}: decode(ctx) vs oracle on every row")
+    stats = compare(d.decode(), oracle.decode_workload(w), "bf16")
+    say(f"  {name}: {stats}")
+    hk, hv = _append_bitwise(d)
+    say(f"  {name}: append bit-exact; decode(ctx+1) on sampled rows")
+    L1 = w.context_lens + 1
+    out = d.decode(context_lens=torch.from_numpy(L1).to(dev))
+    rng = np.random.default_rng(0)
+    rows = [(int(b), int(h)) for b, h in zip(rng.integers(0, w.spec.num_seqs, 64),
+                                             rng.integers(0, w.spec.num_q_heads, 64))]
+    ref = oracle.decode(w.q, hk, hv, w.block_tables, L1, w.scale, pairs=rows)
+    say(f"  {name}: {compare(out, ref, 'bf16', rows=rows)}")
+    del d
+    torch.cuda.empty_cache()

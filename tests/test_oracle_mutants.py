@@ -27,7 +27,7 @@ MUTANTS = {
                              "const int r = (t / bs) % bs;\n        const int64_t k_off"),
     "dropped_scale": ("s[t] = scale * dot;", "s[t] = dot;"),
     "wrong_exp_sign": ("const double w = exp(s[t] - m);", "const double w = exp(m - s[t]);"),
-    "no_normalisation": ("out_row[j] /= denom;", "out_row[j] /= 1.0;"),
+    "no_normalisation": ("out_row[j] = o[j] / denom;", "out_row[j] = o[j];"),
     "dropped_kv_head": ("const int64_t k_off = ((p * bs + r) * Hkv + g) * (int64_t)dk;",
                         "const int64_t k_off = ((p * bs + r) * Hkv) * (int64_t)dk;"),
     "latent_row_stride": ("v_off = ((p * bs + r) * Hkv + g) * (int64_t)dk;",

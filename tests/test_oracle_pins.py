@@ -364,3 +364,14 @@ def test_p11_config_bytes():
     s5 = CONFIGS["c5"]
     assert workloads.kv_bytes_per_token_layer(1, 576, 512, 2, mla=True) == 1152
     assert s4.max_blocks_per_seq == 8193 and s5.max_blocks_per_seq == 129
+
+
+def test_sampled_rows_with_duplicates_match_full_decode():
+    """Row sampling (used at full sizes) equals the full decode, duplicates included."""
+    w = make_workload(custom_spec(3, 8, 2, 32, 16, "f32", ctx=[50, 400, 7]))
+    full = oracle.decode_workload(w)
+    pairs = [(1, 3), (1, 3), (0, 0), (2, 7), (1, 3), (0, 0)]
+    part = oracle.decode_workload(w, pairs=pairs)
+    for b, h in pairs:
+        assert np.array_equal(part[b, h], full[b, h])
+    assert np.isnan(part[2, 0]).all()
