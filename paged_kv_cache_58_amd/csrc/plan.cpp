@@ -22,17 +22,13 @@ pa_status fail(pa_status st, std::string *why, const std::string &msg) {
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Blocks per partition for the grouped path.  512 tokens keeps every
-// partition long enough to stream at full rate while a batch-4, 128K-token
-// workload still yields thousands of work-groups.  PA_PARTITION_BLOCKS (1..64)
-// overrides it for tuning.
-int grouped_part_blocks() {
-    const char *env = std::getenv("PA_PARTITION_BLOCKS");
-    if (env && *env) {
-        int v = std::atoi(env);
-        if (v >= 1 && v <= 64) return v;
-    }
-    return 32;
+// Blocks a work-group streams into LDS on the grouped path (ring depth).
+// Two 8 KB slots per wave let LDS hold eight waves per CU, which beats a
+// deeper ring with fewer waves.  PA_RING_DEPTH (2 or 4) overrides it.
+int grouped_ring_depth() {
+    const char *env = std::getenv("PA_RING_DEPTH");
+    if (env && *env && std::atoi(env) == 4) return 4;
+    return 2;
 }
 
 // Latent path: 64-token blocks; 8 blocks (512 tokens) per partition.
@@ -125,14 +121,26 @@ pa_status plan_decode(const DecodeShape &s, DecodePlan *plan, std::string *why) 
         if (G != 1 && G != 2 && G != 4 && G != 8)
             return fail(PA_ERR_UNSUPPORTED, why,
                         "decode: runs num_q_heads / num_kv_heads in {1, 2, 4, 8}");
+        if ((int64_t)s.num_seqs * s.max_blocks_per_seq * s.num_kv_heads > INT32_MAX)
+            return fail(PA_ERR_SHAPE, why,
+                        "decode: num_seqs * max_blocks_per_seq * num_kv_heads exceeds 2^31-1");
         p.path = DecodePath::kGrouped;
-        p.part_blocks = grouped_part_blocks();
+        p.ring_depth = grouped_ring_depth();
+        p.part_blocks = 0;
+        p.num_parts = 0;
     }
-    p.num_parts = (s.max_blocks_per_seq + p.part_blocks - 1) / p.part_blocks;
-    const size_t rows = (size_t)s.num_seqs * s.num_q_heads * (size_t)p.num_parts;
+    size_t rows;  // (slot, head) rows of partial results
+    if (p.path == DecodePath::kGrouped)
+        rows = ((size_t)kStreamWavesMax + (size_t)s.num_seqs * s.num_kv_heads) * (size_t)G;
+    else {
+        p.num_parts = (s.max_blocks_per_seq + p.part_blocks - 1) / p.part_blocks;
+        rows = (size_t)s.num_seqs * s.num_q_heads * (size_t)p.num_parts;
+    }
     p.acc_offset = 0;
     p.ml_offset = round_up(rows * s.head_dim_v * sizeof(float), kWorkspaceAlign);
-    p.bytes = round_up(p.ml_offset + rows * 2 * sizeof(float), kWorkspaceAlign);
+    p.prefix_offset = round_up(p.ml_offset + rows * 2 * sizeof(float), kWorkspaceAlign);
+    p.bytes = round_up(p.prefix_offset + ((size_t)s.num_seqs + 1) * sizeof(int32_t),
+                       kWorkspaceAlign);
     if (plan) *plan = p;
     return PA_OK;
 }

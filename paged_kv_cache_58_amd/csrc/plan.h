@@ -41,6 +41,11 @@ pa_status check_append(const AppendArgs &a, AppendPlan *plan, std::string *why);
 
 enum class DecodePath { kGrouped, kLatent };
 
+// Most work-groups the grouped path's stream-K partition kernel launches
+// (one per resident wave slot; 256 CUs x 16 waves), which sizes its
+// workspace: a partial slot per work-group plus one per (sequence, KV head).
+constexpr int kStreamWavesMax = 4096;
+
 struct DecodeShape {
     int32_t num_seqs;
     int32_t num_q_heads;
@@ -53,18 +58,25 @@ struct DecodeShape {
     pa_dtype dtype;
 };
 
-// Split-context plan: each sequence's context is cut into partitions of
-// part_blocks cache blocks; one work-group handles one (partition, KV head,
-// sequence) and leaves an unnormalised fp32 accumulator plus (max, sum) in
-// the workspace for the log-sum-exp reduce.
+// Split-context plan.  Both paths leave, per partial result and query head,
+// an unnormalised fp32 accumulator plus (max, sum) in the workspace for the
+// log-sum-exp reduce.
+//  * grouped: stream-K; slots = kStreamWavesMax + num_seqs * num_kv_heads,
+//    each holding the G heads of one KV group; plus the per-sequence block
+//    prefix sums (num_seqs + 1 int32) the partition kernel leaves for the
+//    reduce.
+//  * latent: fixed partitions of part_blocks blocks; slots = num_seqs *
+//    num_parts, each holding all query heads.
 struct DecodePlan {
     DecodePath path;
-    int group;          // query heads per KV head
-    int part_blocks;    // cache blocks per partition
-    int num_parts;      // partitions per sequence at max_blocks_per_seq
-    size_t acc_offset;  // float [num_seqs, num_q_heads, num_parts, head_dim_v]
-    size_t ml_offset;   // float2 [num_seqs, num_q_heads, num_parts] = (max, sum)
-    size_t bytes;       // total workspace bytes
+    int group;             // query heads per KV head
+    int part_blocks;       // latent path: cache blocks per partition
+    int num_parts;         // latent path: partitions per sequence at max_blocks_per_seq
+    int ring_depth;        // grouped path: cache blocks streaming into LDS per wave (2 or 4)
+    size_t acc_offset;     // float [slots, heads per slot, head_dim_v]
+    size_t ml_offset;      // float2 [slots, heads per slot] = (max, sum)
+    size_t prefix_offset;  // grouped path: int32 [num_seqs + 1]
+    size_t bytes;          // total workspace bytes
 };
 
 // Validates the sizes and fills the plan.  Does not look at pointers.

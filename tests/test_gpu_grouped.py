@@ -137,13 +137,30 @@ def test_gqa_equals_mha_on_expanded_cache(dev):
     assert np.abs(gqa - mha).max() <= 2e-2
 
 
-@pytest.mark.parametrize("blocks", ["1", "7", "64"])
-def test_partition_size_does_not_change_result(dev, blocks, monkeypatch):
-    say(f"case: partition of {blocks} blocks")
-    monkeypatch.setenv("PA_PARTITION_BLOCKS", blocks)
-    w = make_workload(custom_spec(3, 16, 2, 128, 16, "bf16", ctx=[1, 333, 2100]), seed=4)
+@pytest.mark.parametrize("waves", ["1", "7", "300", "4096"])
+@pytest.mark.parametrize("ring", ["2", "4"])
+def test_stream_split_does_not_change_result(dev, waves, ring, monkeypatch):
+    """The stream-K split (work-groups sharing the block order) and the LDS
+    ring depth change only rounding: 1 work-group walks every segment, 7 and
+    300 cut segments at uneven places, 4096 leaves most work-groups idle."""
+    say(f"case: {waves} stream work-groups, ring {ring}")
+    monkeypatch.setenv("PA_STREAM_WAVES", waves)
+    monkeypatch.setenv("PA_RING_DEPTH", ring)
+    w = make_workload(custom_spec(5, 16, 2, 128, 16, "bf16", ctx=[1, 333, 0, 4148, 70]), seed=4)
     d = to_device(w, dev)
     say(f"  {compare(d.decode(), oracle.decode_workload(w), 'bf16')}")
+
+
+@pytest.mark.parametrize("dtype,D,hq,hkv", [("bf16", 128, 64, 8), ("f32", 64, 4, 2),
+                                            ("bf16", 64, 16, 4)])
+def test_long_segments_refill_block_ids(dev, dtype, D, hq, hkv, monkeypatch):
+    """Few work-groups over long contexts: each walks hundreds of blocks of one
+    segment, so the block-id buffers refill many times (64 ids per chunk)."""
+    say(f"case: long segments {dtype} D={D}")
+    monkeypatch.setenv("PA_STREAM_WAVES", "3")
+    w = make_workload(custom_spec(2, hq, hkv, D, 16, dtype, ctx=[6000, 3001]), seed=12)
+    d = to_device(w, dev)
+    say(f"  {compare(d.decode(), oracle.decode_workload(w), dtype)}")
 
 
 def test_append_skip_and_latent(dev):
