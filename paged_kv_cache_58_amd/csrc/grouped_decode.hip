@@ -39,46 +39,16 @@
 //    accumulators stay in registers until the partition ends.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cstdint>
-#include <cstdlib>
 
+#include "device_common.h"
 #include "launch.h"
 
 namespace pa {
 namespace {
 
-constexpr int kWave = 64;
 constexpr int kBS = 16;              // tokens per cache block on this path
 constexpr float kSlack = 8.0f;       // lazy-rescale threshold, log2 units
-constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int kMaxDevices = 64;
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float as_f(uint32_t x) { return __builtin_bit_cast(float, x); }
-__device__ __forceinline__ uint32_t as_u(float x) { return __builtin_bit_cast(uint32_t, x); }
-
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                          __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-    bf16x2_t v;
-    v[0] = static_cast<__bf16>(lo);  // round to nearest even
-    v[1] = static_cast<__bf16>(hi);
-    return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ float bf16_lo(uint32_t x) { return as_f(x << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t x) { return as_f(x & 0xffff0000u); }
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return as_f(static_cast<uint32_t>(
-        __builtin_amdgcn_update_dpp(0, static_cast<int>(as_u(x)), CTRL, 0xF, 0xF, false)));
-}
 
 // Sum over the 8 lanes of a token pair (lane bits 0..2).
 __device__ __forceinline__ float sum_over_c(float x) {
@@ -151,44 +121,6 @@ __device__ __forceinline__ float sum_over_tp(float x) {
     return x;
 }
 
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-template <typename T, int D, int G>
-struct Cfg {
-    static constexpr bool kBf16 = sizeof(T) == 2;
-    static constexpr int kRowBytes = D * static_cast<int>(sizeof(T));
-    static constexpr int kChunks = kRowBytes / 16;  // 16-byte chunks per row
-    static constexpr int kCPL = kChunks / 8;        // chunks per lane per token
-    static constexpr int kDPL = D / kWave;          // output dims per lane
-    static constexpr int kPWords = kBf16 ? G * 8 : G * 16;
-    static_assert(kCPL >= 1 && kChunks % 8 == 0, "row must be a multiple of 128 bytes");
-    static_assert(kDPL >= 1, "head dim must be a multiple of 64");
-};
-
-// LDS address of a __shared__ object (what M0 takes for an LDS-DMA load).
-__device__ __forceinline__ uint32_t lds_offset(const void *p) {
-    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-        (const __attribute__((address_space(3))) char *)(p)));
-}
-
-// One global_load_lds_dwordx4: every lane reads 16 bytes at sbase + voff and
-// the wave's 64 x 16 bytes land in LDS at m0 + 16 * lane, without passing
-// through VGPRs.  The nt bit marks the stream as read-once.  Issued from asm
-// so that the compiler does not serialise the ring with vmcnt(0) before every
-// LDS read; the kernel places the exact vmcnt waits itself (wait_vmem).
-__device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t lds) {
-    asm volatile("global_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "{m0}"(lds)
-                 : "memory");
-}
-
-// Wait until at most N vector-memory operations of this wave are in flight
-// (they retire in issue order).
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 // Wait until at most `later` blocks of PER loads each are still in flight.
 template <int PER, int NBUF>
 __device__ __forceinline__ void wait_blocks(int later) {
@@ -202,39 +134,17 @@ __device__ __forceinline__ void wait_blocks(int later) {
     wait_vmem<0>();
 }
 
-__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-// One global_load_lds_dword: lane l's 4 bytes at sbase + voff land in LDS at
-// m0 + 4 * l (used for the block ids of a segment).
-__device__ __forceinline__ void dma4(const void *sbase, uint32_t voff, uint32_t lds) {
-    asm volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
-}
-
-// s_waitcnt the compiler itself understands (it then knows its own loads,
-// issued before, are complete): vmcnt(0), no wait on the other counters.
-__device__ __forceinline__ void drain_vmem() {
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    asm volatile("" ::: "memory");  // and no LDS read may be hoisted above it
-}
-
-// Inclusive prefix sum across the wave.
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int t = __shfl_up(v, d);
-        if (lane >= d) v += t;
-    }
-    return v;
-}
-
-// Blocks each work-group of the stream takes: an equal share of all
-// (sequence, KV head, block) work, and at least kMinShare so that tiny
-// batches do not split into fragments that cost more to merge than to run.
-constexpr int kMinShare = 16;
-__host__ __device__ __forceinline__ int stream_share(int total, int waves) {
-    const int r = (total + waves - 1) / waves;
-    return r > kMinShare ? r : kMinShare;
-}
+template <typename T, int D, int G>
+struct Cfg {
+    static constexpr bool kBf16 = sizeof(T) == 2;
+    static constexpr int kRowBytes = D * static_cast<int>(sizeof(T));
+    static constexpr int kChunks = kRowBytes / 16;  // 16-byte chunks per row
+    static constexpr int kCPL = kChunks / 8;        // chunks per lane per token
+    static constexpr int kDPL = D / kWave;          // output dims per lane
+    static constexpr int kPWords = kBf16 ? G * 8 : G * 16;
+    static_assert(kCPL >= 1 && kChunks % 8 == 0, "row must be a multiple of 128 bytes");
+    static_assert(kDPL >= 1, "head dim must be a multiple of 64");
+};
 
 // ---------------------------------------------------------------------------
 // Split-context partition kernel, stream-K schedule.
@@ -571,236 +481,6 @@ __global__ __launch_bounds__(kWave) void grouped_partition_kernel(
     }
 }
 
-// ---------------------------------------------------------------------------
-// Reduce over the stream-K partial slots of each (sequence, query head):
-// O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
-// One work-group of W waves per (query head, sequence); wave w takes slots
-// w, w + W, ... of the segment.
-// ---------------------------------------------------------------------------
-template <typename T, int D, int G, int W>
-__global__ __launch_bounds__(kWave *W) void stream_reduce_kernel(
-    T *__restrict__ out, const float *__restrict__ ws_acc, const float2 *__restrict__ ws_ml,
-    const int32_t *__restrict__ ws_prefix, const int32_t *__restrict__ context_lens,
-    int num_seqs, int num_kv_heads, int waves) {
-    constexpr int DPL = D / kWave;
-    const int h = blockIdx.x;
-    const int b = blockIdx.y;
-    const int g = h / G;
-    const int hh = h - g * G;
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
-    const int num_q_heads = num_kv_heads * G;
-    const int nb = (context_lens[b] + kBS - 1) / kBS;
-    T *o = out + (static_cast<int64_t>(b) * num_q_heads + h) * D + lane * DPL;
-
-    __shared__ float s_max[W];
-    __shared__ float s_num[W][D];
-    __shared__ float s_den[W];
-
-    if (nb <= 0) {  // empty context: O = 0
-        if (wave == 0)
-#pragma unroll
-            for (int d = 0; d < DPL; ++d) o[d] = static_cast<T>(0.f);
-        return;
-    }
-    const int total = num_kv_heads * ws_prefix[num_seqs];
-    const int share = stream_share(total, waves);
-    const int k = b * num_kv_heads + g;
-    const int seg_lo = num_kv_heads * ws_prefix[b] + g * nb;
-    const int w0 = seg_lo / share;
-    const int n = (seg_lo + nb - 1) / share - w0 + 1;  // partial slots of this segment
-    const int64_t first = (static_cast<int64_t>(w0) + k) * G + hh;  // row of slot w0 + k
-
-    float M = kNegInf;
-    for (int p = tid; p < n; p += kWave * W) M = fmaxf(M, ws_ml[first + static_cast<int64_t>(p) * G].x);
-    for (int sh = 32; sh >= 1; sh >>= 1) M = fmaxf(M, __shfl_xor(M, sh));
-    if constexpr (W > 1) {
-        if (lane == 0) s_max[wave] = M;
-        __syncthreads();
-        M = s_max[0];
-#pragma unroll
-        for (int w = 1; w < W; ++w) M = fmaxf(M, s_max[w]);
-    }
-
-    float num[DPL];
-#pragma unroll
-    for (int d = 0; d < DPL; ++d) num[d] = 0.f;
-    float den = 0.f;
-    for (int p = wave; p < n; p += W) {
-        const int64_t r = first + static_cast<int64_t>(p) * G;
-        const float2 mp = ws_ml[r];
-        const float wgt = exp2_fast(mp.x - M);
-        den = fmaf(wgt, mp.y, den);
-        const float *a = ws_acc + r * D + lane * DPL;
-        if constexpr (DPL % 2 == 0) {
-#pragma unroll
-            for (int d = 0; d < DPL; d += 2) {
-                const float2 v = *reinterpret_cast<const float2 *>(a + d);
-                num[d] = fmaf(wgt, v.x, num[d]);
-                num[d + 1] = fmaf(wgt, v.y, num[d + 1]);
-            }
-        } else {
-            num[0] = fmaf(wgt, a[0], num[0]);
-        }
-    }
-    if constexpr (W > 1) {
-#pragma unroll
-        for (int d = 0; d < DPL; ++d) s_num[wave][lane * DPL + d] = num[d];
-        if (lane == 0) s_den[wave] = den;
-        __syncthreads();
-        if (wave != 0) return;
-#pragma unroll
-        for (int w = 1; w < W; ++w) {
-            den += s_den[w];
-#pragma unroll
-            for (int d = 0; d < DPL; ++d) num[d] += s_num[w][lane * DPL + d];
-        }
-    }
-    if constexpr (sizeof(T) == 2) {
-        if constexpr (DPL % 2 == 0) {
-#pragma unroll
-            for (int d = 0; d < DPL; d += 2)
-                *reinterpret_cast<uint32_t *>(o + d) = pack_bf16(num[d] / den, num[d + 1] / den);
-        } else {
-            const __bf16 r = static_cast<__bf16>(num[0] / den);
-            o[0] = __builtin_bit_cast(T, r);
-        }
-    } else {
-#pragma unroll
-        for (int d = 0; d < DPL; ++d) o[d] = num[d] / den;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Log-sum-exp reduce: O = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,
-// M = max_p m_p, over the partitions that hold tokens of the sequence.
-// One work-group per (query head, sequence); wave w takes partitions w, w+W..
-// ---------------------------------------------------------------------------
-template <typename T, int D, int W>
-__global__ __launch_bounds__(kWave *W) void lse_reduce_kernel(
-    T *__restrict__ out, const float *__restrict__ ws_acc, const float2 *__restrict__ ws_ml,
-    const int32_t *__restrict__ context_lens, int num_q_heads, int num_parts, int part_tokens) {
-    constexpr int DPL = D / kWave;
-    const int h = blockIdx.x;
-    const int b = blockIdx.y;
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
-    const int ctx = context_lens[b];
-    const int n = ctx > 0 ? (ctx + part_tokens - 1) / part_tokens : 0;
-    const int64_t row = static_cast<int64_t>(b) * num_q_heads + h;
-    T *o = out + row * D + lane * DPL;
-
-    __shared__ float s_max[W];
-    __shared__ float s_num[W][D];
-    __shared__ float s_den[W];
-
-    if (n == 0) {  // empty context: O = 0
-        if (wave == 0)
-#pragma unroll
-            for (int d = 0; d < DPL; ++d) o[d] = static_cast<T>(0.f);
-        return;
-    }
-    const float2 *ml = ws_ml + row * num_parts;
-    float M = kNegInf;
-    for (int p = tid; p < n; p += kWave * W) M = fmaxf(M, ml[p].x);
-    for (int sh = 32; sh >= 1; sh >>= 1) M = fmaxf(M, __shfl_xor(M, sh));
-    if constexpr (W > 1) {
-        if (lane == 0) s_max[wave] = M;
-        __syncthreads();
-        M = s_max[0];
-#pragma unroll
-        for (int w = 1; w < W; ++w) M = fmaxf(M, s_max[w]);
-    }
-
-    float num[DPL];
-#pragma unroll
-    for (int d = 0; d < DPL; ++d) num[d] = 0.f;
-    float den = 0.f;
-    for (int p = wave; p < n; p += W) {
-        const float2 mp = ml[p];
-        const float w = exp2_fast(mp.x - M);
-        den = fmaf(w, mp.y, den);
-        const float *a = ws_acc + (row * num_parts + p) * D + lane * DPL;
-        if constexpr (DPL % 2 == 0) {
-#pragma unroll
-            for (int d = 0; d < DPL; d += 2) {
-                const float2 v = *reinterpret_cast<const float2 *>(a + d);
-                num[d] = fmaf(w, v.x, num[d]);
-                num[d + 1] = fmaf(w, v.y, num[d + 1]);
-            }
-        } else {
-            num[0] = fmaf(w, a[0], num[0]);
-        }
-    }
-    if constexpr (W > 1) {
-#pragma unroll
-        for (int d = 0; d < DPL; ++d) s_num[wave][lane * DPL + d] = num[d];
-        if (lane == 0) s_den[wave] = den;
-        __syncthreads();
-        if (wave != 0) return;
-#pragma unroll
-        for (int w = 1; w < W; ++w) {
-            den += s_den[w];
-#pragma unroll
-            for (int d = 0; d < DPL; ++d) num[d] += s_num[w][lane * DPL + d];
-        }
-    }
-    if constexpr (sizeof(T) == 2) {
-        if constexpr (DPL % 2 == 0) {
-#pragma unroll
-            for (int d = 0; d < DPL; d += 2)
-                *reinterpret_cast<uint32_t *>(o + d) = pack_bf16(num[d] / den, num[d + 1] / den);
-        } else {
-            const __bf16 r = static_cast<__bf16>(num[0] / den);
-            o[0] = __builtin_bit_cast(T, r);
-        }
-    } else {
-#pragma unroll
-        for (int d = 0; d < DPL; ++d) o[d] = num[d] / den;
-    }
-}
-
-// Work-groups of the stream: one per wave slot the partition kernel keeps
-// resident on the current device, so that every wave streams from start to
-// end.  Slots per CU = the smaller of the register limit (occupancy query)
-// and the LDS limit (CU LDS / the kernel's static LDS), rounded down to a
-// multiple of the 4 SIMDs so that every SIMD carries the same number of
-// equal shares; capped by the workspace's slot count.
-template <typename K>
-int stream_waves(K kernel) {
-    static std::atomic<int> cache[kMaxDevices];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
-    int w = cache[dev].load(std::memory_order_relaxed);
-    if (w == 0) {
-        int cus = 0, per_cu = 0, lds_cu = 0;
-        hipFuncAttributes attr{};
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kWave, 0) != hipSuccess)
-            per_cu = 0;
-        if (hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
-                                  dev) == hipSuccess &&
-            hipFuncGetAttributes(&attr, reinterpret_cast<const void *>(kernel)) == hipSuccess &&
-            attr.sharedSizeBytes > 0) {
-            const int by_lds = lds_cu / static_cast<int>(attr.sharedSizeBytes);
-            if (by_lds < per_cu) per_cu = by_lds;
-        }
-        if (per_cu >= 4) per_cu -= per_cu % 4;
-        w = cus * per_cu;
-        if (w <= 0) w = 2048;  // 256 CUs x 2 waves per SIMD
-        if (w > kStreamWavesMax) w = kStreamWavesMax;
-        cache[dev].store(w, std::memory_order_relaxed);
-    }
-    if (const char *env = std::getenv("PA_STREAM_WAVES")) {  // tuning / tests
-        const int v = std::atoi(env);
-        if (v >= 1 && v <= kStreamWavesMax) w = v;
-    }
-    return w;
-}
-
 template <typename T, int D, int G, int NBUF>
 pa_status enqueue_grouped(const DecodeShape &s, const DecodeArgs &a, const DecodePlan &p,
                           float scale_log2, hipStream_t stream, std::string *why) {
@@ -809,7 +489,7 @@ pa_status enqueue_grouped(const DecodeShape &s, const DecodeArgs &a, const Decod
     float2 *ml = reinterpret_cast<float2 *>(ws + p.ml_offset);
     int32_t *prefix = reinterpret_cast<int32_t *>(ws + p.prefix_offset);
     const auto kernel = grouped_partition_kernel<T, D, G, NBUF>;
-    const int waves = stream_waves(kernel);
+    const int waves = stream_waves(kernel, kWave, 4, kStreamWavesMax);
     hipLaunchKernelGGL(kernel, dim3(waves), dim3(kWave), 0, stream, acc, ml, prefix,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k_cache),
                        static_cast<const T *>(a.v_cache), a.block_tables, a.context_lens,
@@ -817,9 +497,9 @@ pa_status enqueue_grouped(const DecodeShape &s, const DecodeArgs &a, const Decod
     pa_status st = hip_status(hipGetLastError(), why, "partition launch");
     if (st != PA_OK) return st;
     const dim3 grid(s.num_q_heads, s.num_seqs);
-    hipLaunchKernelGGL((stream_reduce_kernel<T, D, G, 4>), grid, dim3(kWave * 4), 0, stream,
+    hipLaunchKernelGGL((stream_reduce_kernel<T, D, 4>), grid, dim3(kWave * 4), 0, stream,
                        static_cast<T *>(a.out), acc, ml, prefix, a.context_lens, s.num_seqs,
-                       s.num_kv_heads, waves);
+                       s.num_kv_heads, G, kBS, waves);
     return hip_status(hipGetLastError(), why, "reduce launch");
 }
 
@@ -842,37 +522,7 @@ pa_status enqueue_grouped_g(const DecodeShape &s, const DecodeArgs &a, const Dec
     }
 }
 
-template <typename T, int D>
-void enqueue_reduce(const DecodeShape &s, const DecodeArgs &a, const DecodePlan &p,
-                    int part_tokens, hipStream_t stream) {
-    const char *ws = static_cast<const char *>(a.workspace);
-    const float *acc = reinterpret_cast<const float *>(ws + p.acc_offset);
-    const float2 *ml = reinterpret_cast<const float2 *>(ws + p.ml_offset);
-    const dim3 grid(s.num_q_heads, s.num_seqs);
-    if (p.num_parts > 8)
-        hipLaunchKernelGGL((lse_reduce_kernel<T, D, 4>), grid, dim3(kWave * 4), 0, stream,
-                           static_cast<T *>(a.out), acc, ml, a.context_lens, s.num_q_heads,
-                           p.num_parts, part_tokens);
-    else
-        hipLaunchKernelGGL((lse_reduce_kernel<T, D, 1>), grid, dim3(kWave), 0, stream,
-                           static_cast<T *>(a.out), acc, ml, a.context_lens, s.num_q_heads,
-                           p.num_parts, part_tokens);
-}
-
 }  // namespace
-
-pa_status launch_lse_reduce(const DecodeShape &s, const DecodeArgs &a, const DecodePlan &p,
-                            int part_tokens, hipStream_t stream, std::string *why) {
-    if (s.dtype == PA_BF16) {
-        if (s.head_dim_v == 64) enqueue_reduce<uint16_t, 64>(s, a, p, part_tokens, stream);
-        else if (s.head_dim_v == 128) enqueue_reduce<uint16_t, 128>(s, a, p, part_tokens, stream);
-        else enqueue_reduce<uint16_t, 512>(s, a, p, part_tokens, stream);
-    } else {
-        if (s.head_dim_v == 64) enqueue_reduce<float, 64>(s, a, p, part_tokens, stream);
-        else enqueue_reduce<float, 128>(s, a, p, part_tokens, stream);
-    }
-    return hip_status(hipGetLastError(), why, "reduce launch");
-}
 
 pa_status launch_grouped_decode(const DecodeShape &s, const DecodeArgs &a, const DecodePlan &p,
                                 hipStream_t stream, std::string *why) {

@@ -18,13 +18,9 @@ pa_status launch_append(const AppendArgs &a, const AppendPlan &plan, hipStream_t
 pa_status launch_grouped_decode(const DecodeShape &s, const DecodeArgs &a,
                                 const DecodePlan &plan, hipStream_t stream, std::string *why);
 
-// Latent (576/512) decode on MFMA, followed by the same reduce.
+// Latent (576/512) decode on MFMA, followed by the same stream-K reduce.
 pa_status launch_latent_decode(const DecodeShape &s, const DecodeArgs &a,
                                const DecodePlan &plan, hipStream_t stream, std::string *why);
-
-// Log-sum-exp merge of the partition results into `out` (shared by both paths).
-pa_status launch_lse_reduce(const DecodeShape &s, const DecodeArgs &a, const DecodePlan &plan,
-                            int part_tokens, hipStream_t stream, std::string *why);
 
 inline pa_status hip_status(hipError_t e, std::string *why, const char *where) {
     if (e == hipSuccess) return PA_OK;

@@ -31,16 +31,6 @@ int grouped_ring_depth() {
     return 2;
 }
 
-// Latent path: 64-token blocks; 8 blocks (512 tokens) per partition.
-int latent_part_blocks() {
-    const char *env = std::getenv("PA_LATENT_PARTITION_BLOCKS");
-    if (env && *env) {
-        int v = std::atoi(env);
-        if (v >= 1 && v <= 64) return v;
-    }
-    return 8;
-}
-
 }  // namespace
 
 pa_status check_append(const AppendArgs &a, AppendPlan *plan, std::string *why) {
@@ -110,8 +100,9 @@ pa_status plan_decode(const DecodeShape &s, DecodePlan *plan, std::string *why) 
             return fail(PA_ERR_UNSUPPORTED, why,
                         "decode (latent): runs head_dim_k 576, head_dim_v 512, one KV head, "
                         "block_size 64, bf16, num_q_heads a multiple of 16 up to 128");
+        if ((int64_t)s.num_seqs * s.max_blocks_per_seq > INT32_MAX)
+            return fail(PA_ERR_SHAPE, why, "decode: num_seqs * max_blocks_per_seq exceeds 2^31-1");
         p.path = DecodePath::kLatent;
-        p.part_blocks = latent_part_blocks();
     } else {
         if (s.head_dim_k != s.head_dim_v || (s.head_dim_k != 64 && s.head_dim_k != 128))
             return fail(PA_ERR_UNSUPPORTED, why,
@@ -126,16 +117,12 @@ pa_status plan_decode(const DecodeShape &s, DecodePlan *plan, std::string *why) 
                         "decode: num_seqs * max_blocks_per_seq * num_kv_heads exceeds 2^31-1");
         p.path = DecodePath::kGrouped;
         p.ring_depth = grouped_ring_depth();
-        p.part_blocks = 0;
-        p.num_parts = 0;
     }
     size_t rows;  // (slot, head) rows of partial results
     if (p.path == DecodePath::kGrouped)
         rows = ((size_t)kStreamWavesMax + (size_t)s.num_seqs * s.num_kv_heads) * (size_t)G;
-    else {
-        p.num_parts = (s.max_blocks_per_seq + p.part_blocks - 1) / p.part_blocks;
-        rows = (size_t)s.num_seqs * s.num_q_heads * (size_t)p.num_parts;
-    }
+    else
+        rows = ((size_t)kLatentWavesMax + (size_t)s.num_seqs) * (size_t)s.num_q_heads;
     p.acc_offset = 0;
     p.ml_offset = round_up(rows * s.head_dim_v * sizeof(float), kWorkspaceAlign);
     p.prefix_offset = round_up(p.ml_offset + rows * 2 * sizeof(float), kWorkspaceAlign);

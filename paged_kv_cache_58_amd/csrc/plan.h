@@ -46,6 +46,10 @@ enum class DecodePath { kGrouped, kLatent };
 // workspace: a partial slot per work-group plus one per (sequence, KV head).
 constexpr int kStreamWavesMax = 4096;
 
+// Most work-groups of the latent path (one per CU; each covers every query
+// head of a block), which sizes its workspace the same way.
+constexpr int kLatentWavesMax = 512;
+
 struct DecodeShape {
     int32_t num_seqs;
     int32_t num_q_heads;
@@ -65,13 +69,11 @@ struct DecodeShape {
 //    each holding the G heads of one KV group; plus the per-sequence block
 //    prefix sums (num_seqs + 1 int32) the partition kernel leaves for the
 //    reduce.
-//  * latent: fixed partitions of part_blocks blocks; slots = num_seqs *
-//    num_parts, each holding all query heads.
+//  * latent: stream-K as well, with one work-group per CU; slots =
+//    kLatentWavesMax + num_seqs, each holding all query heads.
 struct DecodePlan {
     DecodePath path;
     int group;             // query heads per KV head
-    int part_blocks;       // latent path: cache blocks per partition
-    int num_parts;         // latent path: partitions per sequence at max_blocks_per_seq
     int ring_depth;        // grouped path: cache blocks streaming into LDS per wave (2 or 4)
     size_t acc_offset;     // float [slots, heads per slot, head_dim_v]
     size_t ml_offset;      // float2 [slots, heads per slot] = (max, sum)

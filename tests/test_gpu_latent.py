@@ -1,0 +1,105 @@
+"""GPU parity of the latent (MLA-style) pa_decode path against the CPU oracle:
+one 576-wide cached latent per token is the key and its first 512 values the
+value, shared by every query head."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import compare, host_array, say, to_device, widen
+from workloads import custom_spec, make_workload
+
+pytestmark = pytest.mark.gpu
+
+SCALE = 1.0 / math.sqrt(576)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def _spec(hq, ctx, scale=SCALE):
+    return custom_spec(len(ctx), hq, 1, 576, 64, "bf16", ctx=ctx, head_dim_v=512, mla=True,
+                       scale=scale)
+
+
+@pytest.mark.parametrize("hq,ctx", [
+    (128, [1, 63, 64, 65, 700]),
+    (16, [0, 130, 1000]),
+    (32, [200, 5]),
+    (48, [64, 129, 300]),
+    (80, [1, 500]),
+])
+def test_latent_parity_small(dev, hq, ctx):
+    say(f"case: latent Hq={hq} ctx={ctx}")
+    w = make_workload(_spec(hq, ctx), seed=20 + hq)
+    d = to_device(w, dev)
+    say(f"  {compare(d.decode(), oracle.decode_workload(w), 'bf16')}")
+
+
+def test_latent_rescale_heavy(dev):
+    say("case: latent, scale 1 (wide score range)")
+    w = make_workload(_spec(64, [900, 333], scale=0.5), seed=3)
+    d = to_device(w, dev)
+    say(f"  {compare(d.decode(), oracle.decode_workload(w), 'bf16')}")
+
+
+def test_latent_context_one_is_v_bitwise(dev):
+    say("case: latent ctx=1")
+    w = make_workload(_spec(128, [1, 1, 1]), seed=4)
+    got = host_array(to_device(w, dev).decode())
+    for b in range(3):
+        row = w.k_cache[w.block_tables[b, 0], 0, 0, :512]
+        want = np.broadcast_to(row, (128, 512))
+        assert np.array_equal(got[b].view(np.uint16), want)
+
+
+def test_latent_poison_and_determinism(dev):
+    say("case: latent NaN poison vs zero fill, two runs")
+    w = make_workload(_spec(32, [70, 1, 190]), seed=5)
+    d = to_device(w, dev)
+    a = host_array(d.decode())
+    assert np.array_equal(a, host_array(d.decode()))
+    w.k_cache = np.where(np.isnan(widen(w.k_cache)), np.uint16(0), w.k_cache)
+    b = host_array(to_device(w, dev).decode())
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("waves", ["1", "3", "7", "512"])
+def test_latent_stream_split(dev, waves, monkeypatch):
+    say(f"case: latent, {waves} stream work-groups")
+    monkeypatch.setenv("PA_STREAM_WAVES", waves)
+    w = make_workload(_spec(128, [1, 1300, 0, 4100, 64]), seed=6)
+    d = to_device(w, dev)
+    say(f"  {compare(d.decode(), oracle.decode_workload(w), 'bf16')}")
+
+
+def test_latent_append_then_decode(dev):
+    say("case: latent append + decode(ctx + 1)")
+    w = make_workload(_spec(128, [63, 64, 500]), seed=7)
+    d = to_device(w, dev)
+    hk = w.k_cache.copy()
+    oracle.append(hk, None, w.k_new, None, w.slot_mapping)
+    d.append()
+    L1 = w.context_lens + 1
+    out = d.decode(context_lens=torch.from_numpy(L1).to(dev))
+    ref = oracle.decode(w.q, hk, None, w.block_tables, L1, w.scale, head_dim_v=512)
+    say(f"  {compare(out, ref, 'bf16')}")
+
+
+def test_config5_full(dev):
+    say("case: full config c5 (MLA latent decode)")
+    w = make_workload("c5")
+    d = to_device(w, dev)
+    rng = np.random.default_rng(0)
+    rows = [(int(b), int(h)) for b, h in zip(rng.integers(0, 64, 256), rng.integers(0, 128, 256))]
+    ref = oracle.decode_workload(w, pairs=rows)
+    say(f"  c5 sampled rows: {compare(d.decode(), ref, 'bf16', rows=rows)}")
+    del d
+    torch.cuda.empty_cache()
