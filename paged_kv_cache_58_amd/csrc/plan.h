@@ -49,6 +49,13 @@ constexpr int kStreamWavesMax = 4096;
 // Most work-groups of the latent path (one per CU; each covers every query
 // head of a block), which sizes its workspace the same way.
 constexpr int kLatentWavesMax = 512;
+// Query heads one wave of the latent path covers in its scores.
+constexpr int kLatentHeadTile = 32;
+// Waves of a latent work-group: one per 32 query heads, rounded up to 1, 2
+// or 4 (the 512 output dims are split evenly over the waves).
+inline int latent_waves(int num_q_heads) {
+    return num_q_heads <= kLatentHeadTile ? 1 : num_q_heads <= 2 * kLatentHeadTile ? 2 : 4;
+}
 
 struct DecodeShape {
     int32_t num_seqs;
@@ -70,7 +77,11 @@ struct DecodeShape {
 //    prefix sums (num_seqs + 1 int32) the partition kernel leaves for the
 //    reduce.
 //  * latent: stream-K as well, with one work-group per CU; slots =
-//    kLatentWavesMax + num_seqs, each holding all query heads.
+//    kLatentWavesMax + num_seqs, each holding latent_waves(num_q_heads) * 32
+//    heads (the query heads, padded).  There the accumulator of a slot is
+//    stored in the partition kernel's register order, HT = latent_waves
+//    head tiles: float4 index ((dt * HT + ht) * 4 + qd) * 64 + lane holds
+//    dims 32 dt + 8 qd + 4 (lane >> 5) .. + 3 of head 32 ht + (lane & 31).
 struct DecodePlan {
     DecodePath path;
     int group;             // query heads per KV head
