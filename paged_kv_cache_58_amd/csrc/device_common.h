@@ -87,6 +87,22 @@ __device__ __forceinline__ void drain_vmem() {
     asm volatile("" ::: "memory");  // and no LDS read may be hoisted above it
 }
 
+// Marks a value loaded from global memory as settled: the compiler waits for
+// its load here (it sees the asm read it), and every later use reads the
+// asm's output, not a pending load.  Loads issued before the LDS-DMA ring
+// starts go through this, or the compiler's own vmcnt waits in the loop (it
+// cannot count the ring's asm loads) would drain the ring at every step.
+template <typename V>
+__device__ __forceinline__ void settle(V &v) {
+    asm volatile("" : "+v"(v));
+}
+__device__ __forceinline__ void settle(uint4 &v) {
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    u4 x = __builtin_bit_cast(u4, v);
+    asm volatile("" : "+v"(x));
+    v = __builtin_bit_cast(uint4, x);
+}
+
 // Inclusive prefix sum across the wave.
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
@@ -209,16 +225,17 @@ __global__ __launch_bounds__(kWave *W) void stream_reduce_kernel(
     }
 }
 
-// Work-groups of a stream: one per slot the partition kernel keeps resident
-// on the current device, so that every work-group streams from start to
-// end.  Slots per CU = the smaller of the register limit (occupancy query)
+// Stream shares of a partition kernel: one per wave slot it keeps resident
+// on the current device, so that every share streams from start to end.
+// Work-groups per CU = the smaller of the register limit (occupancy query)
 // and the LDS limit (CU LDS / the kernel's static LDS), rounded down to a
-// multiple of per_cu_multiple (4 for one-wave work-groups, so every SIMD
-// carries the same number of equal shares); capped by the workspace's slot
-// count.  The value is cached per device and kernel instantiation;
-// PA_STREAM_WAVES overrides it (tuning and tests).
+// multiple of per_cu_multiple; shares = work-groups x waves_per_group
+// (each wave of a work-group streams its own share), capped by the
+// workspace's slot count.  The value is cached per device and kernel
+// instantiation; PA_STREAM_WAVES overrides it (tuning and tests).  Launch
+// ceil(shares / waves_per_group) work-groups.
 template <typename K>
-int stream_waves(K kernel, int threads, int per_cu_multiple, int cap) {
+int stream_waves(K kernel, int threads, int per_cu_multiple, int cap, int waves_per_group = 1) {
     static std::atomic<int> cache[kMaxDevices];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
@@ -238,7 +255,7 @@ int stream_waves(K kernel, int threads, int per_cu_multiple, int cap) {
             if (by_lds < per_cu) per_cu = by_lds;
         }
         if (per_cu >= per_cu_multiple) per_cu -= per_cu % per_cu_multiple;
-        w = cus * per_cu;
+        w = cus * per_cu * waves_per_group;
         if (w <= 0) w = 256;
         if (w > cap) w = cap;
         cache[dev].store(w, std::memory_order_relaxed);

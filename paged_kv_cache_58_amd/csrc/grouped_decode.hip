@@ -13,7 +13,9 @@
 // attention kernel is the modification described in "Modification de
 // l'Attention" of the KV-sparsity article).
 //
-// gfx950 mapping (one wave64 work-group per (partition, KV head, sequence)):
+// gfx950 mapping (each wave64 streams its own share of the blocks; a
+// work-group holds kGroupWaves such independent waves, which the hardware
+// places one per SIMD):
 //  * A 16-token cache block of one KV head is 16 rows of D elements.  Lane
 //    (tp = lane / 8, c = lane % 8) owns rows 2tp and 2tp+1, 16-byte chunks
 //    c, c+8, ...: every load is 16 bytes wide and each group of 8 lanes reads
@@ -146,12 +148,22 @@ struct Cfg {
     static_assert(kDPL >= 1, "head dim must be a multiple of 64");
 };
 
+// Independent streaming waves per work-group: 4 (one per SIMD) when their
+// LDS fits in a CU's 160 KB, else 2, else 1.
+template <typename T, int D, int G, int NBUF>
+constexpr int group_waves() {
+    using C = Cfg<T, D, G>;
+    constexpr int per_wave = NBUF * 2 * 2 * C::kCPL * kWave * 16 + C::kPWords * 4 + 2 * kWave * 4 + 8 * 4;
+    return 4 * per_wave <= 160 * 1024 ? 4 : 2 * per_wave <= 160 * 1024 ? 2 : 1;
+}
+
 // ---------------------------------------------------------------------------
 // Split-context partition kernel, stream-K schedule.
 //
 // All (sequence b, KV head g, cache block) work items are laid out in one
-// global order (b, then g, then block) and cut into gridDim.x equal shares;
-// work-group w streams share w, which may cross from one (b, g) "segment" to
+// global order (b, then g, then block) and cut into nshares equal shares;
+// wave w of work-group k streams share s = kGroupWaves k + w, which may cross
+// from one (b, g) "segment" to
 // the next.  For each segment it touches it leaves (acc, max, sum) of the G
 // query heads in partial slot w + (b * Hkv + g); the slots of one segment are
 // therefore consecutive, from w0 + k to w1 + k where w0 and w1 are the first
@@ -160,12 +172,12 @@ struct Cfg {
 // prefix sums for the reduce.  Launched with one work-group per resident
 // wave slot, so every wave streams for the whole kernel.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int G, int NBUF>
-__global__ __launch_bounds__(kWave) void grouped_partition_kernel(
+template <typename T, int D, int G, int NBUF, int kGroupWaves = group_waves<T, D, G, NBUF>()>
+__global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
     float *__restrict__ ws_acc, float2 *__restrict__ ws_ml, int32_t *__restrict__ ws_prefix,
     const T *__restrict__ q, const T *__restrict__ k_cache, const T *__restrict__ v_cache,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
-    float scale_log2, int num_seqs, int num_kv_heads, int max_blocks) {
+    float scale_log2, int num_seqs, int num_kv_heads, int max_blocks, int nshares) {
     using C = Cfg<T, D, G>;
     constexpr int CPL = C::kCPL;
     constexpr int DPL = C::kDPL;
@@ -174,7 +186,10 @@ __global__ __launch_bounds__(kWave) void grouped_partition_kernel(
     constexpr int SLOT_U4 = PER_BLOCK * kWave;
     static_assert((NBUF & (NBUF - 1)) == 0 && NBUF >= 2 && NBUF <= 4, "ring depth 2 or 4");
 
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int sid = blockIdx.x * kGroupWaves + wave;  // this wave's share
+    if (sid >= nshares) return;  // uniform over the wave; waves never wait on each other
     const int tp = lane >> 3;
     const int c = lane & 7;
     constexpr int LPH = 8 / G;                // lanes of a token pair per head
@@ -185,10 +200,15 @@ __global__ __launch_bounds__(kWave) void grouped_partition_kernel(
     // Ring of NBUF blocks.  Slot layout: K then V, each KV_INSTR rows of 64
     // lanes x 16 bytes; row (j * CPL + i), lane (tp, c) = token 2 tp + j,
     // 16-byte chunk c + 8 i of the row.
-    __shared__ __attribute__((aligned(16))) uint4 s_ring[NBUF * SLOT_U4];
-    __shared__ __attribute__((aligned(16))) uint32_t s_p[C::kPWords];
-    __shared__ __attribute__((aligned(16))) int32_t s_ids[2][kWave];
-    __shared__ float s_alpha[8];
+    // (every wave of the work-group has its own)
+    __shared__ __attribute__((aligned(16))) uint4 s_ring_all[kGroupWaves][NBUF * SLOT_U4];
+    __shared__ __attribute__((aligned(16))) uint32_t s_p_all[kGroupWaves][C::kPWords];
+    __shared__ __attribute__((aligned(16))) int32_t s_ids_all[kGroupWaves][2][kWave];
+    __shared__ float s_alpha_all[kGroupWaves][8];
+    uint4 *s_ring = s_ring_all[wave];
+    uint32_t *s_p = s_p_all[wave];
+    int32_t(*s_ids)[kWave] = s_ids_all[wave];
+    float *s_alpha = s_alpha_all[wave];
 
     // ---- this work-group's share of the global block order ----------------
     int seq_blocks_total = 0;
@@ -196,13 +216,13 @@ __global__ __launch_bounds__(kWave) void grouped_partition_kernel(
         const int bb = base + lane;
         const int nb = bb < num_seqs ? (context_lens[bb] + kBS - 1) / kBS : 0;
         const int incl = wave_incl_scan(nb, lane);
-        if (blockIdx.x == 0 && bb < num_seqs) ws_prefix[bb] = seq_blocks_total + incl - nb;
+        if (sid == 0 && bb < num_seqs) ws_prefix[bb] = seq_blocks_total + incl - nb;
         seq_blocks_total += __builtin_amdgcn_readlane(incl, kWave - 1);
     }
-    if (blockIdx.x == 0 && lane == 0) ws_prefix[num_seqs] = seq_blocks_total;
+    if (sid == 0 && lane == 0) ws_prefix[num_seqs] = seq_blocks_total;
     const int total = num_kv_heads * seq_blocks_total;
-    const int share = stream_share(total, static_cast<int>(gridDim.x));
-    const int64_t x0l = static_cast<int64_t>(blockIdx.x) * share;
+    const int share = stream_share(total, nshares);
+    const int64_t x0l = static_cast<int64_t>(sid) * share;
     if (x0l >= total) return;
     const int x0 = static_cast<int>(x0l);
     const int x1 = min(x0 + share, total);
@@ -267,6 +287,10 @@ __global__ __launch_bounds__(kWave) void grouped_partition_kernel(
                 for (int i = 0; i < CPL; ++i)
                     qv[h][i] = *reinterpret_cast<const uint4 *>(qb + h * C::kRowBytes +
                                                                 (c + 8 * i) * 16);
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int i = 0; i < CPL; ++i) settle(qv[h][i]);
         }
         // Byte offsets, inside one physical block, of this lane's two rows.
         uint32_t off[2][CPL];
@@ -362,7 +386,7 @@ __global__ __launch_bounds__(kWave) void grouped_partition_kernel(
                 l_run *= alpha;
                 m_run = m_new;
                 if (tp == 0 && head_writer) s_alpha[hc] = alpha;
-                __syncthreads();
+                wait_lds();  // the wave's own LDS writes are complete
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
                     const float a = s_alpha[h];
@@ -373,7 +397,7 @@ __global__ __launch_bounds__(kWave) void grouped_partition_kernel(
             const float p0 = exp2_fast(x2[0] - m_run);
             const float p1 = exp2_fast(x2[1] - m_run);
 
-            __syncthreads();  // the previous block's reads of s_p are done
+            wait_lds();  // the previous block's reads of s_p are done
             if constexpr (C::kBf16) {
                 const uint32_t pk = pack_bf16(p0, p1);
                 l_run += bf16_lo(pk) + bf16_hi(pk);
@@ -383,7 +407,7 @@ __global__ __launch_bounds__(kWave) void grouped_partition_kernel(
                 if (head_writer)
                     *reinterpret_cast<float2 *>(&s_p[hc * 16 + 2 * tp]) = make_float2(p0, p1);
             }
-            __syncthreads();
+            wait_lds();  // this wave's probabilities are in LDS
 
             // ---- P.V for all G heads of this lane's dims -------------------
             const uint32_t *vw =
@@ -455,7 +479,7 @@ __global__ __launch_bounds__(kWave) void grouped_partition_kernel(
         // ---- this segment's partial: unnormalised acc, running max and sum ----
         const float l_tot = sum_over_tp(l_run);
         const int64_t slot_row =
-            (static_cast<int64_t>(blockIdx.x) + static_cast<int64_t>(b) * num_kv_heads + g) * G;
+            (static_cast<int64_t>(sid) + static_cast<int64_t>(b) * num_kv_heads + g) * G;
         if (tp == 0 && head_writer) ws_ml[slot_row + hc] = make_float2(m_run, l_tot);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -489,11 +513,13 @@ pa_status enqueue_grouped(const DecodeShape &s, const DecodeArgs &a, const Decod
     float2 *ml = reinterpret_cast<float2 *>(ws + p.ml_offset);
     int32_t *prefix = reinterpret_cast<int32_t *>(ws + p.prefix_offset);
     const auto kernel = grouped_partition_kernel<T, D, G, NBUF>;
-    const int waves = stream_waves(kernel, kWave, 4, kStreamWavesMax);
-    hipLaunchKernelGGL(kernel, dim3(waves), dim3(kWave), 0, stream, acc, ml, prefix,
+    constexpr int kGroupWaves = group_waves<T, D, G, NBUF>();
+    const int waves = stream_waves(kernel, kWave * kGroupWaves, 1, kStreamWavesMax, kGroupWaves);
+    const int groups = (waves + kGroupWaves - 1) / kGroupWaves;
+    hipLaunchKernelGGL(kernel, dim3(groups), dim3(kWave * kGroupWaves), 0, stream, acc, ml, prefix,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k_cache),
                        static_cast<const T *>(a.v_cache), a.block_tables, a.context_lens,
-                       scale_log2, s.num_seqs, s.num_kv_heads, s.max_blocks_per_seq);
+                       scale_log2, s.num_seqs, s.num_kv_heads, s.max_blocks_per_seq, waves);
     pa_status st = hip_status(hipGetLastError(), why, "partition launch");
     if (st != PA_OK) return st;
     const dim3 grid(s.num_q_heads, s.num_seqs);

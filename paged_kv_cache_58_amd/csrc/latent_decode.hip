@@ -255,6 +255,8 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
                 q + (static_cast<int64_t>(b) * num_heads + head) * kDK + 8 * hk);
 #pragma unroll
             for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = __builtin_bit_cast(bf16x8_t, qr[2 * ks]);
+#pragma unroll
+            for (int ks = 0; ks < kKSteps; ++ks) settle(qf[ks]);
         } else {
 #pragma unroll
             for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = bf16x8_t{};

@@ -27,8 +27,8 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 // deeper ring with fewer waves.  PA_RING_DEPTH (2 or 4) overrides it.
 int grouped_ring_depth() {
     const char *env = std::getenv("PA_RING_DEPTH");
-    if (env && *env && std::atoi(env) == 4) return 4;
-    return 2;
+    if (env && *env && std::atoi(env) == 2) return 2;
+    return 4;
 }
 
 }  // namespace
