@@ -16,9 +16,9 @@
 //  * A work-group has NW = 1, 2 or 4 waves, one per SIMD, and covers 32 NW
 //    heads (the query heads, padded).  The latent is streamed in units of 32
 //    tokens (half a 64-token block, 36 KB) by global_load_lds_dwordx4 into a
-//    four-slot LDS ring: three units are in flight while one is read, by
-//    every wave, from LDS.  Rows past the context are zero-filled instead of
-//    fetched.
+//    four-slot LDS ring: two units are in flight while one is read, by
+//    every wave, from LDS (deeper read-ahead only stalled the in-order waves
+//    at issue).  Rows past the context are zero-filled instead of fetched.
 //  * Scores: wave w computes S^T[token, head] = L[token, :] . Q^T for heads
 //    32w..32w+31; the latent rows are the A operand (16 contiguous bytes per
 //    lane) and q sits in registers as the B operand for the whole segment.
@@ -60,7 +60,9 @@ constexpr int kBlockB = kLBS * kRowB;         // 72 KB per block in HBM
 constexpr int kUnitTok = 32;                  // tokens per ring slot (half a block)
 constexpr int kUnitMainB = kUnitTok * kMainRowB;  // 32 KB main region
 constexpr int kUnitB = kUnitTok * kRowB;      // 36 KB per slot
-constexpr int kSlots = 4;                     // ring depth: 3 units in flight
+constexpr int kAhead = 2;                     // units in flight while one is computed
+constexpr int kSlots = 4;                     // ring slots (a power of two keeps the
+                                              // slot arithmetic in shifts and immediates)
 constexpr int kDmaPerUnit = kUnitB / 1024;    // 36: 32 main rows + 4 groups of 8 RoPE rows
 constexpr int kHeads = 32;                    // heads per wave in the scores (one tile)
 constexpr int kKSteps = kDK / 16;             // 36 k-steps of q . L
@@ -365,11 +367,19 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
             // online softmax: reg j holds token 8 (j >> 2) + 4 hk + (j & 3) of
             // the unit for this lane's head
             float lmax = kNegInf;
+            if (tok0 + kUnitTok <= ctx) {  // every unit but a sequence's last
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int tk = tok0 + 8 * (j >> 2) + 4 * hk + (j & 3);
-                sa[j] = tk < ctx ? (sa[j] + sb[j]) * scale_log2 : kNegInf;
-                lmax = fmaxf(lmax, sa[j]);
+                for (int j = 0; j < 16; ++j) {
+                    sa[j] = (sa[j] + sb[j]) * scale_log2;
+                    lmax = fmaxf(lmax, sa[j]);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int tk = tok0 + 8 * (j >> 2) + 4 * hk + (j & 3);
+                    sa[j] = tk < ctx ? (sa[j] + sb[j]) * scale_log2 : kNegInf;
+                    lmax = fmaxf(lmax, sa[j]);
+                }
             }
             const float bmax = fmaxf(lmax, __shfl_xor(lmax, 32));
             const bool moved = __builtin_amdgcn_ballot_w64(bmax > m_run + kLSlack) != 0;
@@ -443,7 +453,7 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
             }
         };
 
-        for (int u = 0; u < nunits && u < kSlots - 1; ++u) {
+        for (int u = 0; u < nunits && u < kAhead; ++u) {
             refill_ids(u);
             const char *src = unit_src(u, __builtin_amdgcn_readfirstlane(unit_id(u)));
             for (int k = 0; k < kPer; ++k) issue_row(u, src, k);
@@ -451,11 +461,11 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
         for (int u = 0; u < nunits; ++u) {
             // unit un streams in during this step; its block id is read before
             // the barrier, whose LDS wait covers the read
-            const int un = u + kSlots - 1 < nunits ? u + kSlots - 1 : -1;
+            const int un = u + kAhead < nunits ? u + kAhead : -1;
             const int idn = un >= 0 ? unit_id(un) : 0;
             // this wave's rows of unit u have landed once at most the units
             // issued after it are outstanding
-            const int later = min(nunits - 1 - u, kSlots - 2);
+            const int later = min(nunits - 1 - u, kAhead - 1);
             if (later >= 2 && 2 * kPer <= 63) wait_vmem<(2 * kPer <= 63 ? 2 * kPer : 0)>();
             else if (later >= 1 && kPer <= 63) wait_vmem<(kPer <= 63 ? kPer : 0)>();
             else wait_vmem<0>();
