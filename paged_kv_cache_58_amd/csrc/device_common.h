@@ -29,6 +29,14 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                           __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// The first dot product of a chain, accumulating onto the constant 0 (the
+// VOP3 form; the compiler would otherwise zero a register for v_dot2c).
+__device__ __forceinline__ float dot2_bf16_0(uint32_t a, uint32_t b) {
+    float r;
+    asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     bf16x2_t v;
     v[0] = static_cast<__bf16>(lo);  // round to nearest even
@@ -42,7 +50,7 @@ __device__ __forceinline__ float bf16_hi(uint32_t x) { return as_f(x & 0xffff000
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
     return as_f(static_cast<uint32_t>(
-        __builtin_amdgcn_update_dpp(0, static_cast<int>(as_u(x)), CTRL, 0xF, 0xF, false)));
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(as_u(x)), CTRL, 0xF, 0xF, true)));
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

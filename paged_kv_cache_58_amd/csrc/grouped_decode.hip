@@ -62,49 +62,38 @@ __device__ __forceinline__ float sum_over_c(float x) {
 
 // The 8 lanes of a token pair each hold partial dot products over their own
 // dims for both tokens and all G heads.  Reduce-scatter them so that lane c
-// ends with the full sums (both tokens) of head c / (8 / G): each step keeps
-// half of the remaining heads (chosen by one lane bit) and adds the partner's
-// partials of that half.  Partners: row_half_mirror (c <-> 7 - c) splits on
-// bit 2, quad_perm 2301 (c ^ 2) on bit 1, quad_perm 1032 (c ^ 1) on bit 0; once
-// one head is left the remaining steps are plain all-reduce adds.
-template <int CTRL, int N>
-__device__ __forceinline__ void halve(const float (&in)[2][2 * N], float (&out)[2][N], bool upper) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int k = 0; k < N; ++k) {
-            const float keep = upper ? in[j][N + k] : in[j][k];
-            const float send = upper ? in[j][k] : in[j][N + k];
-            out[j][k] = keep + dpp<CTRL>(send);
-        }
-}
-
+// ends with the full sums (both tokens) of its head hc = c / (8 / G).  Each
+// lane stores its partials in a lane-dependent order: slot i holds head
+// i ^ hc (q is loaded in that order).  A step with partner c ^ m (m = 7:
+// row_half_mirror, m = 2: quad_perm 2301, m = 1: quad_perm 1032) keeps the
+// lower half of the slots, whose heads share the lane's bit of hc, and adds
+// the partner's slot i ^ (m >> s) (s = log2(8 / G)), which holds the same
+// head there; the slot index is the same on every lane, so no select is
+// needed.  Once one head is left the remaining steps are plain all-reduce adds.
 template <int G>
-__device__ __forceinline__ void reduce_scatter_c(const float (&a)[2][G], int c, float (&x)[2]) {
-    const bool b2 = (c >> 2) & 1, b1 = (c >> 1) & 1, b0 = c & 1;
-    if constexpr (G == 8) {
-        float r1[2][4], r2[2][2], r3[2][1];
-        halve<0x141, 4>(a, r1, b2);
-        halve<0x4E, 2>(r1, r2, b1);
-        halve<0xB1, 1>(r2, r3, b0);
-        x[0] = r3[0][0];
-        x[1] = r3[1][0];
-    } else if constexpr (G == 4) {
-        float r1[2][2], r2[2][1];
-        halve<0x141, 2>(a, r1, b2);
-        halve<0x4E, 1>(r1, r2, b1);
-        x[0] = r2[0][0] + dpp<0xB1>(r2[0][0]);
-        x[1] = r2[1][0] + dpp<0xB1>(r2[1][0]);
-    } else if constexpr (G == 2) {
-        float r1[2][1];
-        halve<0x141, 1>(a, r1, b2);
-        x[0] = r1[0][0] + dpp<0x4E>(r1[0][0]);
-        x[1] = r1[1][0] + dpp<0x4E>(r1[1][0]);
-        x[0] += dpp<0xB1>(x[0]);
-        x[1] += dpp<0xB1>(x[1]);
-    } else {
-        x[0] = sum_over_c(a[0][0]);
-        x[1] = sum_over_c(a[1][0]);
+__device__ __forceinline__ void reduce_scatter_c(const float (&a)[2][G], float (&x)[2]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        if constexpr (G == 8) {
+            float r1[4], r2[2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r1[i] = a[j][i] + dpp<0x141>(a[j][i ^ 7]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) r2[i] = r1[i] + dpp<0x4E>(r1[i ^ 2]);
+            x[j] = r2[0] + dpp<0xB1>(r2[1]);
+        } else if constexpr (G == 4) {
+            float r1[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) r1[i] = a[j][i] + dpp<0x141>(a[j][i ^ 3]);
+            const float r2 = r1[0] + dpp<0x4E>(r1[1]);
+            x[j] = r2 + dpp<0xB1>(r2);
+        } else if constexpr (G == 2) {
+            float r1 = a[j][0] + dpp<0x141>(a[j][1]);
+            r1 += dpp<0x4E>(r1);
+            x[j] = r1 + dpp<0xB1>(r1);
+        } else {
+            x[j] = sum_over_c(a[j][0]);
+        }
     }
 }
 
@@ -277,6 +266,7 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
         if (nblk > kWave) fetch_ids(1);
 
         // q slices: chunk (c + 8 i) of each of the G heads of this group.
+        // slot h holds head h ^ hc (the order reduce_scatter_c works in)
         uint4 qv[G][CPL];
         {
             const char *qb = reinterpret_cast<const char *>(q) +
@@ -285,7 +275,7 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
             for (int h = 0; h < G; ++h)
 #pragma unroll
                 for (int i = 0; i < CPL; ++i)
-                    qv[h][i] = *reinterpret_cast<const uint4 *>(qb + h * C::kRowBytes +
+                    qv[h][i] = *reinterpret_cast<const uint4 *>(qb + (h ^ hc) * C::kRowBytes +
                                                                 (c + 8 * i) * 16);
 #pragma unroll
             for (int h = 0; h < G; ++h)
@@ -359,7 +349,8 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
 #pragma unroll
                     for (int i = 0; i < CPL; ++i) {
                         if constexpr (C::kBf16) {
-                            a = dot2_bf16(qv[h][i].x, kr[j][i].x, a);
+                            a = i == 0 ? dot2_bf16_0(qv[h][i].x, kr[j][i].x)
+                                       : dot2_bf16(qv[h][i].x, kr[j][i].x, a);
                             a = dot2_bf16(qv[h][i].y, kr[j][i].y, a);
                             a = dot2_bf16(qv[h][i].z, kr[j][i].z, a);
                             a = dot2_bf16(qv[h][i].w, kr[j][i].w, a);
@@ -375,7 +366,7 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
 
             // ---- online softmax for head hc --------------------------------
             float x2[2];
-            reduce_scatter_c<G>(part_dot, c, x2);
+            reduce_scatter_c<G>(part_dot, x2);
 #pragma unroll
             for (int j = 0; j < 2; ++j) x2[j] = valid[j] ? x2[j] * scale_log2 : kNegInf;
             const float xmax = fmaxf(x2[0], x2[1]);
