@@ -18,7 +18,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 ARCH = "gfx950"
 
-SOURCES = ["plan.cpp", "api.cpp", "append.hip", "grouped_decode.hip", "latent_decode.hip"]
+SOURCES = ["plan.cpp", "api.cpp", "append.hip", "grouped_decode.hip", "gqa_mfma_decode.hip",
+           "latent_decode.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 
@@ -26,6 +27,10 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", "-fvisibility=hidden", "-Wall",
           "-I", INCLUDE, "-I", CSRC]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
           "-packed-fp32-ops"]
+# Per-source extras.  The matrix-core grouped kernel keeps its accumulators in
+# ordinary VGPRs (its rare rescale multiplies them on the VALU; in the
+# accumulation registers every block would copy them out and back).
+EXTRA = {"gqa_mfma_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:
@@ -34,7 +39,7 @@ def _compile(src: str) -> str:
     if src == "plan.cpp":  # pure C++: no HIP headers, built by the host compiler
         cmd = ["g++", *COMMON, "-c", path, "-o", obj]
     else:
-        cmd = [HIPCC, *DEVICE, *COMMON, "-x", "hip", "-c", path, "-o", obj]
+        cmd = [HIPCC, *DEVICE, *COMMON, *EXTRA.get(src, []), "-x", "hip", "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

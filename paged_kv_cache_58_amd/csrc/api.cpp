@@ -89,6 +89,8 @@ PA_EXPORT pa_status pa_decode(void *out, const void *q, const void *k_cache,
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if (plan.path == pa::DecodePath::kLatent)
         st = pa::launch_latent_decode(s, a, plan, hs, &why);
+    else if (plan.path == pa::DecodePath::kGroupedMfma)
+        st = pa::launch_gqa_mfma_decode(s, a, plan, hs, &why);
     else
         st = pa::launch_grouped_decode(s, a, plan, hs, &why);
     return finish(st, why);

@@ -130,6 +130,60 @@ __host__ __device__ __forceinline__ int stream_share(int total, int waves) {
     return r > kMinShare ? r : kMinShare;
 }
 
+// Where stream share `sid` of `nshares` lies in the global (sequence, KV
+// head, block) order of a batch of bs-token blocks: blocks [x0, x1), the
+// first of them block `blk` of segment (b, g), sequence b having nbb
+// blocks.  Share 0 also stores the per-sequence block prefix sums
+// (num_seqs + 1 entries) that the reduce reads.  Uniform over the wave;
+// returns false for a share past the end of the work.
+struct ShareSpan {
+    int x0, x1, b, nbb, g, blk;
+};
+__device__ __forceinline__ bool find_share(int sid, int nshares, int num_seqs, int num_kv_heads,
+                                           int bs, const int32_t *__restrict__ context_lens,
+                                           int32_t *__restrict__ ws_prefix, int lane,
+                                           ShareSpan &sp) {
+    int seq_blocks_total = 0;
+    for (int base = 0; base < num_seqs; base += kWave) {
+        const int bb = base + lane;
+        const int nb = bb < num_seqs ? (context_lens[bb] + bs - 1) / bs : 0;
+        const int incl = wave_incl_scan(nb, lane);
+        if (sid == 0 && bb < num_seqs) ws_prefix[bb] = seq_blocks_total + incl - nb;
+        seq_blocks_total += __builtin_amdgcn_readlane(incl, kWave - 1);
+    }
+    if (sid == 0 && lane == 0) ws_prefix[num_seqs] = seq_blocks_total;
+    const int total = num_kv_heads * seq_blocks_total;
+    const int share = stream_share(total, nshares);
+    const int64_t x0l = static_cast<int64_t>(sid) * share;
+    if (x0l >= total) return false;
+    sp.x0 = static_cast<int>(x0l);
+    sp.x1 = min(sp.x0 + share, total);
+
+    // The sequence holding global block x0: first b whose blocks end past it.
+    sp.b = 0;
+    sp.nbb = 0;
+    int cb = 0;
+    for (int base = 0, carry = 0;; base += kWave) {
+        const int bb = base + lane;
+        const int nb = bb < num_seqs ? (context_lens[bb] + bs - 1) / bs : 0;
+        const int incl = wave_incl_scan(nb, lane);
+        const bool past = bb < num_seqs &&
+                          static_cast<int64_t>(num_kv_heads) * (carry + incl) > sp.x0;
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(past);
+        if (hit != 0) {
+            const int f = __builtin_ctzll(hit);
+            sp.b = base + f;
+            sp.nbb = __builtin_amdgcn_readlane(nb, f);
+            cb = carry + __builtin_amdgcn_readlane(incl, f) - sp.nbb;
+            break;
+        }
+        carry += __builtin_amdgcn_readlane(incl, kWave - 1);
+    }
+    sp.g = (sp.x0 - num_kv_heads * cb) / sp.nbb;
+    sp.blk = (sp.x0 - num_kv_heads * cb) - sp.g * sp.nbb;
+    return true;
+}
+
 // ---------------------------------------------------------------------------
 // Reduce over the stream-K partial slots of each (sequence, query head).
 // Slot row (s * group + h % group) holds head h's partial of the segment
@@ -231,6 +285,26 @@ __global__ __launch_bounds__(kWave *W) void stream_reduce_kernel(
 #pragma unroll
         for (int d = 0; d < DPL; ++d) o[d] = num[d] / den;
     }
+}
+
+// Enqueues the reduce: four waves per (sequence, query head) when there are
+// few of them (long contexts with many partial slots each), else one, so that
+// every row's short chain of dependent loads runs in a single pass of the grid.
+template <typename T, int D>
+hipError_t enqueue_stream_reduce(T *out, const float *ws_acc, const float2 *ws_ml,
+                                 const int32_t *ws_prefix, const int32_t *context_lens,
+                                 int num_seqs, int num_q_heads, int num_kv_heads, int group,
+                                 int block_size, int waves, hipStream_t stream) {
+    const dim3 grid(num_q_heads, num_seqs);
+    if (static_cast<int64_t>(num_seqs) * num_q_heads < 2048)
+        hipLaunchKernelGGL((stream_reduce_kernel<T, D, 4>), grid, dim3(kWave * 4), 0, stream, out,
+                           ws_acc, ws_ml, ws_prefix, context_lens, num_seqs, num_kv_heads, group,
+                           block_size, waves);
+    else
+        hipLaunchKernelGGL((stream_reduce_kernel<T, D, 1>), grid, dim3(kWave), 0, stream, out,
+                           ws_acc, ws_ml, ws_prefix, context_lens, num_seqs, num_kv_heads, group,
+                           block_size, waves);
+    return hipGetLastError();
 }
 
 // Stream shares of a partition kernel: one per wave slot it keeps resident

@@ -1,0 +1,315 @@
+// Grouped-query paged decode attention on the matrix cores (gfx950), bf16,
+// head dim 128, 16-token blocks, up to 16 query heads per KV head.
+//
+// It computes what the VALU grouped kernel computes (exact softmax attention
+// of one query token per sequence over its paged K/V, query head h reading
+// KV head h / G: PagedAttention page table in "Cache KV, attention et
+// optimisation de l'inference", GQA in CS336 lecture 10 notes; the online
+// softmax of "Étape 2: softmax en carreaux"; FlashDecoding partitions merged
+// by the same log-sum-exp reduce), and leaves the same partial results, so
+// the same stream-K schedule and reduce kernel serve both.  What differs is
+// where the arithmetic runs: the G heads of a group share each K/V block,
+// which makes a block's work two small dense products,
+//     S^T[token, head] = K[token, :] . Q^T[:, head]        (16 x 16 x 128)
+//     O^T[dim, head]  += V^T[dim, token] . P^T[token, head] (128 x 16 x 16)
+// and both go to v_mfma (16x16x32 and 16x16x16 bf16) with heads as the
+// 16-wide N dimension (columns G..15 carry a zero query and are dropped).
+// The VALU then has only the softmax of 4 scores per lane to do, instead of
+// G dot products per token and the lane reductions behind them.
+//
+// gfx950 mapping, one wave64 per stream share (4 per work-group, one per SIMD):
+//  * K and V tiles of a block (16 rows of 256 bytes each) stream HBM -> LDS
+//    with global_load_lds_dwordx4 into a ring of NBUF slots, as in the VALU
+//    kernel.  Chunk c (16 bytes) of row t is stored at chunk c ^ t: the
+//    row-wise K reads of a 16-lane phase (16 rows, one chunk column) and the
+//    transposed V reads (4 rows x 2 chunk columns per 16 lanes) then fall on
+//    distinct banks.
+//  * Lane (col = lane % 16, quad = lane / 16) holds, for the scores, row
+//    `col` of K (the A operand: 8 dims per k-step) and head `col` of q (the
+//    B operand, in registers for the whole segment); the product leaves it
+//    the scores of tokens 4 quad .. 4 quad + 3 of head col.  That is exactly
+//    the B-operand layout of the value product, so the probabilities go from
+//    the softmax to the matrix core without leaving the lane; V^T comes from
+//    LDS by ds_read_b64_tr_b16.
+//  * Softmax per head (column): max over the lane's 4 scores and the 4 quads
+//    (two lane exchanges); the running max moves only when a score passes it
+//    by more than kSlack (log2 units), so the rescale of the 32 accumulators
+//    is rare; probabilities are rounded to bf16 for the product and the
+//    running sum adds the rounded values.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace pa {
+namespace {
+
+constexpr int kMBS = 16;                // tokens per cache block
+constexpr int kMD = 128;                // head dim (K and V)
+constexpr int kMRowB = kMD * 2;         // bytes per token row of one head
+constexpr int kMTileB = kMBS * kMRowB;  // 4 KB: one head's K (or V) rows of a block
+constexpr int kMTileDma = kMTileB / 1024;  // 1 KB LDS-DMA loads per tile
+constexpr int kMSlotB = 2 * kMTileB;    // K then V
+constexpr int kMPerBlock = 2 * kMTileDma;  // LDS-DMA loads per block
+constexpr int kMKSteps = kMD / 32;      // score k-steps
+constexpr int kMDimTiles = kMD / 16;    // 16-dim tiles of the output
+constexpr float kMSlack = 8.0f;         // lazy-rescale threshold, log2 units
+constexpr int kMGroupWaves = 4;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x8_t lds_b128(uint32_t byte_addr) {
+    return __builtin_bit_cast(
+        bf16x8_t, *(const __attribute__((address_space(3))) u32x4_t *)(uintptr_t)byte_addr);
+}
+__device__ __forceinline__ s16x4_t lds_tr_b64(uint32_t byte_addr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t *)(uintptr_t)byte_addr);
+}
+
+// Wait until at most `later` blocks of kMPerBlock loads are still in flight.
+template <int NBUF>
+__device__ __forceinline__ void wait_mblocks(int later) {
+    if constexpr (NBUF >= 4) {
+        if (later >= 3) { wait_vmem<3 * kMPerBlock>(); return; }
+        if (later == 2) { wait_vmem<2 * kMPerBlock>(); return; }
+    }
+    if (later >= 1) { wait_vmem<kMPerBlock>(); return; }
+    wait_vmem<0>();
+}
+
+// Partition kernel: the stream-K schedule and partial-slot layout of the
+// VALU grouped kernel (slot row (share + b * Hkv + g) * G + head, fp32
+// accumulator of D dims plus (max, sum) in log2 units).
+template <int NBUF>
+__global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel(
+    float *__restrict__ ws_acc, float2 *__restrict__ ws_ml, int32_t *__restrict__ ws_prefix,
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_cache,
+    const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ block_tables,
+    const int32_t *__restrict__ context_lens, float scale_log2, int num_seqs, int num_kv_heads,
+    int group, int max_blocks, int nshares) {
+    static_assert((NBUF & (NBUF - 1)) == 0 && NBUF >= 2 && NBUF <= 4, "ring depth 2 or 4");
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int sid = blockIdx.x * kMGroupWaves + wave;
+    if (sid >= nshares) return;  // uniform over the wave; waves never wait on each other
+    const int col = lane & 15;
+    const int quad = lane >> 4;
+    const int num_q_heads = num_kv_heads * group;
+
+    __shared__ __attribute__((aligned(16))) char s_ring_all[kMGroupWaves][NBUF * kMSlotB];
+    __shared__ __attribute__((aligned(16))) int32_t s_ids_all[kMGroupWaves][2][kWave];
+    int32_t(*s_ids)[kWave] = s_ids_all[wave];
+    const uint32_t ring_lds = lds_offset(s_ring_all[wave]);
+    const uint32_t ids_lds[2] = {lds_offset(&s_ids[0][0]), lds_offset(&s_ids[1][0])};
+
+    ShareSpan sp;
+    if (!find_share(sid, nshares, num_seqs, num_kv_heads, kMBS, context_lens, ws_prefix, lane, sp))
+        return;
+    const int x1 = sp.x1;
+    int b = sp.b, nbb = sp.nbb, g = sp.g, blk_start = sp.blk;
+
+    const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * kMRowB;
+    const int64_t blk_stride = kMBS * row_stride;
+    const char *kbase = reinterpret_cast<const char *>(k_cache);
+    const char *vbase = reinterpret_cast<const char *>(v_cache);
+
+    // LDS byte offsets (inside a tile) this lane reads.
+    //  K, score k-step j: row col, chunk (4 j + quad) ^ col.
+    //  V^T, dim tile t: the transposed read's source row 4 quad + col / 4,
+    //  dims 16 t + 4 (col % 4) .. + 3, i.e. chunk 2 t + (col % 4) / 2, half col % 2.
+    uint32_t k_rd[kMKSteps];
+#pragma unroll
+    for (int j = 0; j < kMKSteps; ++j)
+        k_rd[j] = col * kMRowB + (((4 * j + quad) ^ col) << 4);
+    const int vrow = 4 * quad + (col >> 2);
+    uint32_t v_rd[kMDimTiles];
+#pragma unroll
+    for (int t = 0; t < kMDimTiles; ++t)
+        v_rd[t] = vrow * kMRowB + (((2 * t + ((col & 3) >> 1)) ^ vrow) << 4) + 8 * (col & 1);
+
+    for (int x = sp.x0;;) {
+        // ======== segment (b, g): blocks [blk_start, blk_start + nblk) ========
+        const int nblk = min(nbb - blk_start, x1 - x);
+        const int ctx = context_lens[b];
+        const int32_t *bt_row = block_tables + static_cast<int64_t>(b) * max_blocks;
+
+        auto fetch_ids = [&](int m) {
+            const int e = min(blk_start + kWave * m + lane, max_blocks - 1);
+            dma4(bt_row, static_cast<uint32_t>(e) * 4u, ids_lds[m & 1]);
+        };
+        fetch_ids(0);
+        if (nblk > kWave) fetch_ids(1);
+
+        // q^T as the score B operand: head col of the group, dims 32 j + 8 quad .. + 7;
+        // columns past the group hold zeros.
+        bf16x8_t qb[kMKSteps];
+        {
+            const bool live = col < group;
+            const uint16_t *qr = q + (static_cast<int64_t>(b) * num_q_heads + g * group +
+                                      (live ? col : 0)) * kMD + 8 * quad;
+#pragma unroll
+            for (int j = 0; j < kMKSteps; ++j) {
+                u32x4_t v = *reinterpret_cast<const u32x4_t *>(qr + 32 * j);
+                asm volatile("" : "+v"(v));
+                if (!live) v = u32x4_t{0u, 0u, 0u, 0u};
+                qb[j] = __builtin_bit_cast(bf16x8_t, v);
+            }
+        }
+        // This lane's DMA sources inside one block: tile row 4 i + quad, chunk col ^ row.
+        uint32_t dma_off[kMTileDma];
+#pragma unroll
+        for (int i = 0; i < kMTileDma; ++i) {
+            const int t = 4 * i + quad;
+            dma_off[i] = static_cast<uint32_t>(t * row_stride + g * kMRowB + ((col ^ t) << 4));
+        }
+        drain_vmem();  // q and the first ids have landed; the ring's accounting starts empty
+
+        float m_run = kNegInf;  // running max of head col (scaled, log2 units)
+        float l_run = 0.f;      // this lane's share of the running sum of head col
+        f32x4_t acc[kMDimTiles];
+#pragma unroll
+        for (int t = 0; t < kMDimTiles; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+        auto issue = [&](int n) {
+            if ((n & (kWave - 1)) == 0 && n > 0 && n + kWave < nblk) fetch_ids((n >> 6) + 1);
+            const int pb = __builtin_amdgcn_readfirstlane(s_ids[(n >> 6) & 1][n & (kWave - 1)]);
+            const char *kb = kbase + static_cast<int64_t>(pb) * blk_stride;
+            const char *vb = vbase + static_cast<int64_t>(pb) * blk_stride;
+            const uint32_t slot = ring_lds + (n & (NBUF - 1)) * kMSlotB;
+#pragma unroll
+            for (int i = 0; i < kMTileDma; ++i) dma16(kb, dma_off[i], slot + i * 1024);
+#pragma unroll
+            for (int i = 0; i < kMTileDma; ++i) dma16(vb, dma_off[i], slot + kMTileB + i * 1024);
+        };
+
+        auto compute_block = [&](int n) {
+            const uint32_t kslot = ring_lds + (n & (NBUF - 1)) * kMSlotB;
+            const uint32_t vslot = kslot + kMTileB;
+            const int valid = ctx - (blk_start + n) * kMBS;  // tokens of this block in context
+
+            // ---- scores S^T[token 4 quad + i, head col] ----
+            bf16x8_t ka[kMKSteps];
+#pragma unroll
+            for (int j = 0; j < kMKSteps; ++j) ka[j] = lds_b128(kslot + k_rd[j]);
+            f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < kMKSteps; ++j)
+                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[j], qb[j], s, 0, 0, 0);
+            // V^T fragments, read while the scores are worked on
+            s16x4_t va[kMDimTiles];
+#pragma unroll
+            for (int t = 0; t < kMDimTiles; ++t) va[t] = lds_tr_b64(vslot + v_rd[t]);
+
+            float x[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = (4 * quad + i < valid) ? s[i] * scale_log2 : kNegInf;
+            float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+            bm = fmaxf(bm, __shfl_xor(bm, 16));
+            bm = fmaxf(bm, __shfl_xor(bm, 32));
+            if (__builtin_amdgcn_ballot_w64(bm > m_run + kMSlack) != 0) {
+                const float m_new = fmaxf(m_run, bm);
+                const float alpha = exp2_fast(m_run - m_new);
+                l_run *= alpha;
+                m_run = m_new;
+#pragma unroll
+                for (int t = 0; t < kMDimTiles; ++t) acc[t] *= alpha;
+            }
+            const uint32_t p01 = pack_bf16(exp2_fast(x[0] - m_run), exp2_fast(x[1] - m_run));
+            const uint32_t p23 = pack_bf16(exp2_fast(x[2] - m_run), exp2_fast(x[3] - m_run));
+            l_run += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
+            const s16x4_t pb = __builtin_bit_cast(s16x4_t, u32x2_t{p01, p23});
+
+            // ---- O^T[16 t + 4 quad + i, head col] += V^T P^T ----
+            if (valid < kMBS) {  // rows past the context contribute exactly zero, NaN or not
+#pragma unroll
+                for (int t = 0; t < kMDimTiles; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * quad + e >= valid) va[t][e] = 0;
+            }
+#pragma unroll
+            for (int t = 0; t < kMDimTiles; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[t], pb, acc[t], 0, 0, 0);
+        };
+
+#pragma unroll
+        for (int n = 0; n < NBUF - 1; ++n)
+            if (n < nblk) issue(n);
+        for (int n = 0; n < nblk; ++n) {
+            if (n + NBUF - 1 < nblk) {
+                wait_lds();  // slot (n - 1) % NBUF and the ids in LDS are read
+                issue(n + NBUF - 1);
+            }
+            wait_mblocks<NBUF>(min(NBUF - 1, nblk - 1 - n));
+            compute_block(n);
+        }
+
+        // ---- this segment's partial: unnormalised acc, running max and sum ----
+        float l_tot = l_run + __shfl_xor(l_run, 16);
+        l_tot += __shfl_xor(l_tot, 32);
+        if (col < group) {
+            const int64_t slot_row =
+                (static_cast<int64_t>(sid) + static_cast<int64_t>(b) * num_kv_heads + g) * group;
+            if (quad == 0) ws_ml[slot_row + col] = make_float2(m_run, l_tot);
+            float *dst = ws_acc + (slot_row + col) * kMD + 4 * quad;
+#pragma unroll
+            for (int t = 0; t < kMDimTiles; ++t)
+                *reinterpret_cast<f32x4_t *>(dst + 16 * t) = acc[t];
+        }
+
+        x += nblk;
+        if (x >= x1) break;
+        blk_start = 0;
+        if (++g == num_kv_heads) {
+            g = 0;
+            do {
+                ++b;
+                nbb = (context_lens[b] + kMBS - 1) / kMBS;
+            } while (nbb == 0);
+        }
+        wait_lds();  // every LDS read of this segment is done before the next one's DMA
+    }
+}
+
+template <int NBUF>
+pa_status enqueue_gqa_mfma(const DecodeShape &s, const DecodeArgs &a, const DecodePlan &p,
+                           float scale_log2, hipStream_t stream, std::string *why) {
+    char *ws = static_cast<char *>(a.workspace);
+    float *acc = reinterpret_cast<float *>(ws + p.acc_offset);
+    float2 *ml = reinterpret_cast<float2 *>(ws + p.ml_offset);
+    int32_t *prefix = reinterpret_cast<int32_t *>(ws + p.prefix_offset);
+    const auto kernel = gqa_mfma_partition_kernel<NBUF>;
+    const int waves = stream_waves(kernel, kWave * kMGroupWaves, 1, kStreamWavesMax, kMGroupWaves);
+    const int groups = (waves + kMGroupWaves - 1) / kMGroupWaves;
+    hipLaunchKernelGGL(kernel, dim3(groups), dim3(kWave * kMGroupWaves), 0, stream, acc, ml,
+                       prefix, static_cast<const uint16_t *>(a.q),
+                       static_cast<const uint16_t *>(a.k_cache),
+                       static_cast<const uint16_t *>(a.v_cache), a.block_tables, a.context_lens,
+                       scale_log2, s.num_seqs, s.num_kv_heads, p.group, s.max_blocks_per_seq,
+                       waves);
+    pa_status st = hip_status(hipGetLastError(), why, "partition launch");
+    if (st != PA_OK) return st;
+    return hip_status(enqueue_stream_reduce<uint16_t, kMD>(
+                          static_cast<uint16_t *>(a.out), acc, ml, prefix, a.context_lens,
+                          s.num_seqs, s.num_q_heads, s.num_kv_heads, p.group, kMBS, waves, stream),
+                      why, "reduce launch");
+}
+
+}  // namespace
+
+pa_status launch_gqa_mfma_decode(const DecodeShape &s, const DecodeArgs &a, const DecodePlan &p,
+                                 hipStream_t stream, std::string *why) {
+    if (s.num_seqs == 0) return PA_OK;
+    const float scale_log2 = static_cast<float>(static_cast<double>(a.scale) * 1.4426950408889634);
+    if (p.ring_depth == 4) return enqueue_gqa_mfma<4>(s, a, p, scale_log2, stream, why);
+    return enqueue_gqa_mfma<2>(s, a, p, scale_log2, stream, why);
+}
+
+}  // namespace pa

@@ -199,43 +199,12 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
     int32_t(*s_ids)[kWave] = s_ids_all[wave];
     float *s_alpha = s_alpha_all[wave];
 
-    // ---- this work-group's share of the global block order ----------------
-    int seq_blocks_total = 0;
-    for (int base = 0; base < num_seqs; base += kWave) {
-        const int bb = base + lane;
-        const int nb = bb < num_seqs ? (context_lens[bb] + kBS - 1) / kBS : 0;
-        const int incl = wave_incl_scan(nb, lane);
-        if (sid == 0 && bb < num_seqs) ws_prefix[bb] = seq_blocks_total + incl - nb;
-        seq_blocks_total += __builtin_amdgcn_readlane(incl, kWave - 1);
-    }
-    if (sid == 0 && lane == 0) ws_prefix[num_seqs] = seq_blocks_total;
-    const int total = num_kv_heads * seq_blocks_total;
-    const int share = stream_share(total, nshares);
-    const int64_t x0l = static_cast<int64_t>(sid) * share;
-    if (x0l >= total) return;
-    const int x0 = static_cast<int>(x0l);
-    const int x1 = min(x0 + share, total);
-
-    // The sequence holding global block x0: first b whose blocks end past it.
-    int b = 0, nbb = 0, cb = 0;
-    for (int base = 0, carry = 0;; base += kWave) {
-        const int bb = base + lane;
-        const int nb = bb < num_seqs ? (context_lens[bb] + kBS - 1) / kBS : 0;
-        const int incl = wave_incl_scan(nb, lane);
-        const bool past = bb < num_seqs &&
-                          static_cast<int64_t>(num_kv_heads) * (carry + incl) > x0;
-        const uint64_t hit = __builtin_amdgcn_ballot_w64(past);
-        if (hit != 0) {
-            const int f = __builtin_ctzll(hit);
-            b = base + f;
-            nbb = __builtin_amdgcn_readlane(nb, f);
-            cb = carry + __builtin_amdgcn_readlane(incl, f) - nbb;
-            break;
-        }
-        carry += __builtin_amdgcn_readlane(incl, kWave - 1);
-    }
-    int g = (x0 - num_kv_heads * cb) / nbb;
-    int blk_start = (x0 - num_kv_heads * cb) - g * nbb;
+    // ---- this wave's share of the global block order -------------------------
+    ShareSpan sp;
+    if (!find_share(sid, nshares, num_seqs, num_kv_heads, kBS, context_lens, ws_prefix, lane, sp))
+        return;
+    const int x1 = sp.x1;
+    int b = sp.b, nbb = sp.nbb, g = sp.g, blk_start = sp.blk;
 
     const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * C::kRowBytes;
     const int64_t blk_stride = kBS * row_stride;
@@ -251,7 +220,7 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
     // bf16 with one dim per lane: which half of the dword holds it
     const uint32_t pv_sel = (kEB == 2 && DPL == 1 && (lane & 1)) ? 0x07060302u : 0x05040100u;
 
-    for (int x = x0;;) {
+    for (int x = sp.x0;;) {
         // ======== segment (b, g): blocks [blk_start, blk_start + nblk) ========
         const int nblk = min(nbb - blk_start, x1 - x);
         const int ctx = context_lens[b];
@@ -513,11 +482,10 @@ pa_status enqueue_grouped(const DecodeShape &s, const DecodeArgs &a, const Decod
                        scale_log2, s.num_seqs, s.num_kv_heads, s.max_blocks_per_seq, waves);
     pa_status st = hip_status(hipGetLastError(), why, "partition launch");
     if (st != PA_OK) return st;
-    const dim3 grid(s.num_q_heads, s.num_seqs);
-    hipLaunchKernelGGL((stream_reduce_kernel<T, D, 4>), grid, dim3(kWave * 4), 0, stream,
-                       static_cast<T *>(a.out), acc, ml, prefix, a.context_lens, s.num_seqs,
-                       s.num_kv_heads, G, kBS, waves);
-    return hip_status(hipGetLastError(), why, "reduce launch");
+    return hip_status(enqueue_stream_reduce<T, D>(static_cast<T *>(a.out), acc, ml, prefix,
+                                                  a.context_lens, s.num_seqs, s.num_q_heads,
+                                                  s.num_kv_heads, G, kBS, waves, stream),
+                      why, "reduce launch");
 }
 
 template <typename T, int D>

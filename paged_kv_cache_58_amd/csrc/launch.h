@@ -18,6 +18,11 @@ pa_status launch_append(const AppendArgs &a, const AppendPlan &plan, hipStream_t
 pa_status launch_grouped_decode(const DecodeShape &s, const DecodeArgs &a,
                                 const DecodePlan &plan, hipStream_t stream, std::string *why);
 
+// The grouped decode with its per-block products on the matrix cores (bf16,
+// head dim 128, block size 16); same workspace layout and reduce.
+pa_status launch_gqa_mfma_decode(const DecodeShape &s, const DecodeArgs &a,
+                                 const DecodePlan &plan, hipStream_t stream, std::string *why);
+
 // Latent (576/512) decode on MFMA, followed by the same stream-K reduce.
 pa_status launch_latent_decode(const DecodeShape &s, const DecodeArgs &a,
                                const DecodePlan &plan, hipStream_t stream, std::string *why);

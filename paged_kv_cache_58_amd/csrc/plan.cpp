@@ -25,6 +25,15 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 // Blocks a work-group streams into LDS on the grouped path (ring depth).
 // Two 8 KB slots per wave let LDS hold eight waves per CU, which beats a
 // deeper ring with fewer waves.  PA_RING_DEPTH (2 or 4) overrides it.
+// Whether a grouped-shape bf16 decode with head dim 128 runs its per-block
+// products on the matrix cores.  PA_GQA_MFMA (0 or 1) overrides the default.
+bool grouped_mfma_default(const DecodeShape &s) {
+    if (s.dtype != PA_BF16 || s.head_dim_k != 128) return false;
+    const char *env = std::getenv("PA_GQA_MFMA");
+    if (env && *env) return std::atoi(env) != 0;
+    return false;
+}
+
 int grouped_ring_depth() {
     const char *env = std::getenv("PA_RING_DEPTH");
     if (env && *env && std::atoi(env) == 2) return 2;
@@ -115,11 +124,11 @@ pa_status plan_decode(const DecodeShape &s, DecodePlan *plan, std::string *why) 
         if ((int64_t)s.num_seqs * s.max_blocks_per_seq * s.num_kv_heads > INT32_MAX)
             return fail(PA_ERR_SHAPE, why,
                         "decode: num_seqs * max_blocks_per_seq * num_kv_heads exceeds 2^31-1");
-        p.path = DecodePath::kGrouped;
+        p.path = grouped_mfma_default(s) ? DecodePath::kGroupedMfma : DecodePath::kGrouped;
         p.ring_depth = grouped_ring_depth();
     }
     size_t rows;  // (slot, head) rows of partial results
-    if (p.path == DecodePath::kGrouped)
+    if (p.path != DecodePath::kLatent)
         rows = ((size_t)kStreamWavesMax + (size_t)s.num_seqs * s.num_kv_heads) * (size_t)G;
     else
         rows = ((size_t)kLatentWavesMax + (size_t)s.num_seqs) *

@@ -39,7 +39,9 @@ struct AppendPlan {
 
 pa_status check_append(const AppendArgs &a, AppendPlan *plan, std::string *why);
 
-enum class DecodePath { kGrouped, kLatent };
+// kGrouped: VALU dot products; kGroupedMfma: the same split and partials with
+// the per-block products on the matrix cores (bf16, head dim 128).
+enum class DecodePath { kGrouped, kGroupedMfma, kLatent };
 
 // Most work-groups the grouped path's stream-K partition kernel launches
 // (one per resident wave slot; 256 CUs x 16 waves), which sizes its

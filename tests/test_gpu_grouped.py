@@ -21,6 +21,15 @@ def dev():
     return torch.device("cuda:0")
 
 
+@pytest.fixture(autouse=True, params=["valu", "mfma"])
+def grouped_path(request, monkeypatch):
+    """Every test runs on both grouped kernels: VALU dot products, and the
+    matrix-core kernel (taken for bf16 with head dim 128; other shapes stay
+    on the VALU kernel either way)."""
+    monkeypatch.setenv("PA_GQA_MFMA", "1" if request.param == "mfma" else "0")
+    return request.param
+
+
 def _append_bitwise(d, slots=None):
     w = d.w
     sm = w.slot_mapping if slots is None else slots
