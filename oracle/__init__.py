@@ -44,6 +44,20 @@ def load_library(path: str):
     lib.oracle_append.restype = I
     lib.oracle_append.argtypes = [P, P, P, ctypes.c_int64, P, ctypes.c_int64, P, I, I,
                                   I, I, I, I, I]
+    lib.oracle_e4m3_value.restype = ctypes.c_double
+    lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_e8m0_value.restype = ctypes.c_double
+    lib.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_encode_array.restype = None
+    lib.oracle_e4m3_encode_array.argtypes = [P, ctypes.c_int64, P]
+    lib.oracle_mx_quantize.restype = I
+    lib.oracle_mx_quantize.argtypes = [P, I, ctypes.c_int64, I, P, P]
+    lib.oracle_append_mxfp8.restype = I
+    lib.oracle_append_mxfp8.argtypes = [P, P, P, P, P, ctypes.c_int64, P, ctypes.c_int64, P,
+                                        I, I, I, I, I, I]
+    lib.oracle_decode_mxfp8.restype = I
+    lib.oracle_decode_mxfp8.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_double, I, I, I, I,
+                                        I, I, I, P, I, I]
     return lib
 
 
@@ -145,3 +159,95 @@ def append(k_cache: np.ndarray, v_cache: Optional[np.ndarray], k: np.ndarray,
                            Hkv, dk, dv, elt)
     if rc != 0:
         raise RuntimeError(f"oracle_append failed with code {rc}")
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 KV cache (OCP Microscaling: E4M3 values, one E8M0 scale per 32).  The
+# arithmetic is in pa_oracle.c; layouts there: K codes [nb, Hkv, bs, d], V
+# codes [nb, Hkv, d, bs], scales [nb, Hkv, bs, d / 32].
+# ---------------------------------------------------------------------------
+
+def e4m3_values(codes: np.ndarray, lib=None) -> np.ndarray:
+    """float64 value of every E4M3 byte in ``codes`` (NaN for S.1111.111)."""
+    lib = _load(lib)
+    lut = np.array([lib.oracle_e4m3_value(c) for c in range(256)], dtype=np.float64)
+    return lut[np.asarray(codes, dtype=np.uint8)]
+
+
+def e8m0_values(scales: np.ndarray, lib=None) -> np.ndarray:
+    """float64 value 2^(e - 127) of every E8M0 byte (NaN for 0xFF)."""
+    lib = _load(lib)
+    lut = np.array([lib.oracle_e8m0_value(c) for c in range(256)], dtype=np.float64)
+    return lut[np.asarray(scales, dtype=np.uint8)]
+
+
+def e4m3_encode(y: np.ndarray, lib=None) -> np.ndarray:
+    """Nearest E4M3 byte of each finite float64, ties to even, saturating at +-448."""
+    lib = _load(lib)
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    out = np.empty(y.shape, dtype=np.uint8)
+    lib.oracle_e4m3_encode_array(_ptr(y), y.size, _ptr(out))
+    return out
+
+
+def mx_quantize(x: np.ndarray, lib=None):
+    """Rows of the last axis (length a multiple of 32) -> (E4M3 codes, E8M0 scales)."""
+    lib = _load(lib)
+    x = np.ascontiguousarray(x)
+    d = x.shape[-1]
+    rows = x.size // d
+    codes = np.empty(x.shape, dtype=np.uint8)
+    scales = np.empty(x.shape[:-1] + (d // 32,), dtype=np.uint8)
+    rc = lib.oracle_mx_quantize(_ptr(x), _dtype_code(x), rows, d, _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise RuntimeError(f"oracle_mx_quantize failed with code {rc}")
+    return codes, scales
+
+
+def append_mxfp8(k8: np.ndarray, v8: np.ndarray, ks: np.ndarray, vs: np.ndarray,
+                 k: np.ndarray, v: np.ndarray, slot_mapping: np.ndarray, lib=None) -> None:
+    """In-place quantizing append of each token's k and v rows into its slot."""
+    lib = _load(lib)
+    for a in (k8, v8, ks, vs):
+        assert a.flags.c_contiguous and a.dtype == np.uint8
+    nb, Hkv, bs, d = k8.shape
+    assert v8.shape == (nb, Hkv, d, bs) and ks.shape == vs.shape == (nb, Hkv, bs, d // 32)
+    k2 = np.ascontiguousarray(k).reshape(k.shape[0], -1)
+    v2 = np.ascontiguousarray(v).reshape(v.shape[0], -1)
+    assert _dtype_code(k2) == _dtype_code(v2)
+    sm = np.ascontiguousarray(slot_mapping, dtype=np.int32)
+    rc = lib.oracle_append_mxfp8(_ptr(k8), _ptr(v8), _ptr(ks), _ptr(vs), _ptr(k2), k2.shape[1],
+                                 _ptr(v2), v2.shape[1], _ptr(sm), sm.shape[0], nb, bs, Hkv, d,
+                                 _dtype_code(k2))
+    if rc != 0:
+        raise RuntimeError(f"oracle_append_mxfp8 failed with code {rc}")
+
+
+def decode_mxfp8(q: np.ndarray, k8: np.ndarray, v8: np.ndarray, ks: np.ndarray, vs: np.ndarray,
+                 block_tables: np.ndarray, context_lens: np.ndarray, scale: float,
+                 pairs: Optional[Sequence] = None, threads: Optional[int] = None,
+                 lib=None) -> np.ndarray:
+    """float64 attention output [B, Hq, d] over MXFP8 caches (values dequantized)."""
+    lib = _load(lib)
+    q = np.ascontiguousarray(q)
+    B, Hq, d = q.shape
+    nb, Hkv, bs, d2 = k8.shape
+    assert d2 == d and v8.shape == (nb, Hkv, d, bs) and ks.shape == vs.shape == (nb, Hkv, bs, d // 32)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    out = np.full((B, Hq, d), np.nan, dtype=np.float64)
+    if pairs is not None:
+        pr = np.ascontiguousarray(
+            np.unique(np.asarray(list(pairs), dtype=np.int32).reshape(-1, 2), axis=0))
+        n_pairs = pr.shape[0]
+    else:
+        pr, n_pairs = None, 0
+    n_threads = default_threads() if threads is None else int(threads)
+    rc = lib.oracle_decode_mxfp8(_ptr(out), _ptr(q), _ptr(np.ascontiguousarray(k8)),
+                                 _ptr(np.ascontiguousarray(v8)), _ptr(np.ascontiguousarray(ks)),
+                                 _ptr(np.ascontiguousarray(vs)), _ptr(bt), _ptr(cl), float(scale),
+                                 B, Hq, Hkv, d, bs, bt.shape[1], _dtype_code(q), _ptr(pr),
+                                 n_pairs, n_threads)
+    if rc != 0:
+        raise RuntimeError(f"oracle_decode_mxfp8 failed with code {rc}")
+    return out
