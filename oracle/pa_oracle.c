@@ -310,7 +310,7 @@ static int decode_row_mxfp8(double *out_row, const void *q, const uint8_t *k8, c
                             const int32_t *context_lens, double scale, int b, int h, int Hq,
                             int Hkv, int d, int bs, int max_blocks, int q_dtype) {
     const int G = Hq / Hkv;
-    const int g = h / G;
+    const int kvh = h / G;
     const int L = context_lens[b];
     const int nsc = d / 32;
     if (L <= 0) {
@@ -323,7 +323,7 @@ static int decode_row_mxfp8(double *out_row, const void *q, const uint8_t *k8, c
     for (int j = 0; j < d; ++j) o[j] = 0.0;
     const int64_t q_off = ((int64_t)b * Hq + h) * d;
     for (int t = 0; t < L; ++t) {
-        const int64_t tile = (int64_t)block_tables[(int64_t)b * max_blocks + t / bs] * Hkv + g;
+        const int64_t tile = (int64_t)block_tables[(int64_t)b * max_blocks + t / bs] * Hkv + kvh;
         const int r = t % bs;
         double dot = 0.0;
         for (int i = 0; i < d; ++i) {
@@ -331,22 +331,22 @@ static int decode_row_mxfp8(double *out_row, const void *q, const uint8_t *k8, c
                               oracle_e8m0_value(ks[(tile * bs + r) * nsc + i / 32]);
             dot += widen(q, q_off + i, q_dtype) * kv;
         }
-        s[t] = scale * dot;
+        s[t] = dot * scale;
     }
-    double m = s[0];
+    double smax = s[0];
     for (int t = 1; t < L; ++t)
-        if (s[t] > m) m = s[t];
-    double denom = 0.0;
+        if (s[t] > smax) smax = s[t];
+    double total = 0.0;
     for (int t = 0; t < L; ++t) {
-        const double w = exp(s[t] - m);
-        denom += w;
-        const int64_t tile = (int64_t)block_tables[(int64_t)b * max_blocks + t / bs] * Hkv + g;
+        const double w = exp(s[t] - smax);
+        total += w;
+        const int64_t tile = (int64_t)block_tables[(int64_t)b * max_blocks + t / bs] * Hkv + kvh;
         const int r = t % bs;
         for (int j = 0; j < d; ++j)
             o[j] += w * oracle_e4m3_value(v8[(tile * d + j) * bs + r]) *
                     oracle_e8m0_value(vs[(tile * bs + r) * nsc + j / 32]);
     }
-    for (int j = 0; j < d; ++j) out_row[j] = o[j] / denom;
+    for (int j = 0; j < d; ++j) out_row[j] = o[j] / total;
     free(s);
     return ORACLE_OK;
 }
