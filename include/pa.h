@@ -150,6 +150,81 @@ pa_status pa_decode(void *out, const void *q, const void *k_cache,
                     pa_dtype dtype, void *workspace, size_t workspace_bytes,
                     void *stream);
 
+/*
+ * MXFP8 KV cache.  Fewer bytes per cached value make memory-bound decode
+ * faster, fp8 being one of the formats (CS336 lecture 10 notes, "第 10 讲：
+ * 推理", "核心概念与定义", quantization bullet), and the scales should be
+ * blockwise rather than per tensor, MXFP8 being the example given (same
+ * notes, "常见陷阱").  MXFP8 is the OCP Microscaling format: every 32
+ * consecutive values share one E8M0 scale byte e (value 2^(e - 127); 0xFF
+ * is NaN) and each value is an FP8 E4M3 byte (sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits; S.1111.111 is NaN; largest magnitude 448).  A
+ * cached value is code * 2^(e - 127).  Cache layouts, one layer, uint8:
+ *
+ *   k_cache  [num_blocks, num_kv_heads, block_size, head_dim]   E4M3 codes
+ *   v_cache  [num_blocks, num_kv_heads, head_dim, block_size]   E4M3 codes,
+ *            each (block, head) tile transposed (dims x tokens)
+ *   k_scale, v_scale  [num_blocks, num_kv_heads, block_size, head_dim / 32]
+ *            E8M0 bytes; byte j of a token row scales its values
+ *            32 j .. 32 j + 31
+ *
+ * Slots, block tables and context lengths mean what they mean for pa_decode.
+ * Supported: head_dim 128; decode also needs block_size 16, bf16 q and out,
+ * num_q_heads / num_kv_heads in {1, 2, 4, 8}.  All cache and scale pointers
+ * must be 16-byte aligned.
+ */
+
+/*
+ * pa_cache_append_mxfp8 — quantize each new token's K and V rows into its
+ * slot of MXFP8 caches.
+ *
+ * For i < num_tokens with s = slot_mapping[i] != -1, p = s / block_size,
+ * r = s % block_size, and each KV head h: every 32-value block of the row
+ * k[i, h, :] gets X = floor(log2(max |value|)) - 8, clamped to [-127, 127]
+ * (X = -127 for an all-zero block); scale byte X + 127 goes to
+ * k_scale[p, h, r, block] and each value * 2^-X, rounded to the nearest
+ * E4M3 value (ties to even, saturating at +-448), to k_cache[p, h, r, :].
+ * v[i, h, :] is quantized the same way into column r of v_cache[p, h] and
+ * v_scale[p, h, r, :].  Nothing else changes.
+ *
+ *   k, v      [num_tokens, num_kv_heads, head_dim] rows of element type
+ *             dtype (PA_F32 or PA_BF16), token i at element i * stride;
+ *             values must be finite (otherwise the codes are unspecified).
+ *   slot_mapping  int32 [num_tokens]; -1 = skip; other slots distinct and
+ *             < num_blocks * block_size.
+ * num_tokens == 0 is a no-op.  Returns PA_ERR_NULL, PA_ERR_SHAPE,
+ * PA_ERR_DTYPE, PA_ERR_UNSUPPORTED (head_dim != 128), PA_ERR_ALIGN or
+ * PA_ERR_HIP.
+ */
+pa_status pa_cache_append_mxfp8(void *k_cache, void *v_cache, void *k_scale,
+                                void *v_scale, const void *k,
+                                int64_t k_token_stride, const void *v,
+                                int64_t v_token_stride,
+                                const int32_t *slot_mapping, int32_t num_tokens,
+                                int32_t num_blocks, int32_t block_size,
+                                int32_t num_kv_heads, int32_t head_dim,
+                                pa_dtype dtype, void *stream);
+
+/*
+ * pa_decode_mxfp8 — pa_decode over MXFP8 caches: the same attention with
+ * every cached K and V value taken as code * 2^(e - 127) (products with
+ * magnitude below 2^-126 may be flushed to zero).  q and out are bf16
+ * (dtype must be PA_BF16), [num_seqs, num_q_heads, head_dim].  The
+ * workspace is the one pa_decode_workspace_size(num_seqs, num_q_heads,
+ * num_kv_heads, head_dim, head_dim, block_size, max_blocks_per_seq) sizes.
+ * Slots at or beyond a sequence's length are never used, whatever their
+ * codes and scales hold.  Errors as for pa_decode.
+ */
+pa_status pa_decode_mxfp8(void *out, const void *q, const void *k_cache,
+                          const void *v_cache, const void *k_scale,
+                          const void *v_scale, const int32_t *block_tables,
+                          const int32_t *context_lens, float scale,
+                          int32_t num_seqs, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t num_blocks,
+                          int32_t max_blocks_per_seq, pa_dtype dtype,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static text for a status code ("PA_OK", ...); never NULL. */
 const char *pa_status_string(pa_status status);
 

@@ -21,8 +21,8 @@ PA_F32, PA_BF16 = 0, 1
 STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_DTYPE",
           4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP", 7: "PA_ERR_ALIGN"}
 
-EXPORTS = ("pa_cache_append", "pa_decode_workspace_size", "pa_decode", "pa_status_string",
-           "pa_last_error")
+EXPORTS = ("pa_cache_append", "pa_decode_workspace_size", "pa_decode", "pa_cache_append_mxfp8",
+           "pa_decode_mxfp8", "pa_status_string", "pa_last_error")
 
 _lib = None
 
@@ -50,6 +50,12 @@ def lib():
         L.pa_decode.restype = ctypes.c_int
         L.pa_decode.argtypes = [P, P, P, P, P, P, ctypes.c_float, I32, I32, I32, I32, I32,
                                 I32, I32, I32, ctypes.c_int, P, ctypes.c_size_t, P]
+        L.pa_cache_append_mxfp8.restype = ctypes.c_int
+        L.pa_cache_append_mxfp8.argtypes = [P, P, P, P, P, I64, P, I64, P, I32, I32, I32, I32,
+                                            I32, ctypes.c_int, P]
+        L.pa_decode_mxfp8.restype = ctypes.c_int
+        L.pa_decode_mxfp8.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_float, I32, I32, I32, I32,
+                                      I32, I32, I32, ctypes.c_int, P, ctypes.c_size_t, P]
         L.pa_status_string.restype = ctypes.c_char_p
         L.pa_status_string.argtypes = [ctypes.c_int]
         L.pa_last_error.restype = ctypes.c_char_p
@@ -146,3 +152,67 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, workspac
         _ptr(context_lens), float(scale), B, hq, hkv, dk, dv, bs, nb, block_tables.shape[1],
         _dtype_code(q), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 KV cache (E4M3 codes, one E8M0 scale per 32 values; layouts in pa.h)
+# ---------------------------------------------------------------------------
+
+MX_BLOCK = 32
+
+
+def alloc_mxfp8_cache(num_blocks, block_size, num_kv_heads, head_dim=128, device="cuda",
+                      fill=None):
+    """(k_cache, v_cache, k_scale, v_scale) uint8 tensors of the MXFP8 layouts."""
+    import torch
+
+    shapes = [(num_blocks, num_kv_heads, block_size, head_dim),
+              (num_blocks, num_kv_heads, head_dim, block_size),
+              (num_blocks, num_kv_heads, block_size, head_dim // MX_BLOCK),
+              (num_blocks, num_kv_heads, block_size, head_dim // MX_BLOCK)]
+    if fill is None:
+        return tuple(torch.empty(sh, dtype=torch.uint8, device=device) for sh in shapes)
+    return tuple(torch.full(sh, fill, dtype=torch.uint8, device=device) for sh in shapes)
+
+
+def cache_append_mxfp8(k_cache, v_cache, k_scale, v_scale, k, v, slot_mapping,
+                       stream=None) -> None:
+    """Quantize k[i] and v[i] ([num_tokens, kv_heads, head_dim], fp32 or bf16)
+    into slot slot_mapping[i] of the MXFP8 caches (-1 skips)."""
+    nb, hkv, bs, d = k_cache.shape
+    n = slot_mapping.shape[0]
+    k2 = k.reshape(n, -1) if n else k
+    v2 = v.reshape(n, -1) if n else v
+    if n and (k2.stride(1) != 1 or v2.stride(1) != 1):
+        raise ValueError("k and v rows must be contiguous")
+    _check(lib().pa_cache_append_mxfp8(
+        _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(k2),
+        k2.stride(0) if n else hkv * d, _ptr(v2), v2.stride(0) if n else hkv * d,
+        _ptr(slot_mapping), n, nb, bs, hkv, d, _dtype_code(k), _stream(stream)))
+
+
+def alloc_mxfp8_workspace(q, k_cache, block_tables):
+    """Workspace for decode_mxfp8 (k_cache in the MXFP8 layout)."""
+    import torch
+
+    B, hq, d = q.shape
+    hkv, bs = k_cache.shape[1], k_cache.shape[2]
+    n = decode_workspace_size(B, hq, hkv, d, d, bs, block_tables.shape[1])
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+
+
+def decode_mxfp8(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, scale,
+                 workspace, stream=None) -> None:
+    """decode() over MXFP8 caches; q and out bf16 [B, Hq, 128]."""
+    B, hq, d = q.shape
+    nb, hkv, bs, _ = k_cache.shape
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("k_scale", k_scale),
+                    ("v_scale", v_scale), ("out", out), ("block_tables", block_tables),
+                    ("context_lens", context_lens)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    _check(lib().pa_decode_mxfp8(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_tables), _ptr(context_lens), float(scale), B, hq, hkv, d, bs, nb,
+        block_tables.shape[1], _dtype_code(q), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))

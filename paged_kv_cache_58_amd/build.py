@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libpa.so")
 ARCH = "gfx950"
 
 SOURCES = ["plan.cpp", "api.cpp", "append.hip", "grouped_decode.hip", "gqa_mfma_decode.hip",
-           "latent_decode.hip"]
+           "latent_decode.hip", "mxfp8_append.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

@@ -82,8 +82,8 @@ PA_EXPORT pa_status pa_decode(void *out, const void *q, const void *k_cache,
     pa::DecodePlan plan{};
     pa_status st = pa::plan_decode(s, &plan, &why);
     if (st != PA_OK) return finish(st, why);
-    const pa::DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens, scale,
-                           num_blocks, workspace, workspace_bytes};
+    const pa::DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens, nullptr,
+                           nullptr, scale, num_blocks, workspace, workspace_bytes};
     st = pa::check_decode(s, a, plan, &why);
     if (st != PA_OK || num_seqs == 0) return finish(st, why);
     hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -93,6 +93,46 @@ PA_EXPORT pa_status pa_decode(void *out, const void *q, const void *k_cache,
         st = pa::launch_gqa_mfma_decode(s, a, plan, hs, &why);
     else
         st = pa::launch_grouped_decode(s, a, plan, hs, &why);
+    return finish(st, why);
+}
+
+PA_EXPORT pa_status pa_cache_append_mxfp8(void *k_cache, void *v_cache, void *k_scale,
+                                          void *v_scale, const void *k, int64_t k_token_stride,
+                                          const void *v, int64_t v_token_stride,
+                                          const int32_t *slot_mapping, int32_t num_tokens,
+                                          int32_t num_blocks, int32_t block_size,
+                                          int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
+                                          void *stream) {
+    const pa::MxAppendArgs a{k_cache, v_cache, k_scale, v_scale, k, k_token_stride, v,
+                             v_token_stride, slot_mapping, num_tokens, num_blocks, block_size,
+                             num_kv_heads, head_dim, dtype};
+    std::string why;
+    pa_status st = pa::check_append_mxfp8(a, &why);
+    if (st != PA_OK || num_tokens == 0) return finish(st, why);
+    st = pa::launch_append_mxfp8(a, static_cast<hipStream_t>(stream), &why);
+    return finish(st, why);
+}
+
+PA_EXPORT pa_status pa_decode_mxfp8(void *out, const void *q, const void *k_cache,
+                                    const void *v_cache, const void *k_scale,
+                                    const void *v_scale, const int32_t *block_tables,
+                                    const int32_t *context_lens, float scale, int32_t num_seqs,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int32_t num_blocks,
+                                    int32_t max_blocks_per_seq, pa_dtype dtype, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+    pa::DecodeShape s = make_shape(false, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                   head_dim, block_size, max_blocks_per_seq, dtype);
+    s.mxfp8 = true;
+    std::string why;
+    pa::DecodePlan plan{};
+    pa_status st = pa::plan_decode(s, &plan, &why);
+    if (st != PA_OK) return finish(st, why);
+    const pa::DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens, k_scale,
+                           v_scale, scale, num_blocks, workspace, workspace_bytes};
+    st = pa::check_decode(s, a, plan, &why);
+    if (st != PA_OK || num_seqs == 0) return finish(st, why);
+    st = pa::launch_mxfp8_decode(s, a, plan, static_cast<hipStream_t>(stream), &why);
     return finish(st, why);
 }
 

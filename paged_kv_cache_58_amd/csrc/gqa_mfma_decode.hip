@@ -1,5 +1,5 @@
-// Grouped-query paged decode attention on the matrix cores (gfx950), bf16,
-// head dim 128, 16-token blocks, up to 16 query heads per KV head.
+// Grouped-query paged decode attention on the matrix cores (gfx950), bf16 or
+// MXFP8 caches, head dim 128, 16-token blocks, up to 16 query heads per KV head.
 //
 // It computes what the VALU grouped kernel computes (exact softmax attention
 // of one query token per sequence over its paged K/V, query head h reading
@@ -36,6 +36,21 @@
 //    by more than kSlack (log2 units), so the rescale of the 32 accumulators
 //    is rare; probabilities are rounded to bf16 for the product and the
 //    running sum adds the rounded values.
+//
+// MXFP8 caches (the blockwise-scaled fp8 of the CS336 lecture 10 notes,
+// "常见陷阱"; E4M3 codes with one E8M0 scale per 32 values of a head row)
+// run the same kernel with half the bytes per block.  Their tiles are
+// contiguous per (block, KV head): K codes as 16 rows of 128 bytes, V codes
+// transposed (128 dims x 16 tokens), and the two 64-byte scale tiles.
+//  * Scores: a lane's K operand is 8 values of one 32-value block of one
+//    token, so one v_cvt_scalef32_pk_bf16_fp8 per value pair turns codes into
+//    bf16 with that block's scale applied (exact, as both are powers of two
+//    times 3-bit mantissas; values below bf16's normal range, |v| < 2^-126,
+//    come out as zero), and the four k-steps chain in one accumulator.
+//  * Values: a V^T operand element is one token's value, each with its own
+//    token's scale, so the codes convert unscaled and the scales go to P^T
+//    instead: P'[t, h] = P[t, h] * 2^X(t, block), one copy of the B operand
+//    per 32-dim block (two output tiles each).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -46,19 +61,36 @@
 namespace pa {
 namespace {
 
-constexpr int kMBS = 16;                // tokens per cache block
-constexpr int kMD = 128;                // head dim (K and V)
-constexpr int kMRowB = kMD * 2;         // bytes per token row of one head
-constexpr int kMTileB = kMBS * kMRowB;  // 4 KB: one head's K (or V) rows of a block
-constexpr int kMTileDma = kMTileB / 1024;  // 1 KB LDS-DMA loads per tile
-constexpr int kMSlotB = 2 * kMTileB;    // K then V
-constexpr int kMPerBlock = 2 * kMTileDma;  // LDS-DMA loads per block
-constexpr int kMKSteps = kMD / 32;      // score k-steps
-constexpr int kMDimTiles = kMD / 16;    // 16-dim tiles of the output
-constexpr float kMSlack = 8.0f;         // lazy-rescale threshold, log2 units
+constexpr int kMBS = 16;              // tokens per cache block
+constexpr int kMD = 128;              // head dim (K and V)
+constexpr int kMKSteps = kMD / 32;    // score k-steps
+constexpr int kMDimTiles = kMD / 16;  // 16-dim tiles of the output
+constexpr float kMSlack = 8.0f;       // lazy-rescale threshold, log2 units
 constexpr int kMGroupWaves = 4;
 
+// Per-format tile geometry of one (block, KV head).
+template <bool MX>
+struct MTile;
+template <>
+struct MTile<false> {                    // bf16, the pages' [nb, bs, Hkv, d] layout
+    static constexpr int kRowB = kMD * 2;        // 256-byte token rows
+    static constexpr int kKB = kMBS * kRowB;     // 4 KB of K (and of V)
+    static constexpr int kDma = kKB / 1024;      // 1 KB LDS-DMA loads per K (or V) tile
+    static constexpr int kSlotB = 2 * kKB;       // K then V
+    static constexpr int kPerBlock = 2 * kDma;   // loads per block
+};
+template <>
+struct MTile<true> {                     // MXFP8
+    static constexpr int kKB = kMBS * kMD;       // 2 KB of K codes (and of V codes)
+    static constexpr int kDma = kKB / 1024;
+    static constexpr int kScaleB = kMBS * (kMD / kMxBlock);  // 64-byte scale tile
+    static constexpr int kScaleLds = kWave * 4;  // a dword LDS-DMA fills 256 bytes
+    static constexpr int kSlotB = 2 * kKB + 2 * kScaleLds;  // K, V^T, K scales, V scales
+    static constexpr int kPerBlock = 2 * kDma + 2;
+};
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -68,32 +100,54 @@ __device__ __forceinline__ bf16x8_t lds_b128(uint32_t byte_addr) {
     return __builtin_bit_cast(
         bf16x8_t, *(const __attribute__((address_space(3))) u32x4_t *)(uintptr_t)byte_addr);
 }
+__device__ __forceinline__ u32x4_t lds_u128(uint32_t byte_addr) {
+    return *(const __attribute__((address_space(3))) u32x4_t *)(uintptr_t)byte_addr;
+}
+__device__ __forceinline__ u32x2_t lds_u64(uint32_t byte_addr) {
+    return *(const __attribute__((address_space(3))) u32x2_t *)(uintptr_t)byte_addr;
+}
+__device__ __forceinline__ uint32_t lds_u32(uint32_t byte_addr) {
+    return *(const __attribute__((address_space(3))) uint32_t *)(uintptr_t)byte_addr;
+}
 __device__ __forceinline__ s16x4_t lds_tr_b64(uint32_t byte_addr) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) s16x4_t *)(uintptr_t)byte_addr);
 }
 
-// Wait until at most `later` blocks of kMPerBlock loads are still in flight.
-template <int NBUF>
+// Two E4M3 codes (the low or high 16 bits of w) as a bf16 pair times scale.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w, float scale) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, HI));
+}
+// 2^(e - 127) for an E8M0 byte e < 255 (e = 0 is the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_f32(uint32_t e) {
+    return as_f(e != 0 ? e << 23 : 0x00400000u);
+}
+
+// Wait until at most `later` blocks of PER loads are still in flight.
+template <int PER, int NBUF>
 __device__ __forceinline__ void wait_mblocks(int later) {
     if constexpr (NBUF >= 4) {
-        if (later >= 3) { wait_vmem<3 * kMPerBlock>(); return; }
-        if (later == 2) { wait_vmem<2 * kMPerBlock>(); return; }
+        if (later >= 3) { wait_vmem<3 * PER>(); return; }
+        if (later == 2) { wait_vmem<2 * PER>(); return; }
     }
-    if (later >= 1) { wait_vmem<kMPerBlock>(); return; }
+    if (later >= 1) { wait_vmem<PER>(); return; }
     wait_vmem<0>();
 }
 
 // Partition kernel: the stream-K schedule and partial-slot layout of the
 // VALU grouped kernel (slot row (share + b * Hkv + g) * G + head, fp32
-// accumulator of D dims plus (max, sum) in log2 units).
-template <int NBUF>
+// accumulator of D dims plus (max, sum) in log2 units).  MX selects MXFP8
+// caches (k_scale, v_scale used); otherwise the caches are bf16.
+template <bool MX, int NBUF>
 __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel(
     float *__restrict__ ws_acc, float2 *__restrict__ ws_ml, int32_t *__restrict__ ws_prefix,
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_cache,
-    const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ block_tables,
+    const uint16_t *__restrict__ q, const void *__restrict__ k_cache,
+    const void *__restrict__ v_cache, const uint8_t *__restrict__ k_scale,
+    const uint8_t *__restrict__ v_scale, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, float scale_log2, int num_seqs, int num_kv_heads,
     int group, int max_blocks, int nshares) {
+    using TL = MTile<MX>;
     static_assert((NBUF & (NBUF - 1)) == 0 && NBUF >= 2 && NBUF <= 4, "ring depth 2 or 4");
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -103,7 +157,7 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
     const int quad = lane >> 4;
     const int num_q_heads = num_kv_heads * group;
 
-    __shared__ __attribute__((aligned(16))) char s_ring_all[kMGroupWaves][NBUF * kMSlotB];
+    __shared__ __attribute__((aligned(16))) char s_ring_all[kMGroupWaves][NBUF * TL::kSlotB];
     __shared__ __attribute__((aligned(16))) int32_t s_ids_all[kMGroupWaves][2][kWave];
     int32_t(*s_ids)[kWave] = s_ids_all[wave];
     const uint32_t ring_lds = lds_offset(s_ring_all[wave]);
@@ -115,24 +169,33 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
     const int x1 = sp.x1;
     int b = sp.b, nbb = sp.nbb, g = sp.g, blk_start = sp.blk;
 
-    const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * kMRowB;
-    const int64_t blk_stride = kMBS * row_stride;
-    const char *kbase = reinterpret_cast<const char *>(k_cache);
-    const char *vbase = reinterpret_cast<const char *>(v_cache);
+    const char *kbase = static_cast<const char *>(k_cache);
+    const char *vbase = static_cast<const char *>(v_cache);
 
     // LDS byte offsets (inside a tile) this lane reads.
-    //  K, score k-step j: row col, chunk (4 j + quad) ^ col.
-    //  V^T, dim tile t: the transposed read's source row 4 quad + col / 4,
-    //  dims 16 t + 4 (col % 4) .. + 3, i.e. chunk 2 t + (col % 4) / 2, half col % 2.
     uint32_t k_rd[kMKSteps];
-#pragma unroll
-    for (int j = 0; j < kMKSteps; ++j)
-        k_rd[j] = col * kMRowB + (((4 * j + quad) ^ col) << 4);
-    const int vrow = 4 * quad + (col >> 2);
     uint32_t v_rd[kMDimTiles];
+    if constexpr (!MX) {
+        //  K, score k-step j: row col, chunk (4 j + quad) ^ col.
+        //  V^T, dim tile t: the transposed read's source row 4 quad + col / 4,
+        //  dims 16 t + 4 (col % 4) .. + 3, i.e. chunk 2 t + (col % 4) / 2, half col % 2.
 #pragma unroll
-    for (int t = 0; t < kMDimTiles; ++t)
-        v_rd[t] = vrow * kMRowB + (((2 * t + ((col & 3) >> 1)) ^ vrow) << 4) + 8 * (col & 1);
+        for (int j = 0; j < kMKSteps; ++j)
+            k_rd[j] = col * TL::kRowB + (((4 * j + quad) ^ col) << 4);
+        const int vrow = 4 * quad + (col >> 2);
+#pragma unroll
+        for (int t = 0; t < kMDimTiles; ++t)
+            v_rd[t] = vrow * TL::kRowB + (((2 * t + ((col & 3) >> 1)) ^ vrow) << 4) + 8 * (col & 1);
+    } else {
+        //  K codes, k-step j: 8 bytes of row col at dims 32 j + 8 quad, i.e. chunk
+        //  2 j + quad / 2 (stored at chunk ^ ((row / 2) % 8)), half quad % 2.
+        //  V^T codes, dim tile t: 4 bytes (tokens 4 quad ..) of row 16 t + col.
+#pragma unroll
+        for (int j = 0; j < kMKSteps; ++j)
+            k_rd[j] = col * kMD + (((2 * j + (quad >> 1)) ^ ((col >> 1) & 7)) << 4) + 8 * (quad & 1);
+#pragma unroll
+        for (int t = 0; t < kMDimTiles; ++t) v_rd[t] = TL::kKB + (16 * t + col) * kMBS + 4 * quad;
+    }
 
     for (int x = sp.x0;;) {
         // ======== segment (b, g): blocks [blk_start, blk_start + nblk) ========
@@ -162,12 +225,25 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
                 qb[j] = __builtin_bit_cast(bf16x8_t, v);
             }
         }
-        // This lane's DMA sources inside one block: tile row 4 i + quad, chunk col ^ row.
-        uint32_t dma_off[kMTileDma];
+        // This lane's DMA sources inside one block's tile.
+        uint32_t dma_off[TL::kDma];
+        if constexpr (!MX) {
+            // tile row 4 i + quad, chunk col ^ row, rows Hkv * 256 bytes apart
+            const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * TL::kRowB;
 #pragma unroll
-        for (int i = 0; i < kMTileDma; ++i) {
-            const int t = 4 * i + quad;
-            dma_off[i] = static_cast<uint32_t>(t * row_stride + g * kMRowB + ((col ^ t) << 4));
+            for (int i = 0; i < TL::kDma; ++i) {
+                const int t = 4 * i + quad;
+                dma_off[i] = static_cast<uint32_t>(t * row_stride + g * TL::kRowB + ((col ^ t) << 4));
+            }
+        } else {
+            // LDS chunk p = 64 i + lane is chunk p % 8 of row p / 8, holding that row's
+            // chunk (p % 8) ^ ((row / 2) % 8)
+#pragma unroll
+            for (int i = 0; i < TL::kDma; ++i) {
+                const int p = kWave * i + lane;
+                const int t = p >> 3;
+                dma_off[i] = static_cast<uint32_t>(t * kMD + (((p & 7) ^ ((t >> 1) & 7)) << 4));
+            }
         }
         drain_vmem();  // q and the first ids have landed; the ring's accounting starts empty
 
@@ -180,32 +256,74 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
         auto issue = [&](int n) {
             if ((n & (kWave - 1)) == 0 && n > 0 && n + kWave < nblk) fetch_ids((n >> 6) + 1);
             const int pb = __builtin_amdgcn_readfirstlane(s_ids[(n >> 6) & 1][n & (kWave - 1)]);
-            const char *kb = kbase + static_cast<int64_t>(pb) * blk_stride;
-            const char *vb = vbase + static_cast<int64_t>(pb) * blk_stride;
-            const uint32_t slot = ring_lds + (n & (NBUF - 1)) * kMSlotB;
+            const uint32_t slot = ring_lds + (n & (NBUF - 1)) * TL::kSlotB;
+            if constexpr (!MX) {
+                const int64_t blk_b = static_cast<int64_t>(kMBS) * num_kv_heads * TL::kRowB;
+                const char *kb = kbase + static_cast<int64_t>(pb) * blk_b;
+                const char *vb = vbase + static_cast<int64_t>(pb) * blk_b;
 #pragma unroll
-            for (int i = 0; i < kMTileDma; ++i) dma16(kb, dma_off[i], slot + i * 1024);
+                for (int i = 0; i < TL::kDma; ++i) dma16(kb, dma_off[i], slot + i * 1024);
 #pragma unroll
-            for (int i = 0; i < kMTileDma; ++i) dma16(vb, dma_off[i], slot + kMTileB + i * 1024);
+                for (int i = 0; i < TL::kDma; ++i) dma16(vb, dma_off[i], slot + TL::kKB + i * 1024);
+            } else {
+                const int64_t tile = static_cast<int64_t>(pb) * num_kv_heads + g;
+                const char *kb = kbase + tile * TL::kKB;
+                const char *vb = vbase + tile * TL::kKB;
+#pragma unroll
+                for (int i = 0; i < TL::kDma; ++i) dma16(kb, dma_off[i], slot + i * 1024);
+#pragma unroll
+                for (int i = 0; i < TL::kDma; ++i)
+                    dma16(vb, static_cast<uint32_t>(kWave * i + lane) * 16u,
+                          slot + TL::kKB + i * 1024);
+                // the 64-byte scale tiles: lanes 16.. repeat lanes 0..15
+                const uint32_t so = static_cast<uint32_t>(lane & 15) * 4u;
+                dma4(k_scale + tile * TL::kScaleB, so, slot + 2 * TL::kKB);
+                dma4(v_scale + tile * TL::kScaleB, so, slot + 2 * TL::kKB + TL::kScaleLds);
+            }
         };
 
         auto compute_block = [&](int n) {
-            const uint32_t kslot = ring_lds + (n & (NBUF - 1)) * kMSlotB;
-            const uint32_t vslot = kslot + kMTileB;
+            const uint32_t kslot = ring_lds + (n & (NBUF - 1)) * TL::kSlotB;
             const int valid = ctx - (blk_start + n) * kMBS;  // tokens of this block in context
 
             // ---- scores S^T[token 4 quad + i, head col] ----
-            bf16x8_t ka[kMKSteps];
-#pragma unroll
-            for (int j = 0; j < kMKSteps; ++j) ka[j] = lds_b128(kslot + k_rd[j]);
             f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            u32x4_t vsc;  // MXFP8: V scales of tokens 4 quad + i (byte = 32-dim block)
+            if constexpr (!MX) {
+                bf16x8_t ka[kMKSteps];
 #pragma unroll
-            for (int j = 0; j < kMKSteps; ++j)
-                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[j], qb[j], s, 0, 0, 0);
+                for (int j = 0; j < kMKSteps; ++j) ka[j] = lds_b128(kslot + k_rd[j]);
+#pragma unroll
+                for (int j = 0; j < kMKSteps; ++j)
+                    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[j], qb[j], s, 0, 0, 0);
+            } else {
+                u32x2_t kc[kMKSteps];
+#pragma unroll
+                for (int j = 0; j < kMKSteps; ++j) kc[j] = lds_u64(kslot + k_rd[j]);
+                const uint32_t ksw = lds_u32(kslot + 2 * TL::kKB + 4 * col);  // token col's scales
+                vsc = lds_u128(kslot + 2 * TL::kKB + TL::kScaleLds + 16 * quad);
+#pragma unroll
+                for (int j = 0; j < kMKSteps; ++j) {
+                    const float ksc = e8m0_f32((ksw >> (8 * j)) & 0xFFu);
+                    const u32x4_t a = {fp8x2_bf16<false>(kc[j].x, ksc), fp8x2_bf16<true>(kc[j].x, ksc),
+                                       fp8x2_bf16<false>(kc[j].y, ksc), fp8x2_bf16<true>(kc[j].y, ksc)};
+                    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                                qb[j], s, 0, 0, 0);
+                }
+            }
             // V^T fragments, read while the scores are worked on
             s16x4_t va[kMDimTiles];
+            if constexpr (!MX) {
 #pragma unroll
-            for (int t = 0; t < kMDimTiles; ++t) va[t] = lds_tr_b64(vslot + v_rd[t]);
+                for (int t = 0; t < kMDimTiles; ++t) va[t] = lds_tr_b64(kslot + TL::kKB + v_rd[t]);
+            } else {
+#pragma unroll
+                for (int t = 0; t < kMDimTiles; ++t) {
+                    const uint32_t w = lds_u32(kslot + v_rd[t]);
+                    va[t] = __builtin_bit_cast(
+                        s16x4_t, u32x2_t{fp8x2_bf16<false>(w, 1.0f), fp8x2_bf16<true>(w, 1.0f)});
+                }
+            }
 
             float x[4];
 #pragma unroll
@@ -221,10 +339,12 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
 #pragma unroll
                 for (int t = 0; t < kMDimTiles; ++t) acc[t] *= alpha;
             }
-            const uint32_t p01 = pack_bf16(exp2_fast(x[0] - m_run), exp2_fast(x[1] - m_run));
-            const uint32_t p23 = pack_bf16(exp2_fast(x[2] - m_run), exp2_fast(x[3] - m_run));
+            float p[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p[i] = exp2_fast(x[i] - m_run);
+            const uint32_t p01 = pack_bf16(p[0], p[1]);
+            const uint32_t p23 = pack_bf16(p[2], p[3]);
             l_run += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
-            const s16x4_t pb = __builtin_bit_cast(s16x4_t, u32x2_t{p01, p23});
 
             // ---- O^T[16 t + 4 quad + i, head col] += V^T P^T ----
             if (valid < kMBS) {  // rows past the context contribute exactly zero, NaN or not
@@ -234,9 +354,25 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
                     for (int e = 0; e < 4; ++e)
                         if (4 * quad + e >= valid) va[t][e] = 0;
             }
+            if constexpr (!MX) {
+                const s16x4_t pb = __builtin_bit_cast(s16x4_t, u32x2_t{p01, p23});
 #pragma unroll
-            for (int t = 0; t < kMDimTiles; ++t)
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[t], pb, acc[t], 0, 0, 0);
+                for (int t = 0; t < kMDimTiles; ++t)
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[t], pb, acc[t], 0, 0, 0);
+            } else {
+#pragma unroll
+                for (int jv = 0; jv < kMD / kMxBlock; ++jv) {
+                    float ps[4];  // ldexp keeps masked (zero) weights zero whatever their scale
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        ps[i] = ldexpf(p[i], static_cast<int>((vsc[i] >> (8 * jv)) & 0xFFu) - 127);
+                    const s16x4_t pb = __builtin_bit_cast(
+                        s16x4_t, u32x2_t{pack_bf16(ps[0], ps[1]), pack_bf16(ps[2], ps[3])});
+#pragma unroll
+                    for (int t = 2 * jv; t < 2 * jv + 2; ++t)
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[t], pb, acc[t], 0, 0, 0);
+                }
+            }
         };
 
 #pragma unroll
@@ -247,7 +383,7 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
                 wait_lds();  // slot (n - 1) % NBUF and the ids in LDS are read
                 issue(n + NBUF - 1);
             }
-            wait_mblocks<NBUF>(min(NBUF - 1, nblk - 1 - n));
+            wait_mblocks<TL::kPerBlock, NBUF>(min(NBUF - 1, nblk - 1 - n));
             compute_block(n);
         }
 
@@ -278,20 +414,20 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
     }
 }
 
-template <int NBUF>
+template <bool MX, int NBUF>
 pa_status enqueue_gqa_mfma(const DecodeShape &s, const DecodeArgs &a, const DecodePlan &p,
                            float scale_log2, hipStream_t stream, std::string *why) {
     char *ws = static_cast<char *>(a.workspace);
     float *acc = reinterpret_cast<float *>(ws + p.acc_offset);
     float2 *ml = reinterpret_cast<float2 *>(ws + p.ml_offset);
     int32_t *prefix = reinterpret_cast<int32_t *>(ws + p.prefix_offset);
-    const auto kernel = gqa_mfma_partition_kernel<NBUF>;
+    const auto kernel = gqa_mfma_partition_kernel<MX, NBUF>;
     const int waves = stream_waves(kernel, kWave * kMGroupWaves, 1, kStreamWavesMax, kMGroupWaves);
     const int groups = (waves + kMGroupWaves - 1) / kMGroupWaves;
     hipLaunchKernelGGL(kernel, dim3(groups), dim3(kWave * kMGroupWaves), 0, stream, acc, ml,
-                       prefix, static_cast<const uint16_t *>(a.q),
-                       static_cast<const uint16_t *>(a.k_cache),
-                       static_cast<const uint16_t *>(a.v_cache), a.block_tables, a.context_lens,
+                       prefix, static_cast<const uint16_t *>(a.q), a.k_cache, a.v_cache,
+                       static_cast<const uint8_t *>(a.k_scale),
+                       static_cast<const uint8_t *>(a.v_scale), a.block_tables, a.context_lens,
                        scale_log2, s.num_seqs, s.num_kv_heads, p.group, s.max_blocks_per_seq,
                        waves);
     pa_status st = hip_status(hipGetLastError(), why, "partition launch");
@@ -302,14 +438,25 @@ pa_status enqueue_gqa_mfma(const DecodeShape &s, const DecodeArgs &a, const Deco
                       why, "reduce launch");
 }
 
+template <bool MX>
+pa_status launch_mfma(const DecodeShape &s, const DecodeArgs &a, const DecodePlan &p,
+                      hipStream_t stream, std::string *why) {
+    if (s.num_seqs == 0) return PA_OK;
+    const float scale_log2 = static_cast<float>(static_cast<double>(a.scale) * 1.4426950408889634);
+    if (p.ring_depth == 4) return enqueue_gqa_mfma<MX, 4>(s, a, p, scale_log2, stream, why);
+    return enqueue_gqa_mfma<MX, 2>(s, a, p, scale_log2, stream, why);
+}
+
 }  // namespace
 
 pa_status launch_gqa_mfma_decode(const DecodeShape &s, const DecodeArgs &a, const DecodePlan &p,
                                  hipStream_t stream, std::string *why) {
-    if (s.num_seqs == 0) return PA_OK;
-    const float scale_log2 = static_cast<float>(static_cast<double>(a.scale) * 1.4426950408889634);
-    if (p.ring_depth == 4) return enqueue_gqa_mfma<4>(s, a, p, scale_log2, stream, why);
-    return enqueue_gqa_mfma<2>(s, a, p, scale_log2, stream, why);
+    return launch_mfma<false>(s, a, p, stream, why);
+}
+
+pa_status launch_mxfp8_decode(const DecodeShape &s, const DecodeArgs &a, const DecodePlan &p,
+                              hipStream_t stream, std::string *why) {
+    return launch_mfma<true>(s, a, p, stream, why);
 }
 
 }  // namespace pa

@@ -23,6 +23,13 @@ pa_status launch_grouped_decode(const DecodeShape &s, const DecodeArgs &a,
 pa_status launch_gqa_mfma_decode(const DecodeShape &s, const DecodeArgs &a,
                                  const DecodePlan &plan, hipStream_t stream, std::string *why);
 
+// Quantizing append into MXFP8 caches (one work-group per token and KV head).
+pa_status launch_append_mxfp8(const MxAppendArgs &a, hipStream_t stream, std::string *why);
+
+// The matrix-core grouped decode over MXFP8 caches, then the stream-K reduce.
+pa_status launch_mxfp8_decode(const DecodeShape &s, const DecodeArgs &a,
+                              const DecodePlan &plan, hipStream_t stream, std::string *why);
+
 // Latent (576/512) decode on MFMA, followed by the same stream-K reduce.
 pa_status launch_latent_decode(const DecodeShape &s, const DecodeArgs &a,
                                const DecodePlan &plan, hipStream_t stream, std::string *why);

@@ -86,6 +86,33 @@ pa_status check_append(const AppendArgs &a, AppendPlan *plan, std::string *why) 
     return PA_OK;
 }
 
+pa_status check_append_mxfp8(const MxAppendArgs &a, std::string *why) {
+    if (!valid_dtype(a.dtype)) return fail(PA_ERR_DTYPE, why, "append (mxfp8): unknown dtype");
+    if (a.num_tokens < 0) return fail(PA_ERR_SHAPE, why, "append (mxfp8): num_tokens < 0");
+    if (a.num_blocks <= 0 || a.block_size <= 0 || a.num_kv_heads <= 0 || a.head_dim <= 0)
+        return fail(PA_ERR_SHAPE, why, "append (mxfp8): num_blocks, block_size, num_kv_heads "
+                                       "and head_dim must be > 0");
+    if (a.head_dim != kMxHeadDim)
+        return fail(PA_ERR_UNSUPPORTED, why, "append (mxfp8): runs head_dim 128");
+    if (a.num_kv_heads > 65535)
+        return fail(PA_ERR_UNSUPPORTED, why, "append (mxfp8): runs at most 65535 KV heads");
+    if (a.num_tokens > 0 && (!a.k_cache || !a.v_cache || !a.k_scale || !a.v_scale || !a.k ||
+                             !a.v || !a.slot_mapping))
+        return fail(PA_ERR_NULL, why, "append (mxfp8): caches, scales, k, v and slot_mapping "
+                                      "must be non-NULL");
+    if ((int64_t)a.num_blocks * a.block_size > INT32_MAX)
+        return fail(PA_ERR_SHAPE, why, "append (mxfp8): more than 2^31-1 slots");
+    const int64_t row = (int64_t)a.num_kv_heads * a.head_dim;
+    if (a.k_token_stride < row || a.v_token_stride < row)
+        return fail(PA_ERR_SHAPE, why, "append (mxfp8): a token stride is smaller than a row");
+    const int eb = elt_bytes(a.dtype);
+    if (!aligned(a.k, eb) || !aligned(a.v, eb) || !aligned(a.k_cache, 16) ||
+        !aligned(a.v_cache, 16) || !aligned(a.k_scale, 16) || !aligned(a.v_scale, 16))
+        return fail(PA_ERR_ALIGN, why, "append (mxfp8): caches and scales must be 16-byte "
+                                       "aligned, k and v aligned to their element size");
+    return PA_OK;
+}
+
 pa_status plan_decode(const DecodeShape &s, DecodePlan *plan, std::string *why) {
     if (!valid_dtype(s.dtype)) return fail(PA_ERR_DTYPE, why, "decode: unknown dtype");
     if (s.num_seqs < 0) return fail(PA_ERR_SHAPE, why, "decode: num_seqs < 0");
@@ -102,7 +129,18 @@ pa_status plan_decode(const DecodeShape &s, DecodePlan *plan, std::string *why) 
     const int G = s.num_q_heads / s.num_kv_heads;
     DecodePlan p{};
     p.group = G;
-    if (s.latent) {
+    if (s.mxfp8) {
+        if (s.latent || s.head_dim_k != kMxHeadDim || s.head_dim_v != kMxHeadDim ||
+            s.block_size != 16 || s.dtype != PA_BF16 || (G != 1 && G != 2 && G != 4 && G != 8))
+            return fail(PA_ERR_UNSUPPORTED, why,
+                        "decode (mxfp8): runs head_dim 128, block_size 16, bf16 q and out, "
+                        "num_q_heads / num_kv_heads in {1, 2, 4, 8}, with a V cache");
+        if ((int64_t)s.num_seqs * s.max_blocks_per_seq * s.num_kv_heads > INT32_MAX)
+            return fail(PA_ERR_SHAPE, why,
+                        "decode: num_seqs * max_blocks_per_seq * num_kv_heads exceeds 2^31-1");
+        p.path = DecodePath::kMxfp8;
+        p.ring_depth = grouped_ring_depth();
+    } else if (s.latent) {
         if (s.head_dim_k != 576 || s.head_dim_v != 512 || s.num_kv_heads != 1 ||
             s.block_size != 64 || s.dtype != PA_BF16 || s.num_q_heads % 16 != 0 ||
             s.num_q_heads > 128)
@@ -154,6 +192,11 @@ pa_status check_decode(const DecodeShape &s, const DecodeArgs &a, const DecodePl
         (a.v_cache && !aligned(a.v_cache, 16)) || !aligned(a.block_tables, 4) ||
         !aligned(a.context_lens, 4))
         return fail(PA_ERR_ALIGN, why, "decode: q, caches and out must be 16-byte aligned");
+    if (s.mxfp8 && (!a.v_cache || !a.k_scale || !a.v_scale))
+        return fail(PA_ERR_NULL, why, "decode (mxfp8): v_cache, k_scale and v_scale must be "
+                                      "non-NULL");
+    if (s.mxfp8 && (!aligned(a.k_scale, 16) || !aligned(a.v_scale, 16)))
+        return fail(PA_ERR_ALIGN, why, "decode (mxfp8): scales must be 16-byte aligned");
     if (!a.workspace || a.workspace_bytes < plan.bytes)
         return fail(PA_ERR_WORKSPACE, why,
                     "decode: workspace missing or smaller than pa_decode_workspace_size()");

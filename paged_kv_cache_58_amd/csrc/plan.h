@@ -39,9 +39,35 @@ struct AppendPlan {
 
 pa_status check_append(const AppendArgs &a, AppendPlan *plan, std::string *why);
 
+// MXFP8 caches (E4M3 codes with one E8M0 scale per 32 values of a head row):
+// K codes [num_blocks, Hkv, bs, d], V codes [num_blocks, Hkv, d, bs], scales
+// [num_blocks, Hkv, bs, d / 32].  The append quantizes fp32 or bf16 rows.
+constexpr int kMxHeadDim = 128;  // head dim the MXFP8 kernels run
+constexpr int kMxBlock = 32;     // values per E8M0 scale
+struct MxAppendArgs {
+    void *k_cache;
+    void *v_cache;
+    void *k_scale;
+    void *v_scale;
+    const void *k;
+    int64_t k_token_stride;
+    const void *v;
+    int64_t v_token_stride;
+    const int32_t *slot_mapping;
+    int32_t num_tokens;
+    int32_t num_blocks;
+    int32_t block_size;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    pa_dtype dtype;  // of k and v
+};
+
+pa_status check_append_mxfp8(const MxAppendArgs &a, std::string *why);
+
 // kGrouped: VALU dot products; kGroupedMfma: the same split and partials with
-// the per-block products on the matrix cores (bf16, head dim 128).
-enum class DecodePath { kGrouped, kGroupedMfma, kLatent };
+// the per-block products on the matrix cores (bf16, head dim 128); kMxfp8: that
+// matrix-core kernel reading MXFP8 caches.
+enum class DecodePath { kGrouped, kGroupedMfma, kMxfp8, kLatent };
 
 // Most work-groups the grouped path's stream-K partition kernel launches
 // (one per resident wave slot; 256 CUs x 16 waves), which sizes its
@@ -68,6 +94,7 @@ struct DecodeShape {
     int32_t block_size;
     int32_t max_blocks_per_seq;
     bool latent;  // v_cache == NULL
+    bool mxfp8;   // MXFP8 caches (dtype is then that of q and out)
     pa_dtype dtype;
 };
 
@@ -104,6 +131,8 @@ struct DecodeArgs {
     const void *v_cache;
     const int32_t *block_tables;
     const int32_t *context_lens;
+    const void *k_scale;  // MXFP8 caches only
+    const void *v_scale;
     float scale;
     int32_t num_blocks;
     void *workspace;

@@ -21,7 +21,7 @@ FAKE = 0x100000  # a 256-byte aligned non-NULL address; never dereferenced here
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_binding_exports():
@@ -126,3 +126,65 @@ def test_append_rejects(kw, status):
 
 def test_append_zero_tokens_is_a_noop():
     assert _append(n=0, kc=None, k=None, sm=None, vc=None, v=None) == 0
+
+
+def _decode_mx(**kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, ksc=FAKE, vsc=FAKE, bt=FAKE, cl=FAKE, scale=0.125,
+             B=4, hq=64, hkv=8, d=128, bs=16, nb=100, mb=16, dtype=pa.PA_BF16, ws=FAKE,
+             wsb=1 << 30)
+    a.update(kw)
+    return pa.lib().pa_decode_mxfp8(a["out"], a["q"], a["k"], a["v"], a["ksc"], a["vsc"],
+                                    a["bt"], a["cl"], a["scale"], a["B"], a["hq"], a["hkv"],
+                                    a["d"], a["bs"], a["nb"], a["mb"], a["dtype"], a["ws"],
+                                    a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ksc=None), 1),
+    (dict(vsc=None), 1),
+    (dict(v=None), 1),
+    (dict(q=None), 1),
+    (dict(d=64), 4),
+    (dict(bs=32), 4),
+    (dict(dtype=pa.PA_F32), 4),  # q and out are bf16
+    (dict(hq=24, hkv=8), 4),
+    (dict(hq=60), 2),
+    (dict(wsb=1024), 5),
+    (dict(ksc=FAKE + 4), 7),
+    (dict(vsc=FAKE + 8), 7),
+])
+def test_decode_mxfp8_rejects(kw, status):
+    assert _decode_mx(**kw) == status
+    assert pa.lib().pa_last_error().decode() != ""
+
+
+def test_decode_mxfp8_no_sequences_is_a_noop():
+    assert _decode_mx(B=0, out=None, q=None, ws=None, wsb=0) == 0
+
+
+def _append_mx(**kw):
+    a = dict(kc=FAKE, vc=FAKE, ksc=FAKE, vsc=FAKE, k=FAKE, ks=1024, v=FAKE, vs=1024, sm=FAKE,
+             n=4, nb=10, bs=16, hkv=8, d=128, dtype=pa.PA_BF16)
+    a.update(kw)
+    return pa.lib().pa_cache_append_mxfp8(a["kc"], a["vc"], a["ksc"], a["vsc"], a["k"], a["ks"],
+                                          a["v"], a["vs"], a["sm"], a["n"], a["nb"], a["bs"],
+                                          a["hkv"], a["d"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=9), 3),
+    (dict(k=None), 1),
+    (dict(vsc=None), 1),
+    (dict(sm=None), 1),
+    (dict(ks=100), 2),
+    (dict(n=-1), 2),
+    (dict(d=64), 4),
+    (dict(kc=FAKE + 2), 7),
+    (dict(k=FAKE + 1), 7),
+])
+def test_append_mxfp8_rejects(kw, status):
+    assert _append_mx(**kw) == status
+
+
+def test_append_mxfp8_zero_tokens_is_a_noop():
+    assert _append_mx(n=0, kc=None, vc=None, ksc=None, vsc=None, k=None, v=None, sm=None) == 0
