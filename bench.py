@@ -4,7 +4,10 @@
 A step is one pass of the whole hot path over one batch: pa_cache_append of
 each sequence's new token through the slot mapping, then pa_decode of every
 sequence over its context including that token.  Inputs are seeded synthetic
-data of the named workload, resident in HBM before timing starts.
+data of the named workload, resident in HBM before timing starts.  With
+--kv-format mxfp8 the caches hold the workload's K/V rows quantized to MXFP8
+(quantized by the library before timing) and the step is
+pa_cache_append_mxfp8 + pa_decode_mxfp8.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -33,8 +36,8 @@ WORKLOAD_TEXT = {
     "c5": "MLA-style latent decode bf16: batch 64, 128 heads over one 576-dim latent "
           "(V = first 512), block 64, ctx U[2048,8192]",
 }
-KERNEL_SOURCES = ["grouped_decode.hip", "latent_decode.hip", "append.hip", "device_common.h",
-                  "plan.cpp", "plan.h"]
+KERNEL_SOURCES = ["grouped_decode.hip", "gqa_mfma_decode.hip", "latent_decode.hip", "append.hip",
+                  "mxfp8_append.hip", "device_common.h", "plan.cpp", "plan.h"]
 
 
 def log(msg: str) -> None:
@@ -62,12 +65,104 @@ def load_traffic(cfg: str, decode_bytes: int):
     return t.get("hbm_bytes_per_decode")
 
 
+def valid_slots(w, seqs=None):
+    """Slots of every cached token t < ctx_b of the listed sequences."""
+    import numpy as np
+
+    bs = w.spec.block_size
+    seqs = range(w.spec.num_seqs) if seqs is None else seqs
+    parts = []
+    for b in seqs:
+        t = np.arange(int(w.context_lens[b]))
+        parts.append(w.block_tables[b, t // bs] * bs + t % bs)
+    return np.concatenate(parts).astype(np.int32)
+
+
+def mx_oracle_check(w, L1, got, decode_bytes, args, oracle):
+    """Oracle check of an MXFP8 run on a sample of sequences: the oracle
+    quantizes those sequences' rows (and the appended token) into its own
+    pools and decodes them; that decode is also the timed CPU leg."""
+    import numpy as np
+
+    spec = w.spec
+    bs = spec.block_size
+    seqs = sorted(set(np.linspace(0, spec.num_seqs - 1, min(6, spec.num_seqs)).astype(int).tolist()))
+    nb = w.num_blocks
+    pools = (np.full((nb, spec.num_kv_heads, bs, 128), 0x7F, np.uint8),
+             np.full((nb, spec.num_kv_heads, 128, bs), 0x7F, np.uint8),
+             np.full((nb, spec.num_kv_heads, bs, 4), 0x7F, np.uint8),
+             np.full((nb, spec.num_kv_heads, bs, 4), 0x7F, np.uint8))
+    sl = valid_slots(w, seqs)
+    oracle.append_mxfp8(*pools, np.ascontiguousarray(w.k_cache[sl // bs, sl % bs]),
+                        np.ascontiguousarray(w.v_cache[sl // bs, sl % bs]), sl)
+    new = np.full(spec.num_seqs, -1, np.int32)
+    new[seqs] = w.slot_mapping[seqs]
+    oracle.append_mxfp8(*pools, w.k_new, w.v_new, new)
+    pairs = [(b, h) for b in seqs for h in range(spec.num_q_heads)]
+    threads = oracle.default_threads()
+    t_c = time.perf_counter()
+    ref = oracle.decode_mxfp8(w.q, *pools, w.block_tables, L1, w.scale, pairs=pairs,
+                              threads=threads)
+    cpu_s = time.perf_counter() - t_c
+    sel = np.array(pairs)
+    d = np.abs(got[sel[:, 0], sel[:, 1]] - ref[sel[:, 0], sel[:, 1]])
+    frac = float(L1[seqs].sum()) / float(L1.sum())
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = {"value": round(decode_bytes * frac / cpu_s / 1e9, 3), "unit": "GB/s",
+               "cores": threads, "kind": "oracle",
+               "sample": f"oracle MXFP8 decode of {len(seqs)} of the {spec.num_seqs} sequences "
+                         f"({frac:.1%} of the attended tokens, all {spec.num_q_heads} heads), "
+                         f"fp64, {cpu_s:.2f} s wall; GB/s over that sample's share of the bytes",
+               "tokens_per_s": round(len(seqs) / cpu_s, 3)}
+        log(f"[bench] oracle (mxfp8 sample): {cpu_s:.2f}s on {threads} threads")
+    return d, cpu
+
+
+def native_oracle_check(w, L1, got, decode_bytes, args, oracle):
+    """Oracle check of a run on the workload's own caches: 128 sampled rows
+    with --no-cpu-baseline, else the full decode, timed (median of 3) as the
+    CPU leg."""
+    import numpy as np
+
+    spec = w.spec
+    hk = w.k_cache.copy()
+    hv = None if w.v_cache is None else w.v_cache.copy()
+    oracle.append(hk, hv, w.k_new, w.v_new, w.slot_mapping)
+    if args.no_cpu_baseline:
+        rng = np.random.default_rng(0)
+        rows = [(int(b), int(h)) for b, h in zip(rng.integers(0, spec.num_seqs, 128),
+                                                 rng.integers(0, spec.num_q_heads, 128))]
+        ref = oracle.decode(w.q, hk, hv, w.block_tables, L1, w.scale, pairs=rows,
+                            head_dim_v=spec.head_dim_v)
+        sel = np.array(rows)
+        return np.abs(got[sel[:, 0], sel[:, 1]] - ref[sel[:, 0], sel[:, 1]]), None
+    threads = oracle.default_threads()
+    times = []
+    for _ in range(3):  # median of three full decodes
+        t_c = time.perf_counter()
+        ref = oracle.decode(w.q, hk, hv, w.block_tables, L1, w.scale, threads=threads,
+                            head_dim_v=spec.head_dim_v)
+        times.append(time.perf_counter() - t_c)
+    cpu_s = float(np.median(times))
+    cpu = {"value": round(decode_bytes / cpu_s / 1e9, 3), "unit": "GB/s",
+           "cores": threads, "kind": "oracle",
+           "sample": f"the full decode of the {args.config} batch "
+                     f"({spec.num_seqs} seqs x {spec.num_q_heads} heads), fp64, "
+                     f"median of 3 runs, {cpu_s:.2f} s wall each",
+           "tokens_per_s": round(spec.num_seqs / cpu_s, 3)}
+    log(f"[bench] oracle: {cpu_s:.2f}s per decode on {threads} threads")
+    return np.abs(got - ref), cpu
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="c3", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--kv-format", default="native", choices=["native", "mxfp8"],
+                    help="cache format: the workload's dtype, or MXFP8 (bf16 d=128 shapes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter scaling)")
@@ -101,20 +196,50 @@ def main() -> int:
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
-    q, kc, vc = to_dev(w.q), to_dev(w.k_cache), to_dev(w.v_cache)
+    mx = args.kv_format == "mxfp8"
+    if mx and (spec.dtype != "bf16" or spec.mla or spec.head_dim_k != 128):
+        log(f"--kv-format mxfp8 runs the bf16 head-dim-128 workloads, not {args.config}")
+        return 2
+    q = to_dev(w.q)
     k_new, v_new = to_dev(w.k_new), to_dev(w.v_new)
     bt = torch.from_numpy(w.block_tables).to(dev)
     L1 = (w.context_lens + 1).astype(np.int32)  # context after the append
     cl = torch.from_numpy(L1).to(dev)
     sm = torch.from_numpy(w.slot_mapping).to(dev)
-    ws = pa.alloc_workspace(q, kc, bt, head_dim_v=spec.head_dim_v)
     out = torch.empty((spec.num_seqs, spec.num_q_heads, spec.head_dim_v), dtype=q.dtype,
                       device=dev)
+    if not mx:
+        kc, vc = to_dev(w.k_cache), to_dev(w.v_cache)
+        ws = pa.alloc_workspace(q, kc, bt, head_dim_v=spec.head_dim_v)
+
+        def append():
+            pa.cache_append(kc, vc, k_new, v_new, sm)
+
+        def decode():
+            pa.decode(out, q, kc, vc, bt, cl, w.scale, ws)
+    else:
+        # MXFP8 pools (unused slots hold the E4M3 NaN code), filled with every
+        # cached row of the workload by the library's quantizing append
+        bs = spec.block_size
+        pools = pa.alloc_mxfp8_cache(w.num_blocks, bs, spec.num_kv_heads, 128, dev, fill=0x7F)
+        slots = valid_slots(w)
+        for lo in range(0, slots.size, 1 << 16):
+            sl = slots[lo: lo + (1 << 16)]
+            pa.cache_append_mxfp8(*pools, to_dev(np.ascontiguousarray(w.k_cache[sl // bs, sl % bs])),
+                                  to_dev(np.ascontiguousarray(w.v_cache[sl // bs, sl % bs])),
+                                  torch.from_numpy(sl).to(dev))
+        ws = pa.alloc_mxfp8_workspace(q, pools[0], bt)
+
+        def append():
+            pa.cache_append_mxfp8(*pools, k_new, v_new, sm)
+
+        def decode():
+            pa.decode_mxfp8(out, q, *pools, bt, cl, w.scale, ws)
     torch.cuda.synchronize()
 
     def step():
-        pa.cache_append(kc, vc, k_new, v_new, sm)
-        pa.decode(out, q, kc, vc, bt, cl, w.scale, ws)
+        append()
+        decode()
 
     for _ in range(args.warmup):
         step()
@@ -131,9 +256,9 @@ def main() -> int:
     start.record()
     for i in range(K):
         ev[i][0].record()
-        pa.cache_append(kc, vc, k_new, v_new, sm)
+        append()
         ev[i][1].record()
-        pa.decode(out, q, kc, vc, bt, cl, w.scale, ws)
+        decode()
         ev[i][2].record()
     end.record()
     torch.cuda.synchronize()
@@ -145,8 +270,8 @@ def main() -> int:
 
     # accounting over the context actually attended (ctx + 1)
     w_after = workloads.Workload(**{**w.__dict__, "context_lens": L1})
-    decode_bytes = workloads.algorithmic_bytes(w_after)
-    append_bytes = workloads.append_bytes(w)
+    decode_bytes = (workloads.algorithmic_bytes_mxfp8 if mx else workloads.algorithmic_bytes)(w_after)
+    append_bytes = (workloads.append_bytes_mxfp8 if mx else workloads.append_bytes)(w)
     flops = workloads.algorithmic_flops(w_after)
     step_bytes = decode_bytes + append_bytes
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -170,38 +295,13 @@ def main() -> int:
     import oracle
 
     got = out.float().cpu().numpy().astype(np.float64)
-    hk = w.k_cache.copy()
-    hv = None if w.v_cache is None else w.v_cache.copy()
-    oracle.append(hk, hv, w.k_new, w.v_new, w.slot_mapping)
-    cpu = None
-    if args.no_cpu_baseline:
-        rng = np.random.default_rng(0)
-        rows = [(int(b), int(h)) for b, h in zip(rng.integers(0, spec.num_seqs, 128),
-                                                 rng.integers(0, spec.num_q_heads, 128))]
-        ref = oracle.decode(w.q, hk, hv, w.block_tables, L1, w.scale, pairs=rows,
-                            head_dim_v=spec.head_dim_v)
-        sel = np.array(rows)
-        d = np.abs(got[sel[:, 0], sel[:, 1]] - ref[sel[:, 0], sel[:, 1]])
+    if mx:
+        d, cpu = mx_oracle_check(w, L1, got, decode_bytes, args, oracle)
     else:
-        threads = oracle.default_threads()
-        times = []
-        for _ in range(3):  # median of three full decodes
-            t_c = time.perf_counter()
-            ref = oracle.decode(w.q, hk, hv, w.block_tables, L1, w.scale, threads=threads,
-                                head_dim_v=spec.head_dim_v)
-            times.append(time.perf_counter() - t_c)
-        cpu_s = float(np.median(times))
-        d = np.abs(got - ref)
-        cpu = {"value": round(decode_bytes / cpu_s / 1e9, 3), "unit": "GB/s",
-               "cores": threads, "kind": "oracle",
-               "sample": f"the full decode of the {args.config} batch "
-                         f"({spec.num_seqs} seqs x {spec.num_q_heads} heads), fp64, "
-                         f"median of 3 runs, {cpu_s:.2f} s wall each",
-               "tokens_per_s": round(spec.num_seqs / cpu_s, 3)}
-        log(f"[bench] oracle: {cpu_s:.2f}s per decode on {threads} threads")
+        d, cpu = native_oracle_check(w, L1, got, decode_bytes, args, oracle)
     max_err = float(d.max())
 
-    traffic = load_traffic(args.config, decode_bytes)
+    traffic = load_traffic(args.config + ("_mxfp8" if mx else ""), decode_bytes)
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -215,7 +315,9 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": spec.dtype,
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT[args.config], "name": spec.name,
+        "config": {"workload": WORKLOAD_TEXT[args.config] + (
+                       ", KV cache in MXFP8 (E4M3 + E8M0 per 32 values)" if mx else ""),
+                   "name": spec.name + ("-mxfp8" if mx else ""), "kv_format": args.kv_format,
                    "global_batch": spec.num_seqs, "seq_len": int(L1.max()),
                    "mean_context": float(L1.mean()), "parallelism": "single GPU"},
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
@@ -225,7 +327,8 @@ def main() -> int:
         "us_decode_p10_p90": [round(float(np.percentile(t_decode, 10)) * 1e3, 2),
                               round(float(np.percentile(t_decode, 90)) * 1e3, 2)],
         "decode_tflops": round(flops / (dec_ms * 1e-3) / 1e12, 3),
-        "roofline": {"bound": "hbm", "kernel": "pa_decode (partition + log-sum-exp reduce)",
+        "roofline": {"bound": "hbm", "kernel": ("pa_decode_mxfp8" if mx else "pa_decode") +
+                     " (partition + log-sum-exp reduce)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": decode_bytes},
@@ -233,6 +336,8 @@ def main() -> int:
         "max_abs_err_vs_oracle": max_err,
         "wall_s_timed": round(wall, 4),
     }
+    if mx:
+        result["dtype"] = "fp8-e4m3 (MXFP8 cache), bf16 q/out, fp32 accumulate"
     if spec.mla:
         # the latent contraction sits near the ridge: its matrix-core roofline too
         tflops = flops / (dec_ms * 1e-3) / 1e12

@@ -308,3 +308,32 @@ def append_bytes(w: Workload) -> int:
     s = w.spec
     row = s.num_kv_heads * (s.head_dim_k + (0 if s.mla else s.head_dim_v)) * s.elt
     return 2 * row * int((w.slot_mapping >= 0).sum()) + 4 * s.num_seqs
+
+
+# MXFP8 caches: one E4M3 byte per value plus one E8M0 byte per 32 values.
+MX_BLOCK = 32
+
+
+def mxfp8_kv_bytes_per_token_layer(num_kv_heads, head_dim) -> int:
+    return 2 * num_kv_heads * (head_dim + head_dim // MX_BLOCK)
+
+
+def algorithmic_bytes_mxfp8(w: Workload) -> int:
+    """algorithmic_bytes() with the K/V rows stored as MXFP8 (q and O stay in
+    the workload's dtype)."""
+    s = w.spec
+    ctx = w.context_lens.astype(np.int64)
+    kv = int(ctx.sum()) * mxfp8_kv_bytes_per_token_layer(s.num_kv_heads, s.head_dim_k)
+    q = s.num_seqs * s.num_q_heads * s.head_dim_k * s.elt
+    o = s.num_seqs * s.num_q_heads * s.head_dim_v * s.elt
+    ids = 4 * int((-(-ctx // s.block_size)).sum())
+    return kv + q + o + ids + 4 * s.num_seqs
+
+
+def append_bytes_mxfp8(w: Workload) -> int:
+    """Bytes one quantizing append moves: the source rows read, codes and
+    scales written, and the slot ids."""
+    s = w.spec
+    n = int((w.slot_mapping >= 0).sum())
+    src = 2 * s.num_kv_heads * s.head_dim_k * s.elt
+    return n * (src + mxfp8_kv_bytes_per_token_layer(s.num_kv_heads, s.head_dim_k)) + 4 * s.num_seqs
