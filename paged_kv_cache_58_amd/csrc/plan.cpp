@@ -22,9 +22,6 @@ pa_status fail(pa_status st, std::string *why, const std::string &msg) {
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Blocks a work-group streams into LDS on the grouped path (ring depth).
-// Two 8 KB slots per wave let LDS hold eight waves per CU, which beats a
-// deeper ring with fewer waves.  PA_RING_DEPTH (2 or 4) overrides it.
 // Whether a grouped-shape bf16 decode with head dim 128 runs its per-block
 // products on the matrix cores.  PA_GQA_MFMA (0 or 1) overrides the default.
 bool grouped_mfma_default(const DecodeShape &s) {
@@ -34,10 +31,14 @@ bool grouped_mfma_default(const DecodeShape &s) {
     return false;
 }
 
-int grouped_ring_depth() {
+// Cache blocks each wave of the grouped paths streams into LDS (ring depth):
+// four 8 KB bf16 slots per wave (four waves per CU) measure faster than two
+// with eight waves; MXFP8 slots are half the size and take two.
+// PA_RING_DEPTH (2 or 4) overrides either default.
+int grouped_ring_depth(int default_depth = 4) {
     const char *env = std::getenv("PA_RING_DEPTH");
-    if (env && *env && std::atoi(env) == 2) return 2;
-    return 4;
+    if (env && *env) return std::atoi(env) == 2 ? 2 : 4;
+    return default_depth;
 }
 
 }  // namespace
@@ -139,7 +140,9 @@ pa_status plan_decode(const DecodeShape &s, DecodePlan *plan, std::string *why) 
             return fail(PA_ERR_SHAPE, why,
                         "decode: num_seqs * max_blocks_per_seq * num_kv_heads exceeds 2^31-1");
         p.path = DecodePath::kMxfp8;
-        p.ring_depth = grouped_ring_depth();
+        // half-size MXFP8 slots: two per wave let LDS hold 16 waves per CU,
+        // which measures faster than four slots at 8 waves
+        p.ring_depth = grouped_ring_depth(2);
     } else if (s.latent) {
         if (s.head_dim_k != 576 || s.head_dim_v != 512 || s.num_kv_heads != 1 ||
             s.block_size != 64 || s.dtype != PA_BF16 || s.num_q_heads % 16 != 0 ||
