@@ -251,3 +251,41 @@ def decode_mxfp8(q: np.ndarray, k8: np.ndarray, v8: np.ndarray, ks: np.ndarray, 
     if rc != 0:
         raise RuntimeError(f"oracle_decode_mxfp8 failed with code {rc}")
     return out
+
+
+# ---------------------------------------------------------------------------
+# Several new query tokens per sequence, causal among themselves
+# ---------------------------------------------------------------------------
+
+def visible_lengths(context_lens: np.ndarray, q_len: int) -> np.ndarray:
+    """[B, q_len] number of cached tokens query i of sequence b may attend:
+    the last q_len of the L_b cached tokens are the queries themselves, and
+    query i sits at position L_b - q_len + i, seeing tokens 0 .. that
+    position (the causal mask of "Étape 2: Attention avec KV Cache").  A
+    query whose position would be negative sees nothing."""
+    L = np.asarray(context_lens, dtype=np.int64)[:, None]
+    return np.clip(L - q_len + 1 + np.arange(q_len)[None, :], 0, None).astype(np.int32)
+
+
+def decode_multi(q: np.ndarray, k_cache, v_cache, block_tables, context_lens, scale,
+                 mxfp8: Optional[tuple] = None, pairs: Optional[Sequence] = None,
+                 threads: Optional[int] = None) -> np.ndarray:
+    """float64 [B, q_len, Hq, d]: each query row through the single-query
+    oracle over its visible prefix.  q [B, q_len, Hq, d].  With ``mxfp8`` =
+    (k_scale, v_scale) the caches are MXFP8 codes (decode_mxfp8's layouts).
+    ``pairs`` optionally lists (b, i) query rows to compute (others NaN)."""
+    B, Q = q.shape[0], q.shape[1]
+    vis = visible_lengths(context_lens, Q)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    todo = [(b, i) for b in range(B) for i in range(Q)] if pairs is None else list(pairs)
+    out = np.full(q.shape[:3] + ((v_cache.shape[2] if mxfp8 else v_cache.shape[3]),),
+                  np.nan, dtype=np.float64)
+    for b, i in todo:
+        q1 = np.ascontiguousarray(q[b, i][None])
+        cl = vis[b, i:i + 1]
+        if mxfp8 is None:
+            out[b, i] = decode(q1, k_cache, v_cache, bt[b:b + 1], cl, scale, threads=threads)[0]
+        else:
+            out[b, i] = decode_mxfp8(q1, k_cache, v_cache, mxfp8[0], mxfp8[1], bt[b:b + 1], cl,
+                                     scale, threads=threads)[0]
+    return out
