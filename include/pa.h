@@ -225,6 +225,50 @@ pa_status pa_decode_mxfp8(void *out, const void *q, const void *k_cache,
                           int32_t max_blocks_per_seq, pa_dtype dtype,
                           void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Several new query tokens per sequence, causal among themselves: the shape
+ * of verifying k drafted tokens in one pass of the target model (section
+ * "Décodage spéculatif" of "Optimisation de l'inférence": the candidates are
+ * scored in one forward pass that looks like a prefill) and of a prefill
+ * chunk over a paged context.  The last q_len of a sequence's L = context_lens[b] cached
+ * tokens are its queries (appended to the cache beforehand), and query i,
+ * at position L - q_len + i, attends to tokens 0 .. L - q_len + i: the
+ * upper-triangular mask of "Étape 2: Attention avec KV Cache" on the same
+ * page.  A query whose position is negative (L < q_len - i) gets O = 0.
+ *
+ * pa_decode_multi_workspace_size — bytes of workspace pa_decode_multi needs
+ * (0 when the sizes are not valid); the same for both cache formats.
+ */
+size_t pa_decode_multi_workspace_size(int32_t num_seqs, int32_t q_len,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size,
+                                      int32_t max_blocks_per_seq);
+
+/*
+ * pa_decode_multi — for b < num_seqs, i < q_len, h < num_q_heads:
+ *   out[b, i, h, :] = softmax_t(scale * q[b, i, h, :] . K[t, g, :]) V[t, g, :]
+ * over t < L_b - q_len + i + 1, g = h / (num_q_heads / num_kv_heads).
+ *
+ *   q, out       [num_seqs, q_len, num_q_heads, head_dim], bf16 (dtype must
+ *                be PA_BF16).
+ *   k_cache, v_cache  bf16 [num_blocks, block_size, num_kv_heads, head_dim]
+ *                when k_scale == v_scale == NULL; MXFP8 codes in the
+ *                layouts of pa_cache_append_mxfp8 when both scales are set.
+ *   other arguments as for pa_decode.
+ * Runs head_dim 128, block_size 16, (num_q_heads / num_kv_heads) * q_len
+ * <= 64; q_len == 1 is the single-query decode.  Errors as for pa_decode;
+ * PA_ERR_NULL when exactly one scale pointer is NULL.
+ */
+pa_status pa_decode_multi(void *out, const void *q, const void *k_cache,
+                          const void *v_cache, const void *k_scale,
+                          const void *v_scale, const int32_t *block_tables,
+                          const int32_t *context_lens, float scale,
+                          int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t num_blocks,
+                          int32_t max_blocks_per_seq, pa_dtype dtype,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static text for a status code ("PA_OK", ...); never NULL. */
 const char *pa_status_string(pa_status status);
 

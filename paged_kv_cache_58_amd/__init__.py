@@ -22,7 +22,8 @@ STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_DTYPE",
           4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP", 7: "PA_ERR_ALIGN"}
 
 EXPORTS = ("pa_cache_append", "pa_decode_workspace_size", "pa_decode", "pa_cache_append_mxfp8",
-           "pa_decode_mxfp8", "pa_status_string", "pa_last_error")
+           "pa_decode_mxfp8", "pa_decode_multi_workspace_size", "pa_decode_multi",
+           "pa_status_string", "pa_last_error")
 
 _lib = None
 
@@ -56,6 +57,11 @@ def lib():
         L.pa_decode_mxfp8.restype = ctypes.c_int
         L.pa_decode_mxfp8.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_float, I32, I32, I32, I32,
                                       I32, I32, I32, ctypes.c_int, P, ctypes.c_size_t, P]
+        L.pa_decode_multi_workspace_size.restype = ctypes.c_size_t
+        L.pa_decode_multi_workspace_size.argtypes = [I32] * 7
+        L.pa_decode_multi.restype = ctypes.c_int
+        L.pa_decode_multi.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_float, I32, I32, I32, I32,
+                                      I32, I32, I32, I32, ctypes.c_int, P, ctypes.c_size_t, P]
         L.pa_status_string.restype = ctypes.c_char_p
         L.pa_status_string.argtypes = [ctypes.c_int]
         L.pa_last_error.restype = ctypes.c_char_p
@@ -214,5 +220,46 @@ def decode_mxfp8(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, conte
     _check(lib().pa_decode_mxfp8(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
         _ptr(block_tables), _ptr(context_lens), float(scale), B, hq, hkv, d, bs, nb,
+        block_tables.shape[1], _dtype_code(q), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Several new query tokens per sequence (causal among themselves)
+# ---------------------------------------------------------------------------
+
+def decode_multi_workspace_size(num_seqs, q_len, num_q_heads, num_kv_heads, head_dim, block_size,
+                                max_blocks_per_seq) -> int:
+    return int(lib().pa_decode_multi_workspace_size(num_seqs, q_len, num_q_heads, num_kv_heads,
+                                                    head_dim, block_size, max_blocks_per_seq))
+
+
+def alloc_multi_workspace(q, num_kv_heads, block_size, block_tables):
+    """Workspace for decode_multi; q is [B, q_len, Hq, d]."""
+    import torch
+
+    B, Q, hq, d = q.shape
+    n = decode_multi_workspace_size(B, Q, hq, num_kv_heads, d, block_size, block_tables.shape[1])
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+
+
+def decode_multi(out, q, k_cache, v_cache, block_tables, context_lens, scale, workspace,
+                 k_scale=None, v_scale=None, stream=None) -> None:
+    """q [B, q_len, Hq, d] bf16: the last q_len of each sequence's context_lens[b]
+    cached tokens, query i attending to tokens 0 .. L_b - q_len + i.  out
+    [B, q_len, Hq, d].  bf16 caches [num_blocks, block_size, Hkv, d], or MXFP8
+    caches (layouts of cache_append_mxfp8) when k_scale and v_scale are given."""
+    B, Q, hq, d = q.shape
+    if k_scale is None:
+        nb, bs, hkv, _ = k_cache.shape
+    else:
+        nb, hkv, bs, _ = k_cache.shape
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("out", out),
+                    ("block_tables", block_tables), ("context_lens", context_lens)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    _check(lib().pa_decode_multi(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_tables), _ptr(context_lens), float(scale), B, Q, hq, hkv, d, bs, nb,
         block_tables.shape[1], _dtype_code(q), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))

@@ -136,6 +136,49 @@ PA_EXPORT pa_status pa_decode_mxfp8(void *out, const void *q, const void *k_cach
     return finish(st, why);
 }
 
+PA_EXPORT size_t pa_decode_multi_workspace_size(int32_t num_seqs, int32_t q_len,
+                                                int32_t num_q_heads, int32_t num_kv_heads,
+                                                int32_t head_dim, int32_t block_size,
+                                                int32_t max_blocks_per_seq) {
+    pa::DecodeShape s = make_shape(false, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                   head_dim, block_size, max_blocks_per_seq, PA_BF16);
+    s.q_len = q_len;
+    pa::DecodePlan plan{};
+    if (pa::plan_decode(s, &plan, nullptr) != PA_OK) return 0;
+    return plan.bytes;
+}
+
+PA_EXPORT pa_status pa_decode_multi(void *out, const void *q, const void *k_cache,
+                                    const void *v_cache, const void *k_scale,
+                                    const void *v_scale, const int32_t *block_tables,
+                                    const int32_t *context_lens, float scale, int32_t num_seqs,
+                                    int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                    int32_t max_blocks_per_seq, pa_dtype dtype, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+    std::string why;
+    if ((k_scale == nullptr) != (v_scale == nullptr))
+        return finish(PA_ERR_NULL, "decode (several queries): k_scale and v_scale must both be "
+                                   "NULL (bf16 caches) or both set (MXFP8 caches)");
+    pa::DecodeShape s = make_shape(false, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                   head_dim, block_size, max_blocks_per_seq, dtype);
+    s.mxfp8 = k_scale != nullptr;
+    s.q_len = q_len;
+    pa::DecodePlan plan{};
+    pa_status st = pa::plan_decode(s, &plan, &why);
+    if (st != PA_OK) return finish(st, why);
+    if (!v_cache && num_seqs > 0)
+        return finish(PA_ERR_NULL, "decode (several queries): v_cache must be non-NULL");
+    const pa::DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens, k_scale,
+                           v_scale, scale, num_blocks, workspace, workspace_bytes};
+    st = pa::check_decode(s, a, plan, &why);
+    if (st != PA_OK || num_seqs == 0) return finish(st, why);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    st = s.mxfp8 ? pa::launch_mxfp8_decode(s, a, plan, hs, &why)
+                 : pa::launch_gqa_mfma_decode(s, a, plan, hs, &why);
+    return finish(st, why);
+}
+
 PA_EXPORT const char *pa_status_string(pa_status status) {
     switch (status) {
         case PA_OK: return "PA_OK";

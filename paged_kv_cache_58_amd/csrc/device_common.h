@@ -185,29 +185,33 @@ __device__ __forceinline__ bool find_share(int sid, int nshares, int num_seqs, i
 }
 
 // ---------------------------------------------------------------------------
-// Reduce over the stream-K partial slots of each (sequence, query head).
-// Slot row (s * group + h % group) holds head h's partial of the segment
-// (sequence, KV head h / group) from stream share s:
-// O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
-// One work-group of W waves per (query head, sequence); wave w takes slots
-// w, w + W, ... of the segment.
+// Reduce over the stream-K partial slots of each (sequence, query, query
+// head).  A segment (sequence, KV head g) has C = group * q_len columns, column
+// i * group + h % group for query i and head h; slot row (s * C + column)
+// holds that column's partial of the segment from stream share s:
+// O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s, M = max_s m_s
+// (O = 0 when no slot saw a token: an empty context).  One work-group of W
+// waves per (query, query head, sequence), blockIdx.x = i * Hq + h; wave w
+// takes slots w, w + W, ... of the segment.  out is [B, q_len, Hq, D].
 // ---------------------------------------------------------------------------
 template <typename T, int D, int W>
 __global__ __launch_bounds__(kWave *W) void stream_reduce_kernel(
     T *__restrict__ out, const float *__restrict__ ws_acc, const float2 *__restrict__ ws_ml,
     const int32_t *__restrict__ ws_prefix, const int32_t *__restrict__ context_lens,
-    int num_seqs, int num_kv_heads, int group, int block_size, int waves) {
+    int num_seqs, int num_kv_heads, int group, int block_size, int waves, int q_len) {
     constexpr int DPL = D / kWave;
-    const int h = blockIdx.x;
+    const int num_q_heads = num_kv_heads * group;
+    const int qi = blockIdx.x / num_q_heads;
+    const int h = blockIdx.x - qi * num_q_heads;
     const int b = blockIdx.y;
     const int g = h / group;
-    const int hh = h - g * group;
+    const int hh = qi * group + (h - g * group);  // column within the segment
+    const int ncols = group * q_len;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    const int num_q_heads = num_kv_heads * group;
     const int nb = (context_lens[b] + block_size - 1) / block_size;
-    T *o = out + (static_cast<int64_t>(b) * num_q_heads + h) * D + lane * DPL;
+    T *o = out + ((static_cast<int64_t>(b) * q_len + qi) * num_q_heads + h) * D + lane * DPL;
 
     __shared__ float s_max[W];
     __shared__ float s_num[W][D];
@@ -225,10 +229,10 @@ __global__ __launch_bounds__(kWave *W) void stream_reduce_kernel(
     const int seg_lo = num_kv_heads * ws_prefix[b] + g * nb;
     const int w0 = seg_lo / share;
     const int n = (seg_lo + nb - 1) / share - w0 + 1;  // partial slots of this segment
-    const int64_t first = (static_cast<int64_t>(w0) + k) * group + hh;  // row of slot w0 + k
+    const int64_t first = (static_cast<int64_t>(w0) + k) * ncols + hh;  // row of slot w0 + k
 
     float M = kNegInf;
-    for (int p = tid; p < n; p += kWave * W) M = fmaxf(M, ws_ml[first + static_cast<int64_t>(p) * group].x);
+    for (int p = tid; p < n; p += kWave * W) M = fmaxf(M, ws_ml[first + static_cast<int64_t>(p) * ncols].x);
     for (int sh = 32; sh >= 1; sh >>= 1) M = fmaxf(M, __shfl_xor(M, sh));
     if constexpr (W > 1) {
         if (lane == 0) s_max[wave] = M;
@@ -242,8 +246,14 @@ __global__ __launch_bounds__(kWave *W) void stream_reduce_kernel(
 #pragma unroll
     for (int d = 0; d < DPL; ++d) num[d] = 0.f;
     float den = 0.f;
+    if (M == kNegInf) {  // no slot saw a token (a query that sees nothing): O = 0
+        if (wave == 0)
+#pragma unroll
+            for (int d = 0; d < DPL; ++d) o[d] = static_cast<T>(0.f);
+        return;
+    }
     for (int p = wave; p < n; p += W) {
-        const int64_t r = first + static_cast<int64_t>(p) * group;
+        const int64_t r = first + static_cast<int64_t>(p) * ncols;
         const float2 mp = ws_ml[r];
         const float wgt = exp2_fast(mp.x - M);
         den = fmaf(wgt, mp.y, den);
@@ -294,16 +304,16 @@ template <typename T, int D>
 hipError_t enqueue_stream_reduce(T *out, const float *ws_acc, const float2 *ws_ml,
                                  const int32_t *ws_prefix, const int32_t *context_lens,
                                  int num_seqs, int num_q_heads, int num_kv_heads, int group,
-                                 int block_size, int waves, hipStream_t stream) {
-    const dim3 grid(num_q_heads, num_seqs);
-    if (static_cast<int64_t>(num_seqs) * num_q_heads < 2048)
+                                 int block_size, int waves, hipStream_t stream, int q_len = 1) {
+    const dim3 grid(num_q_heads * q_len, num_seqs);
+    if (static_cast<int64_t>(num_seqs) * num_q_heads * q_len < 2048)
         hipLaunchKernelGGL((stream_reduce_kernel<T, D, 4>), grid, dim3(kWave * 4), 0, stream, out,
                            ws_acc, ws_ml, ws_prefix, context_lens, num_seqs, num_kv_heads, group,
-                           block_size, waves);
+                           block_size, waves, q_len);
     else
         hipLaunchKernelGGL((stream_reduce_kernel<T, D, 1>), grid, dim3(kWave), 0, stream, out,
                            ws_acc, ws_ml, ws_prefix, context_lens, num_seqs, num_kv_heads, group,
-                           block_size, waves);
+                           block_size, waves, q_len);
     return hipGetLastError();
 }
 

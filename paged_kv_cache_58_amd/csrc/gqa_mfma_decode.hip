@@ -66,6 +66,7 @@ constexpr int kMD = 128;              // head dim (K and V)
 constexpr int kMKSteps = kMD / 32;    // score k-steps
 constexpr int kMDimTiles = kMD / 16;  // 16-dim tiles of the output
 constexpr float kMSlack = 8.0f;       // lazy-rescale threshold, log2 units
+constexpr float kMFloor = -3.0e38f;   // finite stand-in for a running max of -inf
 constexpr int kMGroupWaves = 4;
 
 // Per-format tile geometry of one (block, KV head).
@@ -136,17 +137,24 @@ __device__ __forceinline__ void wait_mblocks(int later) {
 }
 
 // Partition kernel: the stream-K schedule and partial-slot layout of the
-// VALU grouped kernel (slot row (share + b * Hkv + g) * G + head, fp32
+// VALU grouped kernel (slot row (share + b * Hkv + g) * C + column, fp32
 // accumulator of D dims plus (max, sum) in log2 units).  MX selects MXFP8
 // caches (k_scale, v_scale used); otherwise the caches are bf16.
-template <bool MX, int NBUF>
+//
+// Columns: with q_len new query tokens per sequence (causal among
+// themselves, as in the masked attention of "Étape 2: Attention avec KV
+// Cache": query i of the last q_len cached tokens sees tokens up to
+// position L - q_len + i), the N dimension of the products holds C = G *
+// q_len (query, head) pairs, column c = i * G + h, in NT tiles of 16.  One
+// K/V fetch and one V^T read then serve all of them.  q is [B, q_len, Hq, D].
+template <bool MX, int NBUF, int NT>
 __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel(
     float *__restrict__ ws_acc, float2 *__restrict__ ws_ml, int32_t *__restrict__ ws_prefix,
     const uint16_t *__restrict__ q, const void *__restrict__ k_cache,
     const void *__restrict__ v_cache, const uint8_t *__restrict__ k_scale,
     const uint8_t *__restrict__ v_scale, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, float scale_log2, int num_seqs, int num_kv_heads,
-    int group, int max_blocks, int nshares) {
+    int group, int q_len, int max_blocks, int nshares) {
     using TL = MTile<MX>;
     static_assert((NBUF & (NBUF - 1)) == 0 && NBUF >= 2 && NBUF <= 4, "ring depth 2 or 4");
     const int lane = threadIdx.x & (kWave - 1);
@@ -156,6 +164,17 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
     const int col = lane & 15;
     const int quad = lane >> 4;
     const int num_q_heads = num_kv_heads * group;
+    const int ncols = group * q_len;
+    // this lane's columns (one per tile): query qi[ct], head hh[ct] of the group
+    int qi[NT], hh[NT];
+    bool live[NT];
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+        const int c = 16 * ct + col;
+        live[ct] = c < ncols;
+        qi[ct] = live[ct] ? c / group : 0;
+        hh[ct] = live[ct] ? c - qi[ct] * group : 0;
+    }
 
     __shared__ __attribute__((aligned(16))) char s_ring_all[kMGroupWaves][NBUF * TL::kSlotB];
     __shared__ __attribute__((aligned(16))) int32_t s_ids_all[kMGroupWaves][2][kWave];
@@ -210,21 +229,27 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
         fetch_ids(0);
         if (nblk > kWave) fetch_ids(1);
 
-        // q^T as the score B operand: head col of the group, dims 32 j + 8 quad .. + 7;
-        // columns past the group hold zeros.
-        bf16x8_t qb[kMKSteps];
-        {
-            const bool live = col < group;
-            const uint16_t *qr = q + (static_cast<int64_t>(b) * num_q_heads + g * group +
-                                      (live ? col : 0)) * kMD + 8 * quad;
+        // q^T as the score B operand: column (query qi, head g G + hh), dims
+        // 32 j + 8 quad .. + 7; columns past G * q_len hold zeros.
+        bf16x8_t qb[NT][kMKSteps];
+        // tokens below lim[ct] are visible to this lane's column of tile ct
+        int lim[NT];
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+            const uint16_t *qr =
+                q + ((static_cast<int64_t>(b) * q_len + qi[ct]) * num_q_heads + g * group + hh[ct]) *
+                        kMD + 8 * quad;
 #pragma unroll
             for (int j = 0; j < kMKSteps; ++j) {
                 u32x4_t v = *reinterpret_cast<const u32x4_t *>(qr + 32 * j);
                 asm volatile("" : "+v"(v));
-                if (!live) v = u32x4_t{0u, 0u, 0u, 0u};
-                qb[j] = __builtin_bit_cast(bf16x8_t, v);
+                if (!live[ct]) v = u32x4_t{0u, 0u, 0u, 0u};
+                qb[ct][j] = __builtin_bit_cast(bf16x8_t, v);
             }
+            lim[ct] = live[ct] ? ctx - q_len + 1 + qi[ct] : ctx;
         }
+        // blocks ending at or before this token are visible to every column
+        const int all_visible = ctx - q_len + 1;
         // This lane's DMA sources inside one block's tile.
         uint32_t dma_off[TL::kDma];
         if constexpr (!MX) {
@@ -247,11 +272,16 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
         }
         drain_vmem();  // q and the first ids have landed; the ring's accounting starts empty
 
-        float m_run = kNegInf;  // running max of head col (scaled, log2 units)
-        float l_run = 0.f;      // this lane's share of the running sum of head col
-        f32x4_t acc[kMDimTiles];
+        float m_run[NT];  // running max of the lane's column (scaled, log2 units)
+        float l_run[NT];  // this lane's share of the column's running sum
+        f32x4_t acc[NT][kMDimTiles];
 #pragma unroll
-        for (int t = 0; t < kMDimTiles; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int ct = 0; ct < NT; ++ct) {
+            m_run[ct] = kNegInf;
+            l_run[ct] = 0.f;
+#pragma unroll
+            for (int t = 0; t < kMDimTiles; ++t) acc[ct][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
 
         auto issue = [&](int n) {
             if ((n & (kWave - 1)) == 0 && n > 0 && n + kWave < nblk) fetch_ids((n >> 6) + 1);
@@ -284,31 +314,43 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
 
         auto compute_block = [&](int n) {
             const uint32_t kslot = ring_lds + (n & (NBUF - 1)) * TL::kSlotB;
-            const int valid = ctx - (blk_start + n) * kMBS;  // tokens of this block in context
+            const int tok0 = (blk_start + n) * kMBS;
+            const int valid = ctx - tok0;  // tokens of this block in context
 
-            // ---- scores S^T[token 4 quad + i, head col] ----
-            f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            // ---- scores S^T[token 4 quad + i, column 16 ct + col] ----
+            f32x4_t s[NT];
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct) s[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             u32x4_t vsc;  // MXFP8: V scales of tokens 4 quad + i (byte = 32-dim block)
+            uint32_t vw[kMDimTiles];  // MXFP8: V^T codes, tokens 4 quad .. of dim 16 t + col
             if constexpr (!MX) {
                 bf16x8_t ka[kMKSteps];
 #pragma unroll
                 for (int j = 0; j < kMKSteps; ++j) ka[j] = lds_b128(kslot + k_rd[j]);
 #pragma unroll
                 for (int j = 0; j < kMKSteps; ++j)
-                    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[j], qb[j], s, 0, 0, 0);
+#pragma unroll
+                    for (int ct = 0; ct < NT; ++ct)
+                        s[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[j], qb[ct][j], s[ct], 0, 0, 0);
             } else {
+                // every LDS read of the block first, so their latencies overlap
                 u32x2_t kc[kMKSteps];
 #pragma unroll
                 for (int j = 0; j < kMKSteps; ++j) kc[j] = lds_u64(kslot + k_rd[j]);
                 const uint32_t ksw = lds_u32(kslot + 2 * TL::kKB + 4 * col);  // token col's scales
                 vsc = lds_u128(kslot + 2 * TL::kKB + TL::kScaleLds + 16 * quad);
 #pragma unroll
+                for (int t = 0; t < kMDimTiles; ++t) vw[t] = lds_u32(kslot + v_rd[t]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
                 for (int j = 0; j < kMKSteps; ++j) {
                     const float ksc = e8m0_f32((ksw >> (8 * j)) & 0xFFu);
                     const u32x4_t a = {fp8x2_bf16<false>(kc[j].x, ksc), fp8x2_bf16<true>(kc[j].x, ksc),
                                        fp8x2_bf16<false>(kc[j].y, ksc), fp8x2_bf16<true>(kc[j].y, ksc)};
-                    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                                qb[j], s, 0, 0, 0);
+#pragma unroll
+                    for (int ct = 0; ct < NT; ++ct)
+                        s[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, a), qb[ct][j], s[ct], 0, 0, 0);
                 }
             }
             // V^T fragments, read while the scores are worked on
@@ -318,33 +360,50 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
                 for (int t = 0; t < kMDimTiles; ++t) va[t] = lds_tr_b64(kslot + TL::kKB + v_rd[t]);
             } else {
 #pragma unroll
-                for (int t = 0; t < kMDimTiles; ++t) {
-                    const uint32_t w = lds_u32(kslot + v_rd[t]);
-                    va[t] = __builtin_bit_cast(
-                        s16x4_t, u32x2_t{fp8x2_bf16<false>(w, 1.0f), fp8x2_bf16<true>(w, 1.0f)});
-                }
+                for (int t = 0; t < kMDimTiles; ++t)
+                    va[t] = __builtin_bit_cast(s16x4_t, u32x2_t{fp8x2_bf16<false>(vw[t], 1.0f),
+                                                                fp8x2_bf16<true>(vw[t], 1.0f)});
             }
 
-            float x[4];
+            // ---- online softmax per column; probabilities rounded to bf16 ----
+            const bool full = tok0 + kMBS <= all_visible;  // no column masks a token of this block
+            float p[NT][4];
+            uint32_t p01[NT], p23[NT];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = (4 * quad + i < valid) ? s[i] * scale_log2 : kNegInf;
-            float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-            bm = fmaxf(bm, __shfl_xor(bm, 16));
-            bm = fmaxf(bm, __shfl_xor(bm, 32));
-            if (__builtin_amdgcn_ballot_w64(bm > m_run + kMSlack) != 0) {
-                const float m_new = fmaxf(m_run, bm);
-                const float alpha = exp2_fast(m_run - m_new);
-                l_run *= alpha;
-                m_run = m_new;
+            for (int ct = 0; ct < NT; ++ct) {
+                float x[4];
+                if (full) {
 #pragma unroll
-                for (int t = 0; t < kMDimTiles; ++t) acc[t] *= alpha;
+                    for (int i = 0; i < 4; ++i) x[i] = s[ct][i] * scale_log2;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        x[i] = (tok0 + 4 * quad + i < lim[ct]) ? s[ct][i] * scale_log2 : kNegInf;
+                }
+                float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+                bm = fmaxf(bm, __shfl_xor(bm, 16));
+                bm = fmaxf(bm, __shfl_xor(bm, 32));
+                // A column that has seen no visible token yet keeps m_run = -inf
+                // (with several queries a block can be masked for some columns
+                // only).  The branch below is taken by the whole wave, so both
+                // maxima are clamped to a finite floor: such a column then gets
+                // alpha = 1 and weights 0, never exp2(-inf + inf).
+                if (__builtin_amdgcn_ballot_w64(bm > m_run[ct] + kMSlack) != 0) {
+                    const float m_new = fmaxf(m_run[ct], bm);
+                    const float alpha =
+                        exp2_fast(fmaxf(m_run[ct], kMFloor) - fmaxf(m_new, kMFloor));
+                    l_run[ct] *= alpha;
+                    m_run[ct] = m_new;
+#pragma unroll
+                    for (int t = 0; t < kMDimTiles; ++t) acc[ct][t] *= alpha;
+                }
+                const float m_e = fmaxf(m_run[ct], kMFloor);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) p[ct][i] = exp2_fast(x[i] - m_e);
+                p01[ct] = pack_bf16(p[ct][0], p[ct][1]);
+                p23[ct] = pack_bf16(p[ct][2], p[ct][3]);
+                l_run[ct] += (bf16_lo(p01[ct]) + bf16_hi(p01[ct])) + (bf16_lo(p23[ct]) + bf16_hi(p23[ct]));
             }
-            float p[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) p[i] = exp2_fast(x[i] - m_run);
-            const uint32_t p01 = pack_bf16(p[0], p[1]);
-            const uint32_t p23 = pack_bf16(p[2], p[3]);
-            l_run += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
 
             // ---- O^T[16 t + 4 quad + i, head col] += V^T P^T ----
             if (valid < kMBS) {  // rows past the context contribute exactly zero, NaN or not
@@ -355,22 +414,32 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
                         if (4 * quad + e >= valid) va[t][e] = 0;
             }
             if constexpr (!MX) {
-                const s16x4_t pb = __builtin_bit_cast(s16x4_t, u32x2_t{p01, p23});
 #pragma unroll
-                for (int t = 0; t < kMDimTiles; ++t)
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[t], pb, acc[t], 0, 0, 0);
+                for (int ct = 0; ct < NT; ++ct) {
+                    const s16x4_t pb = __builtin_bit_cast(s16x4_t, u32x2_t{p01[ct], p23[ct]});
+#pragma unroll
+                    for (int t = 0; t < kMDimTiles; ++t)
+                        acc[ct][t] =
+                            __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[t], pb, acc[ct][t], 0, 0, 0);
+                }
             } else {
 #pragma unroll
                 for (int jv = 0; jv < kMD / kMxBlock; ++jv) {
-                    float ps[4];  // ldexp keeps masked (zero) weights zero whatever their scale
+                    int e[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        ps[i] = ldexpf(p[i], static_cast<int>((vsc[i] >> (8 * jv)) & 0xFFu) - 127);
-                    const s16x4_t pb = __builtin_bit_cast(
-                        s16x4_t, u32x2_t{pack_bf16(ps[0], ps[1]), pack_bf16(ps[2], ps[3])});
+                    for (int i = 0; i < 4; ++i) e[i] = static_cast<int>((vsc[i] >> (8 * jv)) & 0xFFu) - 127;
 #pragma unroll
-                    for (int t = 2 * jv; t < 2 * jv + 2; ++t)
-                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[t], pb, acc[t], 0, 0, 0);
+                    for (int ct = 0; ct < NT; ++ct) {
+                        float ps[4];  // ldexp keeps masked (zero) weights zero whatever their scale
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) ps[i] = ldexpf(p[ct][i], e[i]);
+                        const s16x4_t pb = __builtin_bit_cast(
+                            s16x4_t, u32x2_t{pack_bf16(ps[0], ps[1]), pack_bf16(ps[2], ps[3])});
+#pragma unroll
+                        for (int t = 2 * jv; t < 2 * jv + 2; ++t)
+                            acc[ct][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[t], pb,
+                                                                                  acc[ct][t], 0, 0, 0);
+                    }
                 }
             }
         };
@@ -388,16 +457,20 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
         }
 
         // ---- this segment's partial: unnormalised acc, running max and sum ----
-        float l_tot = l_run + __shfl_xor(l_run, 16);
-        l_tot += __shfl_xor(l_tot, 32);
-        if (col < group) {
-            const int64_t slot_row =
-                (static_cast<int64_t>(sid) + static_cast<int64_t>(b) * num_kv_heads + g) * group;
-            if (quad == 0) ws_ml[slot_row + col] = make_float2(m_run, l_tot);
-            float *dst = ws_acc + (slot_row + col) * kMD + 4 * quad;
+        const int64_t slot_row =
+            (static_cast<int64_t>(sid) + static_cast<int64_t>(b) * num_kv_heads + g) * ncols;
 #pragma unroll
-            for (int t = 0; t < kMDimTiles; ++t)
-                *reinterpret_cast<f32x4_t *>(dst + 16 * t) = acc[t];
+        for (int ct = 0; ct < NT; ++ct) {
+            float l_tot = l_run[ct] + __shfl_xor(l_run[ct], 16);
+            l_tot += __shfl_xor(l_tot, 32);
+            if (live[ct]) {
+                const int64_t row = slot_row + 16 * ct + col;
+                if (quad == 0) ws_ml[row] = make_float2(m_run[ct], l_tot);
+                float *dst = ws_acc + row * kMD + 4 * quad;
+#pragma unroll
+                for (int t = 0; t < kMDimTiles; ++t)
+                    *reinterpret_cast<f32x4_t *>(dst + 16 * t) = acc[ct][t];
+            }
         }
 
         x += nblk;
@@ -414,28 +487,36 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
     }
 }
 
-template <bool MX, int NBUF>
+template <bool MX, int NBUF, int NT>
 pa_status enqueue_gqa_mfma(const DecodeShape &s, const DecodeArgs &a, const DecodePlan &p,
                            float scale_log2, hipStream_t stream, std::string *why) {
     char *ws = static_cast<char *>(a.workspace);
     float *acc = reinterpret_cast<float *>(ws + p.acc_offset);
     float2 *ml = reinterpret_cast<float2 *>(ws + p.ml_offset);
     int32_t *prefix = reinterpret_cast<int32_t *>(ws + p.prefix_offset);
-    const auto kernel = gqa_mfma_partition_kernel<MX, NBUF>;
+    const auto kernel = gqa_mfma_partition_kernel<MX, NBUF, NT>;
     const int waves = stream_waves(kernel, kWave * kMGroupWaves, 1, kStreamWavesMax, kMGroupWaves);
     const int groups = (waves + kMGroupWaves - 1) / kMGroupWaves;
     hipLaunchKernelGGL(kernel, dim3(groups), dim3(kWave * kMGroupWaves), 0, stream, acc, ml,
                        prefix, static_cast<const uint16_t *>(a.q), a.k_cache, a.v_cache,
                        static_cast<const uint8_t *>(a.k_scale),
                        static_cast<const uint8_t *>(a.v_scale), a.block_tables, a.context_lens,
-                       scale_log2, s.num_seqs, s.num_kv_heads, p.group, s.max_blocks_per_seq,
-                       waves);
+                       scale_log2, s.num_seqs, s.num_kv_heads, p.group, s.q_len,
+                       s.max_blocks_per_seq, waves);
     pa_status st = hip_status(hipGetLastError(), why, "partition launch");
     if (st != PA_OK) return st;
     return hip_status(enqueue_stream_reduce<uint16_t, kMD>(
                           static_cast<uint16_t *>(a.out), acc, ml, prefix, a.context_lens,
-                          s.num_seqs, s.num_q_heads, s.num_kv_heads, p.group, kMBS, waves, stream),
+                          s.num_seqs, s.num_q_heads, s.num_kv_heads, p.group, kMBS, waves, stream,
+                          s.q_len),
                       why, "reduce launch");
+}
+
+template <bool MX, int NT>
+pa_status launch_mfma_nt(const DecodeShape &s, const DecodeArgs &a, const DecodePlan &p,
+                         float scale_log2, hipStream_t stream, std::string *why) {
+    if (p.ring_depth == 4) return enqueue_gqa_mfma<MX, 4, NT>(s, a, p, scale_log2, stream, why);
+    return enqueue_gqa_mfma<MX, 2, NT>(s, a, p, scale_log2, stream, why);
 }
 
 template <bool MX>
@@ -443,8 +524,10 @@ pa_status launch_mfma(const DecodeShape &s, const DecodeArgs &a, const DecodePla
                       hipStream_t stream, std::string *why) {
     if (s.num_seqs == 0) return PA_OK;
     const float scale_log2 = static_cast<float>(static_cast<double>(a.scale) * 1.4426950408889634);
-    if (p.ring_depth == 4) return enqueue_gqa_mfma<MX, 4>(s, a, p, scale_log2, stream, why);
-    return enqueue_gqa_mfma<MX, 2>(s, a, p, scale_log2, stream, why);
+    const int cols = p.group * s.q_len;  // at most 16 * kMaxColTiles (plan_decode checks it)
+    if (cols <= 16) return launch_mfma_nt<MX, 1>(s, a, p, scale_log2, stream, why);
+    if (cols <= 32) return launch_mfma_nt<MX, 2>(s, a, p, scale_log2, stream, why);
+    return launch_mfma_nt<MX, 4>(s, a, p, scale_log2, stream, why);
 }
 
 }  // namespace

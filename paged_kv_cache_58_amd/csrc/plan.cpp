@@ -130,6 +130,14 @@ pa_status plan_decode(const DecodeShape &s, DecodePlan *plan, std::string *why) 
     const int G = s.num_q_heads / s.num_kv_heads;
     DecodePlan p{};
     p.group = G;
+    if (s.q_len < 1) return fail(PA_ERR_SHAPE, why, "decode: q_len must be >= 1");
+    if (s.q_len > 1 && (s.latent || (!s.mxfp8 && s.dtype != PA_BF16) || s.head_dim_k != 128 ||
+                        s.head_dim_v != 128 || s.block_size != 16 ||
+                        (int64_t)G * s.q_len > 16 * kMaxColTiles))
+        return fail(PA_ERR_UNSUPPORTED, why,
+                    "decode (several queries per sequence): runs bf16 q with bf16 or MXFP8 "
+                    "caches, head_dim 128, block_size 16, (num_q_heads / num_kv_heads) * "
+                    "q_len <= 64");
     if (s.mxfp8) {
         if (s.latent || s.head_dim_k != kMxHeadDim || s.head_dim_v != kMxHeadDim ||
             s.block_size != 16 || s.dtype != PA_BF16 || (G != 1 && G != 2 && G != 4 && G != 8))
@@ -165,12 +173,14 @@ pa_status plan_decode(const DecodeShape &s, DecodePlan *plan, std::string *why) 
         if ((int64_t)s.num_seqs * s.max_blocks_per_seq * s.num_kv_heads > INT32_MAX)
             return fail(PA_ERR_SHAPE, why,
                         "decode: num_seqs * max_blocks_per_seq * num_kv_heads exceeds 2^31-1");
-        p.path = grouped_mfma_default(s) ? DecodePath::kGroupedMfma : DecodePath::kGrouped;
+        p.path = s.q_len > 1 || grouped_mfma_default(s) ? DecodePath::kGroupedMfma
+                                                         : DecodePath::kGrouped;
         p.ring_depth = grouped_ring_depth();
     }
     size_t rows;  // (slot, head) rows of partial results
     if (p.path != DecodePath::kLatent)
-        rows = ((size_t)kStreamWavesMax + (size_t)s.num_seqs * s.num_kv_heads) * (size_t)G;
+        rows = ((size_t)kStreamWavesMax + (size_t)s.num_seqs * s.num_kv_heads) * (size_t)G *
+               (size_t)s.q_len;
     else
         rows = ((size_t)kLatentWavesMax + (size_t)s.num_seqs) *
                (size_t)(latent_waves(s.num_q_heads) * kLatentHeadTile);

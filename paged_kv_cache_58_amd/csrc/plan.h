@@ -96,7 +96,12 @@ struct DecodeShape {
     bool latent;  // v_cache == NULL
     bool mxfp8;   // MXFP8 caches (dtype is then that of q and out)
     pa_dtype dtype;
+    int32_t q_len = 1;  // new query tokens per sequence, causal among themselves
 };
+
+// Most (query, head) columns one KV head's work may carry on the matrix-core
+// grouped kernel: G * q_len <= 16 * kMaxColTiles.
+constexpr int kMaxColTiles = 4;
 
 // Split-context plan.  Both paths leave, per partial result and query head,
 // an unnormalised fp32 accumulator plus (max, sum) in the workspace for the

@@ -188,3 +188,41 @@ def test_append_mxfp8_rejects(kw, status):
 
 def test_append_mxfp8_zero_tokens_is_a_noop():
     assert _append_mx(n=0, kc=None, vc=None, ksc=None, vsc=None, k=None, v=None, sm=None) == 0
+
+
+def _decode_multi(**kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, ksc=None, vsc=None, bt=FAKE, cl=FAKE, scale=0.125,
+             B=4, Q=4, hq=64, hkv=8, d=128, bs=16, nb=100, mb=16, dtype=pa.PA_BF16, ws=FAKE,
+             wsb=1 << 30)
+    a.update(kw)
+    return pa.lib().pa_decode_multi(a["out"], a["q"], a["k"], a["v"], a["ksc"], a["vsc"], a["bt"],
+                                    a["cl"], a["scale"], a["B"], a["Q"], a["hq"], a["hkv"], a["d"],
+                                    a["bs"], a["nb"], a["mb"], a["dtype"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ksc=FAKE), 1),           # one scale pointer without the other
+    (dict(vsc=FAKE), 1),
+    (dict(v=None), 1),
+    (dict(q=None), 1),
+    (dict(Q=0), 2),
+    (dict(Q=9), 4),                # G * q_len = 72 > 64
+    (dict(hq=8, hkv=8, Q=65), 4),
+    (dict(d=64), 4),
+    (dict(bs=32), 4),
+    (dict(dtype=pa.PA_F32), 4),
+    (dict(wsb=1024), 5),
+    (dict(ksc=FAKE + 4, vsc=FAKE), 7),
+])
+def test_decode_multi_rejects(kw, status):
+    assert _decode_multi(**kw) == status
+    assert pa.lib().pa_last_error().decode() != ""
+
+
+def test_decode_multi_workspace_size():
+    one = pa.decode_workspace_size(100, 64, 8, 128, 128, 16, 513)
+    four = pa.decode_multi_workspace_size(100, 4, 64, 8, 128, 16, 513)
+    assert four > 3 * one and four % 256 == 0
+    assert pa.decode_multi_workspace_size(100, 1, 64, 8, 128, 16, 513) == one
+    assert pa.decode_multi_workspace_size(100, 9, 64, 8, 128, 16, 513) == 0
+    assert _decode_multi(B=0, out=None, q=None, ws=None, wsb=0) == 0
