@@ -7,7 +7,10 @@ sequence over its context including that token.  Inputs are seeded synthetic
 data of the named workload, resident in HBM before timing starts.  With
 --kv-format mxfp8 the caches hold the workload's K/V rows quantized to MXFP8
 (quantized by the library before timing) and the step is
-pa_cache_append_mxfp8 + pa_decode_mxfp8.
+pa_cache_append_mxfp8 + pa_decode_mxfp8.  With --q-len K > 1 the decode is
+pa_decode_multi: the last K cached tokens of every sequence (the appended one
+among them) are its queries, causal among themselves, the shape of verifying
+K - 1 drafted tokens plus the new one in one pass.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -78,15 +81,19 @@ def valid_slots(w, seqs=None):
     return np.concatenate(parts).astype(np.int32)
 
 
-def mx_oracle_check(w, L1, got, decode_bytes, args, oracle):
-    """Oracle check of an MXFP8 run on a sample of sequences: the oracle
-    quantizes those sequences' rows (and the appended token) into its own
-    pools and decodes them; that decode is also the timed CPU leg."""
+def sample_seqs(spec):
+    import numpy as np
+
+    return sorted(set(np.linspace(0, spec.num_seqs - 1, min(6, spec.num_seqs)).astype(int).tolist()))
+
+
+def oracle_mx_pools(w, seqs, oracle):
+    """The oracle's own MXFP8 pools holding the listed sequences' cached rows
+    and their appended token."""
     import numpy as np
 
     spec = w.spec
     bs = spec.block_size
-    seqs = sorted(set(np.linspace(0, spec.num_seqs - 1, min(6, spec.num_seqs)).astype(int).tolist()))
     nb = w.num_blocks
     pools = (np.full((nb, spec.num_kv_heads, bs, 128), 0x7F, np.uint8),
              np.full((nb, spec.num_kv_heads, 128, bs), 0x7F, np.uint8),
@@ -98,6 +105,53 @@ def mx_oracle_check(w, L1, got, decode_bytes, args, oracle):
     new = np.full(spec.num_seqs, -1, np.int32)
     new[seqs] = w.slot_mapping[seqs]
     oracle.append_mxfp8(*pools, w.k_new, w.v_new, new)
+    return pools
+
+
+def multi_oracle_check(w, L1, got, q_host, decode_bytes, args, oracle, mx):
+    """Oracle check of a several-queries run on a sample of sequences (all
+    queries and heads), also timed as the CPU leg."""
+    import numpy as np
+
+    spec = w.spec
+    seqs = sample_seqs(spec)
+    Q = q_host.shape[1]
+    if mx:
+        pools = oracle_mx_pools(w, seqs, oracle)
+        caches, mxs = (pools[0], pools[1]), (pools[2], pools[3])
+    else:
+        hk, hv = w.k_cache.copy(), w.v_cache.copy()
+        oracle.append(hk, hv, w.k_new, w.v_new, w.slot_mapping)
+        caches, mxs = (hk, hv), None
+    pairs = [(b, i) for b in seqs for i in range(Q)]
+    t_c = time.perf_counter()
+    ref = oracle.decode_multi(q_host, caches[0], caches[1], w.block_tables, L1, w.scale,
+                              mxfp8=mxs, pairs=pairs)
+    cpu_s = time.perf_counter() - t_c
+    sel = np.array(pairs)
+    d = np.abs(got[sel[:, 0], sel[:, 1]] - ref[sel[:, 0], sel[:, 1]])
+    frac = float(L1[seqs].sum()) / float(L1.sum())
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = {"value": round(decode_bytes * frac / cpu_s / 1e9, 3), "unit": "GB/s",
+               "cores": oracle.default_threads(), "kind": "oracle",
+               "sample": f"oracle decode of {len(seqs)} of the {spec.num_seqs} sequences x {Q} "
+                         f"queries x all heads ({frac:.1%} of the attended tokens), fp64, "
+                         f"{cpu_s:.2f} s wall; GB/s over that sample's share of the bytes",
+               "tokens_per_s": round(len(seqs) * Q / cpu_s, 3)}
+        log(f"[bench] oracle (sample, q_len {Q}): {cpu_s:.2f}s")
+    return d, cpu
+
+
+def mx_oracle_check(w, L1, got, decode_bytes, args, oracle):
+    """Oracle check of an MXFP8 run on a sample of sequences: the oracle
+    quantizes those sequences' rows (and the appended token) into its own
+    pools and decodes them; that decode is also the timed CPU leg."""
+    import numpy as np
+
+    spec = w.spec
+    seqs = sample_seqs(spec)
+    pools = oracle_mx_pools(w, seqs, oracle)
     pairs = [(b, h) for b in seqs for h in range(spec.num_q_heads)]
     threads = oracle.default_threads()
     t_c = time.perf_counter()
@@ -163,6 +217,8 @@ def main() -> int:
     ap.add_argument("--config", default="c3", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--kv-format", default="native", choices=["native", "mxfp8"],
                     help="cache format: the workload's dtype, or MXFP8 (bf16 d=128 shapes)")
+    ap.add_argument("--q-len", type=int, default=1,
+                    help="query tokens per sequence (pa_decode_multi when > 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter scaling)")
@@ -200,23 +256,34 @@ def main() -> int:
     if mx and (spec.dtype != "bf16" or spec.mla or spec.head_dim_k != 128):
         log(f"--kv-format mxfp8 runs the bf16 head-dim-128 workloads, not {args.config}")
         return 2
-    q = to_dev(w.q)
+    Q = args.q_len
+    if Q > 1 and (spec.dtype != "bf16" or spec.mla or spec.head_dim_k != 128):
+        log(f"--q-len > 1 runs the bf16 head-dim-128 workloads, not {args.config}")
+        return 2
+    q_host = w.q if Q == 1 else workloads.multi_query(w, Q)
+    q = to_dev(q_host)
     k_new, v_new = to_dev(w.k_new), to_dev(w.v_new)
     bt = torch.from_numpy(w.block_tables).to(dev)
     L1 = (w.context_lens + 1).astype(np.int32)  # context after the append
     cl = torch.from_numpy(L1).to(dev)
     sm = torch.from_numpy(w.slot_mapping).to(dev)
-    out = torch.empty((spec.num_seqs, spec.num_q_heads, spec.head_dim_v), dtype=q.dtype,
-                      device=dev)
+    out = torch.empty(q.shape[:-1] + (spec.head_dim_v,), dtype=q.dtype, device=dev)
     if not mx:
         kc, vc = to_dev(w.k_cache), to_dev(w.v_cache)
-        ws = pa.alloc_workspace(q, kc, bt, head_dim_v=spec.head_dim_v)
 
         def append():
             pa.cache_append(kc, vc, k_new, v_new, sm)
 
-        def decode():
-            pa.decode(out, q, kc, vc, bt, cl, w.scale, ws)
+        if Q == 1:
+            ws = pa.alloc_workspace(q, kc, bt, head_dim_v=spec.head_dim_v)
+
+            def decode():
+                pa.decode(out, q, kc, vc, bt, cl, w.scale, ws)
+        else:
+            ws = pa.alloc_multi_workspace(q, spec.num_kv_heads, spec.block_size, bt)
+
+            def decode():
+                pa.decode_multi(out, q, kc, vc, bt, cl, w.scale, ws)
     else:
         # MXFP8 pools (unused slots hold the E4M3 NaN code), filled with every
         # cached row of the workload by the library's quantizing append
@@ -228,13 +295,20 @@ def main() -> int:
             pa.cache_append_mxfp8(*pools, to_dev(np.ascontiguousarray(w.k_cache[sl // bs, sl % bs])),
                                   to_dev(np.ascontiguousarray(w.v_cache[sl // bs, sl % bs])),
                                   torch.from_numpy(sl).to(dev))
-        ws = pa.alloc_mxfp8_workspace(q, pools[0], bt)
-
         def append():
             pa.cache_append_mxfp8(*pools, k_new, v_new, sm)
 
-        def decode():
-            pa.decode_mxfp8(out, q, *pools, bt, cl, w.scale, ws)
+        if Q == 1:
+            ws = pa.alloc_mxfp8_workspace(q, pools[0], bt)
+
+            def decode():
+                pa.decode_mxfp8(out, q, *pools, bt, cl, w.scale, ws)
+        else:
+            ws = pa.alloc_multi_workspace(q, spec.num_kv_heads, spec.block_size, bt)
+
+            def decode():
+                pa.decode_multi(out, q, pools[0], pools[1], bt, cl, w.scale, ws,
+                                k_scale=pools[2], v_scale=pools[3])
     torch.cuda.synchronize()
 
     def step():
@@ -271,8 +345,15 @@ def main() -> int:
     # accounting over the context actually attended (ctx + 1)
     w_after = workloads.Workload(**{**w.__dict__, "context_lens": L1})
     decode_bytes = (workloads.algorithmic_bytes_mxfp8 if mx else workloads.algorithmic_bytes)(w_after)
+    # q and O scale with the queries per sequence; the cache is read once
+    qo_bytes = spec.num_seqs * spec.num_q_heads * (spec.head_dim_k + spec.head_dim_v) * spec.elt
+    decode_bytes += (Q - 1) * qo_bytes
     append_bytes = (workloads.append_bytes_mxfp8 if mx else workloads.append_bytes)(w)
-    flops = workloads.algorithmic_flops(w_after)
+    if Q == 1:
+        flops = workloads.algorithmic_flops(w_after)
+    else:  # each query over the tokens it sees
+        seen = int(np.clip(L1[:, None] - Q + 1 + np.arange(Q)[None, :], 0, None).sum())
+        flops = 2 * spec.num_q_heads * (spec.head_dim_k + spec.head_dim_v) * seen
     step_bytes = decode_bytes + append_bytes
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     dec_ms = float(np.mean(t_decode))
@@ -295,13 +376,15 @@ def main() -> int:
     import oracle
 
     got = out.float().cpu().numpy().astype(np.float64)
-    if mx:
+    if Q > 1:
+        d, cpu = multi_oracle_check(w, L1, got, q_host, decode_bytes, args, oracle, mx)
+    elif mx:
         d, cpu = mx_oracle_check(w, L1, got, decode_bytes, args, oracle)
     else:
         d, cpu = native_oracle_check(w, L1, got, decode_bytes, args, oracle)
     max_err = float(d.max())
 
-    traffic = load_traffic(args.config + ("_mxfp8" if mx else ""), decode_bytes)
+    traffic = load_traffic(args.config + ("_mxfp8" if mx else ""), decode_bytes) if Q == 1 else None
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -316,12 +399,15 @@ def main() -> int:
         "dtype": spec.dtype,
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.config] + (
-                       ", KV cache in MXFP8 (E4M3 + E8M0 per 32 values)" if mx else ""),
-                   "name": spec.name + ("-mxfp8" if mx else ""), "kv_format": args.kv_format,
+                       ", KV cache in MXFP8 (E4M3 + E8M0 per 32 values)" if mx else "") + (
+                       f", {Q} causal query tokens per sequence" if Q > 1 else ""),
+                   "name": spec.name + ("-mxfp8" if mx else "") + (f"-q{Q}" if Q > 1 else ""),
+                   "kv_format": args.kv_format,
                    "global_batch": spec.num_seqs, "seq_len": int(L1.max()),
                    "mean_context": float(L1.mean()), "parallelism": "single GPU"},
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
-        "decode_tokens_per_s": round(spec.num_seqs / (ms_per_step * 1e-3), 1),
+        "decode_tokens_per_s": round(spec.num_seqs * Q / (ms_per_step * 1e-3), 1),
+        "q_len": Q,
         "us_append": round(float(np.mean(t_append)) * 1e3, 2),
         "us_decode": round(dec_ms * 1e3, 2),
         "us_decode_p10_p90": [round(float(np.percentile(t_decode, 10)) * 1e3, 2),

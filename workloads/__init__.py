@@ -337,3 +337,12 @@ def append_bytes_mxfp8(w: Workload) -> int:
     n = int((w.slot_mapping >= 0).sum())
     src = 2 * s.num_kv_heads * s.head_dim_k * s.elt
     return n * (src + mxfp8_kv_bytes_per_token_layer(s.num_kv_heads, s.head_dim_k)) + 4 * s.num_seqs
+
+
+def multi_query(w: Workload, q_len: int) -> np.ndarray:
+    """Seeded queries for q_len new tokens per sequence, [B, q_len, Hq, d_k] in
+    the workload's dtype, drawn from their own branch of the workload's seed
+    (independent of every other array)."""
+    s = w.spec
+    ss = np.random.SeedSequence([w.seed, 1000 + q_len])
+    return _values(ss, (s.num_seqs, q_len, s.num_q_heads, s.head_dim_k), s.dtype)
