@@ -269,6 +269,84 @@ pa_status pa_decode_multi(void *out, const void *q, const void *k_cache,
                           int32_t max_blocks_per_seq, pa_dtype dtype,
                           void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Host block manager: the caller side that turns token ids into block tables
+ * and slot mappings.  It follows the block manager of "Implémentation du
+ * cache" in the nano-vLLM article (a pool allocated once, a chained hash per
+ * full block built from the previous block's hash and the block's own token
+ * ids so that shared prefixes map to the same physical blocks, and reference
+ * counts that keep shared blocks alive) and PagedAttention's prefix sharing
+ * and copy-on-write in the CS336 lecture 10 notes ("核心概念与定义").
+ * Host memory only, no GPU calls; not thread-safe.  Sequence ids are the
+ * caller's.  Status codes: PA_ERR_NULL (NULL handle or array), PA_ERR_SHAPE
+ * (unknown or duplicate sequence id, table too small), PA_ERR_WORKSPACE (no
+ * free block; nothing changes).
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+/* A manager of num_blocks blocks of block_size token slots, all free; NULL
+ * for non-positive sizes or when memory runs out. */
+pa_block_manager *pa_bm_create(int32_t num_blocks, int32_t block_size);
+void pa_bm_destroy(pa_block_manager *m);
+int32_t pa_bm_num_free(const pa_block_manager *m);
+/* Sequences holding the block (-1 for an id outside the pool). */
+int32_t pa_bm_ref_count(const pa_block_manager *m, int32_t block);
+
+/*
+ * pa_bm_add_sequence — admit a sequence whose first num_tokens tokens are
+ * tokens[].  Each full block of tokens whose chained hash and token ids match
+ * a block already held (for the same preceding blocks) reuses that block;
+ * the first miss and everything after it take fresh blocks, as does a partly
+ * filled last block.  *num_cached (may be NULL) receives the number of
+ * leading tokens whose K/V are already in shared blocks: the caller appends
+ * K/V only for tokens from there on, at slot block_table[t / block_size] *
+ * block_size + t % block_size.
+ */
+pa_status pa_bm_add_sequence(pa_block_manager *m, int64_t seq_id, const int32_t *tokens,
+                             int32_t num_tokens, int32_t *num_cached);
+
+/*
+ * pa_bm_append_token — one more token for the sequence; *slot receives the
+ * cache slot its K/V go to.  A full last block gets a fresh block after it;
+ * a partly filled last block shared with another sequence (after a fork) is
+ * first replaced by a fresh block, and the (shared, fresh) pair is queued
+ * for pa_copy_blocks, which must run before the token's K/V are written.
+ * A block that fills up becomes shareable under its chained hash.
+ */
+pa_status pa_bm_append_token(pa_block_manager *m, int64_t seq_id, int32_t token,
+                             int32_t *slot);
+
+/* pa_bm_fork — child starts as a copy of parent, sharing all its blocks. */
+pa_status pa_bm_fork(pa_block_manager *m, int64_t parent, int64_t child);
+
+/* pa_bm_free_sequence — release the sequence's blocks (a block returns to
+ * the free list when no sequence holds it). */
+pa_status pa_bm_free_sequence(pa_block_manager *m, int64_t seq_id);
+
+/* Tokens of the sequence so far (-1 for an unknown id). */
+int64_t pa_bm_num_tokens(const pa_block_manager *m, int64_t seq_id);
+
+/* The sequence's block ids into out[0 .. max_blocks), padded with -1. */
+pa_status pa_bm_block_table(const pa_block_manager *m, int64_t seq_id, int32_t *out,
+                            int32_t max_blocks);
+
+/* Moves up to max_pairs queued copy-on-write pairs into src[], dst[] (host
+ * arrays); returns how many. */
+int32_t pa_bm_take_copies(pa_block_manager *m, int32_t *src, int32_t *dst,
+                          int32_t max_pairs);
+
+/*
+ * pa_copy_blocks — on the GPU, block dst[i] of pool becomes a copy of block
+ * src[i] (block i occupies bytes [i * block_bytes, (i + 1) * block_bytes)),
+ * for i < num_pairs.  Call it once per pool array: K and V, and k_scale and
+ * v_scale of an MXFP8 cache (their block sizes differ).  src and dst are
+ * int32 DEVICE arrays; no destination may also be a source.  pool and
+ * block_bytes must be multiples of 16 bytes (PA_ERR_ALIGN); at most 65535
+ * pairs per call (PA_ERR_UNSUPPORTED).
+ */
+pa_status pa_copy_blocks(void *pool, int64_t block_bytes, const int32_t *src,
+                         const int32_t *dst, int32_t num_pairs, void *stream);
+
 /* Static text for a status code ("PA_OK", ...); never NULL. */
 const char *pa_status_string(pa_status status);
 

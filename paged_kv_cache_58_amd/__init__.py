@@ -23,6 +23,9 @@ STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_DTYPE",
 
 EXPORTS = ("pa_cache_append", "pa_decode_workspace_size", "pa_decode", "pa_cache_append_mxfp8",
            "pa_decode_mxfp8", "pa_decode_multi_workspace_size", "pa_decode_multi",
+           "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free", "pa_bm_ref_count",
+           "pa_bm_add_sequence", "pa_bm_append_token", "pa_bm_fork", "pa_bm_free_sequence",
+           "pa_bm_num_tokens", "pa_bm_block_table", "pa_bm_take_copies", "pa_copy_blocks",
            "pa_status_string", "pa_last_error")
 
 _lib = None
@@ -62,6 +65,30 @@ def lib():
         L.pa_decode_multi.restype = ctypes.c_int
         L.pa_decode_multi.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_float, I32, I32, I32, I32,
                                       I32, I32, I32, I32, ctypes.c_int, P, ctypes.c_size_t, P]
+        L.pa_bm_create.restype = P
+        L.pa_bm_create.argtypes = [I32, I32]
+        L.pa_bm_destroy.restype = None
+        L.pa_bm_destroy.argtypes = [P]
+        L.pa_bm_num_free.restype = I32
+        L.pa_bm_num_free.argtypes = [P]
+        L.pa_bm_ref_count.restype = I32
+        L.pa_bm_ref_count.argtypes = [P, I32]
+        L.pa_bm_add_sequence.restype = ctypes.c_int
+        L.pa_bm_add_sequence.argtypes = [P, I64, P, I32, P]
+        L.pa_bm_append_token.restype = ctypes.c_int
+        L.pa_bm_append_token.argtypes = [P, I64, I32, P]
+        L.pa_bm_fork.restype = ctypes.c_int
+        L.pa_bm_fork.argtypes = [P, I64, I64]
+        L.pa_bm_free_sequence.restype = ctypes.c_int
+        L.pa_bm_free_sequence.argtypes = [P, I64]
+        L.pa_bm_num_tokens.restype = I64
+        L.pa_bm_num_tokens.argtypes = [P, I64]
+        L.pa_bm_block_table.restype = ctypes.c_int
+        L.pa_bm_block_table.argtypes = [P, I64, P, I32]
+        L.pa_bm_take_copies.restype = I32
+        L.pa_bm_take_copies.argtypes = [P, P, P, I32]
+        L.pa_copy_blocks.restype = ctypes.c_int
+        L.pa_copy_blocks.argtypes = [P, I64, P, P, I32, P]
         L.pa_status_string.restype = ctypes.c_char_p
         L.pa_status_string.argtypes = [ctypes.c_int]
         L.pa_last_error.restype = ctypes.c_char_p
@@ -263,3 +290,87 @@ def decode_multi(out, q, k_cache, v_cache, block_tables, context_lens, scale, wo
         _ptr(block_tables), _ptr(context_lens), float(scale), B, Q, hq, hkv, d, bs, nb,
         block_tables.shape[1], _dtype_code(q), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Host block manager (prefix sharing by chained block hashes, reference
+# counts, copy-on-write) and the block-copy kernel
+# ---------------------------------------------------------------------------
+
+class BlockManager:
+    """ctypes wrapper of the pa_bm_* calls (host memory only)."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        self._h = lib().pa_bm_create(num_blocks, block_size)
+        if not self._h:
+            raise ValueError("pa_bm_create failed (sizes must be positive)")
+        self.num_blocks, self.block_size = num_blocks, block_size
+
+    def close(self) -> None:
+        if self._h:
+            lib().pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # interpreter teardown
+            pass
+
+    @property
+    def num_free(self) -> int:
+        return int(lib().pa_bm_num_free(self._h))
+
+    def ref_count(self, block: int) -> int:
+        return int(lib().pa_bm_ref_count(self._h, block))
+
+    def add_sequence(self, seq_id: int, tokens) -> int:
+        """Admit a sequence; returns how many leading tokens are already cached."""
+        import numpy as np
+
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        cached = ctypes.c_int32(0)
+        _check(lib().pa_bm_add_sequence(self._h, seq_id, t.ctypes.data_as(ctypes.c_void_p),
+                                        t.size, ctypes.byref(cached)))
+        return int(cached.value)
+
+    def append_token(self, seq_id: int, token: int) -> int:
+        """One more token; returns its cache slot."""
+        slot = ctypes.c_int32(0)
+        _check(lib().pa_bm_append_token(self._h, seq_id, token, ctypes.byref(slot)))
+        return int(slot.value)
+
+    def fork(self, parent: int, child: int) -> None:
+        _check(lib().pa_bm_fork(self._h, parent, child))
+
+    def free(self, seq_id: int) -> None:
+        _check(lib().pa_bm_free_sequence(self._h, seq_id))
+
+    def num_tokens(self, seq_id: int) -> int:
+        return int(lib().pa_bm_num_tokens(self._h, seq_id))
+
+    def block_table(self, seq_id: int, max_blocks: int):
+        import numpy as np
+
+        out = np.empty(max_blocks, dtype=np.int32)
+        _check(lib().pa_bm_block_table(self._h, seq_id, out.ctypes.data_as(ctypes.c_void_p),
+                                       max_blocks))
+        return out
+
+    def take_copies(self, max_pairs: int = 4096):
+        import numpy as np
+
+        src = np.empty(max_pairs, dtype=np.int32)
+        dst = np.empty(max_pairs, dtype=np.int32)
+        n = lib().pa_bm_take_copies(self._h, src.ctypes.data_as(ctypes.c_void_p),
+                                    dst.ctypes.data_as(ctypes.c_void_p), max_pairs)
+        return src[:n].copy(), dst[:n].copy()
+
+
+def copy_blocks(pool, src, dst, stream=None) -> None:
+    """Block dst[i] of pool (first axis = blocks) becomes a copy of block
+    src[i]; src and dst int32 device tensors."""
+    n = int(src.numel())
+    block_bytes = pool[0].numel() * pool.element_size() if pool.shape[0] else 0
+    _check(lib().pa_copy_blocks(_ptr(pool), block_bytes, _ptr(src), _ptr(dst), n,
+                                _stream(stream)))

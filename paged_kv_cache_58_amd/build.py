@@ -18,8 +18,9 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 ARCH = "gfx950"
 
-SOURCES = ["plan.cpp", "api.cpp", "append.hip", "grouped_decode.hip", "gqa_mfma_decode.hip",
-           "latent_decode.hip", "mxfp8_append.hip"]
+SOURCES = ["plan.cpp", "block_manager.cpp", "api.cpp", "append.hip", "grouped_decode.hip",
+           "gqa_mfma_decode.hip", "latent_decode.hip", "mxfp8_append.hip", "block_copy.hip"]
+HOST_ONLY = {"plan.cpp", "block_manager.cpp"}  # pure C++: no HIP headers
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 
@@ -36,7 +37,7 @@ EXTRA = {"gqa_mfma_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 def _compile(src: str) -> str:
     path = os.path.join(CSRC, src)
     obj = os.path.join(BUILD, src.rsplit(".", 1)[0] + ".o")
-    if src == "plan.cpp":  # pure C++: no HIP headers, built by the host compiler
+    if src in HOST_ONLY:  # built by the host compiler
         cmd = ["g++", *COMMON, "-c", path, "-o", obj]
     else:
         cmd = [HIPCC, *DEVICE, *COMMON, *EXTRA.get(src, []), "-x", "hip", "-c", path, "-o", obj]

@@ -179,6 +179,22 @@ PA_EXPORT pa_status pa_decode_multi(void *out, const void *q, const void *k_cach
     return finish(st, why);
 }
 
+PA_EXPORT pa_status pa_copy_blocks(void *pool, int64_t block_bytes, const int32_t *src,
+                                   const int32_t *dst, int32_t num_pairs, void *stream) {
+    if (num_pairs < 0 || block_bytes <= 0)
+        return finish(PA_ERR_SHAPE, "copy_blocks: num_pairs < 0 or block_bytes <= 0");
+    if (num_pairs == 0) return finish(PA_OK, "");
+    if (!pool || !src || !dst) return finish(PA_ERR_NULL, "copy_blocks: pool, src and dst must be non-NULL");
+    if (num_pairs > 65535) return finish(PA_ERR_UNSUPPORTED, "copy_blocks: at most 65535 pairs per call");
+    if (block_bytes % 16 != 0 || reinterpret_cast<uintptr_t>(pool) % 16 != 0 ||
+        reinterpret_cast<uintptr_t>(src) % 4 != 0 || reinterpret_cast<uintptr_t>(dst) % 4 != 0)
+        return finish(PA_ERR_ALIGN, "copy_blocks: pool and block_bytes must be multiples of 16 bytes");
+    std::string why;
+    const pa_status st = pa::launch_copy_blocks(pool, block_bytes, src, dst, num_pairs,
+                                                static_cast<hipStream_t>(stream), &why);
+    return finish(st, why);
+}
+
 PA_EXPORT const char *pa_status_string(pa_status status) {
     switch (status) {
         case PA_OK: return "PA_OK";

@@ -30,6 +30,11 @@ pa_status launch_append_mxfp8(const MxAppendArgs &a, hipStream_t stream, std::st
 pa_status launch_mxfp8_decode(const DecodeShape &s, const DecodeArgs &a,
                               const DecodePlan &plan, hipStream_t stream, std::string *why);
 
+// Copies num_pairs whole blocks of block_bytes inside pool (src[i] -> dst[i]).
+pa_status launch_copy_blocks(void *pool, int64_t block_bytes, const int32_t *src,
+                             const int32_t *dst, int32_t num_pairs, hipStream_t stream,
+                             std::string *why);
+
 // Latent (576/512) decode on MFMA, followed by the same stream-K reduce.
 pa_status launch_latent_decode(const DecodeShape &s, const DecodeArgs &a,
                                const DecodePlan &plan, hipStream_t stream, std::string *why);
