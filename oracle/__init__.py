@@ -289,3 +289,78 @@ def decode_multi(q: np.ndarray, k_cache, v_cache, block_tables, context_lens, sc
             out[b, i] = decode_mxfp8(q1, k_cache, v_cache, mxfp8[0], mxfp8[1], bt[b:b + 1], cl,
                                      scale, threads=threads)[0]
     return out
+
+
+# ---------------------------------------------------------------------------
+# Sliding window, log-sum-exp, per-token attention mass (numpy, float64)
+# ---------------------------------------------------------------------------
+
+def _widen64(a: np.ndarray) -> np.ndarray:
+    """float32 or bf16 bit patterns (uint16) widened exactly to float64."""
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def window_start(L: int, window: int) -> int:
+    """First token a query of a length-L sequence attends with a sliding
+    window of ``window`` tokens (0: no window)."""
+    return L - window if (window > 0 and L > window) else 0
+
+
+def _gather(pool, bt_row, start, L, bs):
+    t = np.arange(start, L)
+    return _widen64(pool[bt_row[t // bs], t % bs])  # [n, Hkv, d]
+
+
+def decode_window(q, k_cache, v_cache, block_tables, context_lens, scale, window=0):
+    """Plain softmax attention of each query over its sequence's tokens
+    [max(0, L - window), L) in float64.  Returns (O [B, Hq, dv], lse [B, Hq])
+    with lse = log(sum_t exp(s_t)), s_t = scale * q . k_t; a sequence with
+    no token gives O = 0 and lse = -inf."""
+    B, Hq, _ = q.shape
+    bs, Hkv = k_cache.shape[1], k_cache.shape[2]
+    G = Hq // Hkv
+    dv = v_cache.shape[3]
+    O = np.zeros((B, Hq, dv))
+    lse = np.full((B, Hq), -np.inf)
+    qq = _widen64(q)
+    for b in range(B):
+        L = int(context_lens[b])
+        st = window_start(L, window)
+        if L <= st:
+            continue
+        K = _gather(k_cache, block_tables[b], st, L, bs)
+        V = _gather(v_cache, block_tables[b], st, L, bs)
+        for h in range(Hq):
+            g = h // G
+            s = scale * (K[:, g] @ qq[b, h])
+            m = s.max()
+            w = np.exp(s - m)
+            O[b, h] = (w @ V[:, g]) / w.sum()
+            lse[b, h] = m + np.log(w.sum())
+    return O, lse
+
+
+def attention_scores(q, k_cache, block_tables, context_lens, lse, scale, window=0,
+                     max_context=None):
+    """[B, Hkv, max_context] float64: for each token t of the window, the sum
+    over the query heads h of KV head g of exp(scale q_h . k_t - lse[b, h]);
+    0 elsewhere."""
+    B, Hq, _ = q.shape
+    bs, Hkv = k_cache.shape[1], k_cache.shape[2]
+    G = Hq // Hkv
+    if max_context is None:
+        max_context = int(np.max(context_lens)) if B else 0
+    out = np.zeros((B, Hkv, max_context))
+    qq = _widen64(q)
+    for b in range(B):
+        L = int(context_lens[b])
+        st = window_start(L, window)
+        if L <= st:
+            continue
+        K = _gather(k_cache, block_tables[b], st, L, bs)
+        for g in range(Hkv):
+            for h in range(g * G, (g + 1) * G):
+                out[b, g, st:L] += np.exp(scale * (K[:, g] @ qq[b, h]) - lse[b, h])
+    return out
