@@ -270,6 +270,56 @@ pa_status pa_decode_multi(void *out, const void *q, const void *k_cache,
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Sliding window and exported log-sum-exp, for per-layer KV sparsity.  The
+ * KV-sparsity article ("Comment KV Sparsity permet une accélération de 1,5x
+ * pour vLLM") lets each layer run a full cache or a sliding window
+ * ("Sparsité par couche et parallélisme de tenseurs"; local attention over a
+ * window is in the CS336 lecture 10 notes, "核心概念与定义"), has the
+ * attention kernel export its row max and sum, and recomputes each cached
+ * token's softmax probability from them to score the tokens a layer keeps
+ * ("Modification de l'Attention").
+ *
+ * pa_decode_ex — pa_decode with two options:
+ *   window  > 0: the query of a sequence of length L attends only to tokens
+ *           [max(0, L - window), L); 0 attends to all of them.
+ *   lse     optional fp32 [num_seqs, num_q_heads] output (NULL skips it):
+ *           log(sum_t exp(s_t)) over the attended tokens, s_t = scale *
+ *           q . k_t, natural log; -inf for an empty context.  It is
+ *           accumulated from the same bf16-rounded weights as the output.
+ * bf16 or fp32 caches [num_blocks, block_size, num_kv_heads, head_dim] (no
+ * latent mode); shapes and workspace as for pa_decode.
+ */
+pa_status pa_decode_ex(void *out, float *lse, const void *q, const void *k_cache,
+                       const void *v_cache, const int32_t *block_tables,
+                       const int32_t *context_lens, float scale, int32_t window,
+                       int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                       int32_t max_blocks_per_seq, pa_dtype dtype, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/*
+ * pa_attention_scores — the attention mass each cached token gets from the
+ * query heads sharing its KV head:
+ *   scores[b, g, t] = sum over h with h / G == g of exp(scale * q[b, h] .
+ *                     k_t - lse[b, h])
+ * for t in the window [max(0, L - window), L) (window 0: all of [0, L)), and
+ * 0 for every other t < max_context.  With the lse of pa_decode_ex each
+ * head's values sum to 1 over the window, so a row sums to G.
+ *   scores   fp32 [num_seqs, num_kv_heads, max_context], written whole.
+ *   q, k_cache, block_tables, context_lens as for pa_decode (dtype PA_F32 or
+ *   PA_BF16); lse fp32 [num_seqs, num_q_heads].
+ * Runs head_dim 64 or 128, block_size 16, num_q_heads / num_kv_heads <= 16;
+ * every context must be <= max_context <= max_blocks_per_seq * block_size.
+ */
+pa_status pa_attention_scores(float *scores, const void *q, const void *k_cache,
+                              const int32_t *block_tables, const int32_t *context_lens,
+                              const float *lse, float scale, int32_t window,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size,
+                              int32_t max_blocks_per_seq, int32_t max_context,
+                              pa_dtype dtype, void *stream);
+
+/*
  * Host block manager: the caller side that turns token ids into block tables
  * and slot mappings.  It follows the block manager of "Implémentation du
  * cache" in the nano-vLLM article (a pool allocated once, a chained hash per

@@ -26,6 +26,7 @@ EXPORTS = ("pa_cache_append", "pa_decode_workspace_size", "pa_decode", "pa_cache
            "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free", "pa_bm_ref_count",
            "pa_bm_add_sequence", "pa_bm_append_token", "pa_bm_fork", "pa_bm_free_sequence",
            "pa_bm_num_tokens", "pa_bm_block_table", "pa_bm_take_copies", "pa_copy_blocks",
+           "pa_decode_ex", "pa_attention_scores",
            "pa_status_string", "pa_last_error")
 
 _lib = None
@@ -87,6 +88,12 @@ def lib():
         L.pa_bm_block_table.argtypes = [P, I64, P, I32]
         L.pa_bm_take_copies.restype = I32
         L.pa_bm_take_copies.argtypes = [P, P, P, I32]
+        L.pa_decode_ex.restype = ctypes.c_int
+        L.pa_decode_ex.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, I32, I32, I32, I32, I32,
+                                   I32, I32, I32, ctypes.c_int, P, ctypes.c_size_t, P]
+        L.pa_attention_scores.restype = ctypes.c_int
+        L.pa_attention_scores.argtypes = [P, P, P, P, P, P, ctypes.c_float, I32, I32, I32, I32,
+                                          I32, I32, I32, I32, ctypes.c_int, P]
         L.pa_copy_blocks.restype = ctypes.c_int
         L.pa_copy_blocks.argtypes = [P, I64, P, P, I32, P]
         L.pa_status_string.restype = ctypes.c_char_p
@@ -374,3 +381,37 @@ def copy_blocks(pool, src, dst, stream=None) -> None:
     block_bytes = pool[0].numel() * pool.element_size() if pool.shape[0] else 0
     _check(lib().pa_copy_blocks(_ptr(pool), block_bytes, _ptr(src), _ptr(dst), n,
                                 _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Sliding window, exported log-sum-exp, per-token attention mass
+# ---------------------------------------------------------------------------
+
+def decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, scale, workspace, window=0,
+              lse=None, stream=None) -> None:
+    """decode() attending only to the last ``window`` tokens of each sequence
+    (0: all), optionally writing the log-sum-exp of the scores into ``lse``
+    (fp32 [B, Hq])."""
+    B, hq, d = q.shape
+    nb, bs, hkv, _ = k_cache.shape
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("out", out),
+                    ("block_tables", block_tables), ("context_lens", context_lens)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    _check(lib().pa_decode_ex(
+        _ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        _ptr(context_lens), float(scale), int(window), B, hq, hkv, d, bs, nb,
+        block_tables.shape[1], _dtype_code(q), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def attention_scores(scores, q, k_cache, block_tables, context_lens, lse, scale, window=0,
+                     stream=None) -> None:
+    """scores fp32 [B, Hkv, max_context]: each token's attention mass from the
+    query heads of its KV head, exp(scale q.k - lse) summed over the group."""
+    B, hq, d = q.shape
+    nb, bs, hkv, _ = k_cache.shape
+    _check(lib().pa_attention_scores(
+        _ptr(scores), _ptr(q), _ptr(k_cache), _ptr(block_tables), _ptr(context_lens), _ptr(lse),
+        float(scale), int(window), B, hq, hkv, d, bs, block_tables.shape[1], scores.shape[2],
+        _dtype_code(q), _stream(stream)))

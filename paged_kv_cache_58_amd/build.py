@@ -19,7 +19,8 @@ LIB = os.path.join(PKG, "libpa.so")
 ARCH = "gfx950"
 
 SOURCES = ["plan.cpp", "block_manager.cpp", "api.cpp", "append.hip", "grouped_decode.hip",
-           "gqa_mfma_decode.hip", "latent_decode.hip", "mxfp8_append.hip", "block_copy.hip"]
+           "gqa_mfma_decode.hip", "latent_decode.hip", "mxfp8_append.hip", "block_copy.hip",
+           "attention_scores.hip"]
 HOST_ONLY = {"plan.cpp", "block_manager.cpp"}  # pure C++: no HIP headers
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

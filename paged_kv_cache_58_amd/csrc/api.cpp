@@ -179,6 +179,69 @@ PA_EXPORT pa_status pa_decode_multi(void *out, const void *q, const void *k_cach
     return finish(st, why);
 }
 
+PA_EXPORT pa_status pa_decode_ex(void *out, float *lse, const void *q, const void *k_cache,
+                                 const void *v_cache, const int32_t *block_tables,
+                                 const int32_t *context_lens, float scale, int32_t window,
+                                 int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                 int32_t max_blocks_per_seq, pa_dtype dtype, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+    pa::DecodeShape s = make_shape(false, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                   head_dim, block_size, max_blocks_per_seq, dtype);
+    s.window = window;
+    std::string why;
+    if (!v_cache && num_seqs > 0)
+        return finish(PA_ERR_NULL, "decode_ex: v_cache must be non-NULL (no latent mode)");
+    pa::DecodePlan plan{};
+    pa_status st = pa::plan_decode(s, &plan, &why);
+    if (st != PA_OK) return finish(st, why);
+    if (lse && reinterpret_cast<uintptr_t>(lse) % 4 != 0)
+        return finish(PA_ERR_ALIGN, "decode_ex: lse must be 4-byte aligned");
+    pa::DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens, nullptr, nullptr,
+                     scale, num_blocks, workspace, workspace_bytes};
+    a.lse = lse;
+    st = pa::check_decode(s, a, plan, &why);
+    if (st != PA_OK || num_seqs == 0) return finish(st, why);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    st = plan.path == pa::DecodePath::kGroupedMfma ? pa::launch_gqa_mfma_decode(s, a, plan, hs, &why)
+                                                   : pa::launch_grouped_decode(s, a, plan, hs, &why);
+    return finish(st, why);
+}
+
+PA_EXPORT pa_status pa_attention_scores(float *scores, const void *q, const void *k_cache,
+                                        const int32_t *block_tables, const int32_t *context_lens,
+                                        const float *lse, float scale, int32_t window,
+                                        int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t block_size, int32_t max_blocks_per_seq,
+                                        int32_t max_context, pa_dtype dtype, void *stream) {
+    if (dtype != PA_F32 && dtype != PA_BF16) return finish(PA_ERR_DTYPE, "scores: unknown dtype");
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || max_blocks_per_seq <= 0 || max_context < 0 || window < 0 ||
+        num_q_heads % num_kv_heads != 0)
+        return finish(PA_ERR_SHAPE, "scores: sizes must be positive, num_q_heads a multiple of "
+                                    "num_kv_heads");
+    if ((head_dim != 64 && head_dim != 128) || block_size != 16 || num_q_heads / num_kv_heads > 16 ||
+        num_kv_heads > 65535 || num_seqs > 65535)
+        return finish(PA_ERR_UNSUPPORTED, "scores: runs head_dim 64 or 128, block_size 16, "
+                                          "num_q_heads / num_kv_heads <= 16");
+    if ((int64_t)max_context > (int64_t)max_blocks_per_seq * block_size)
+        return finish(PA_ERR_SHAPE, "scores: max_context exceeds the block table's capacity");
+    if (num_seqs == 0 || max_context == 0) return finish(PA_OK, "");
+    if (!scores || !q || !k_cache || !block_tables || !context_lens || !lse)
+        return finish(PA_ERR_NULL, "scores: scores, q, k_cache, block_tables, context_lens and "
+                                   "lse must be non-NULL");
+    if (reinterpret_cast<uintptr_t>(q) % 16 != 0 || reinterpret_cast<uintptr_t>(k_cache) % 16 != 0 ||
+        reinterpret_cast<uintptr_t>(scores) % 4 != 0 || reinterpret_cast<uintptr_t>(lse) % 4 != 0)
+        return finish(PA_ERR_ALIGN, "scores: q and k_cache must be 16-byte aligned");
+    std::string why;
+    const pa_status st = pa::launch_attention_scores(
+        scores, q, k_cache, block_tables, context_lens, lse, scale, window, num_seqs, num_q_heads,
+        num_kv_heads, head_dim, max_blocks_per_seq, max_context, dtype,
+        static_cast<hipStream_t>(stream), &why);
+    return finish(st, why);
+}
+
 PA_EXPORT pa_status pa_copy_blocks(void *pool, int64_t block_bytes, const int32_t *src,
                                    const int32_t *dst, int32_t num_pairs, void *stream) {
     if (num_pairs < 0 || block_bytes <= 0)

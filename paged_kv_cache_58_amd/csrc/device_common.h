@@ -130,23 +130,38 @@ __host__ __device__ __forceinline__ int stream_share(int total, int waves) {
     return r > kMinShare ? r : kMinShare;
 }
 
+// Sliding window (per-layer local attention): with window w > 0 the query of
+// a sequence of length L attends to tokens [max(0, L - w), L).  The first of
+// them lies in block window_first_block(); the blocks a sequence contributes
+// to the work are those from there to its last block.
+__host__ __device__ __forceinline__ int window_start(int L, int window) {
+    return (window > 0 && L > window) ? L - window : 0;
+}
+__host__ __device__ __forceinline__ int window_first_block(int L, int window, int bs) {
+    return window_start(L, window) / bs;
+}
+__host__ __device__ __forceinline__ int window_blocks(int L, int window, int bs) {
+    return (L + bs - 1) / bs - window_first_block(L, window, bs);
+}
+
 // Where stream share `sid` of `nshares` lies in the global (sequence, KV
-// head, block) order of a batch of bs-token blocks: blocks [x0, x1), the
-// first of them block `blk` of segment (b, g), sequence b having nbb
-// blocks.  Share 0 also stores the per-sequence block prefix sums
-// (num_seqs + 1 entries) that the reduce reads.  Uniform over the wave;
-// returns false for a share past the end of the work.
+// head, block) order of a batch of bs-token blocks (the blocks of each
+// sequence's window): blocks [x0, x1), the first of them block `blk` of
+// the window of segment (b, g), sequence b having nbb such blocks.  Share 0
+// also stores the per-sequence block prefix sums (num_seqs + 1 entries) that
+// the reduce reads.  Uniform over the wave; returns false for a share past
+// the end of the work.
 struct ShareSpan {
     int x0, x1, b, nbb, g, blk;
 };
 __device__ __forceinline__ bool find_share(int sid, int nshares, int num_seqs, int num_kv_heads,
                                            int bs, const int32_t *__restrict__ context_lens,
                                            int32_t *__restrict__ ws_prefix, int lane,
-                                           ShareSpan &sp) {
+                                           ShareSpan &sp, int window = 0) {
     int seq_blocks_total = 0;
     for (int base = 0; base < num_seqs; base += kWave) {
         const int bb = base + lane;
-        const int nb = bb < num_seqs ? (context_lens[bb] + bs - 1) / bs : 0;
+        const int nb = bb < num_seqs ? window_blocks(context_lens[bb], window, bs) : 0;
         const int incl = wave_incl_scan(nb, lane);
         if (sid == 0 && bb < num_seqs) ws_prefix[bb] = seq_blocks_total + incl - nb;
         seq_blocks_total += __builtin_amdgcn_readlane(incl, kWave - 1);
@@ -165,7 +180,7 @@ __device__ __forceinline__ bool find_share(int sid, int nshares, int num_seqs, i
     int cb = 0;
     for (int base = 0, carry = 0;; base += kWave) {
         const int bb = base + lane;
-        const int nb = bb < num_seqs ? (context_lens[bb] + bs - 1) / bs : 0;
+        const int nb = bb < num_seqs ? window_blocks(context_lens[bb], window, bs) : 0;
         const int incl = wave_incl_scan(nb, lane);
         const bool past = bb < num_seqs &&
                           static_cast<int64_t>(num_kv_heads) * (carry + incl) > sp.x0;
@@ -198,7 +213,8 @@ template <typename T, int D, int W>
 __global__ __launch_bounds__(kWave *W) void stream_reduce_kernel(
     T *__restrict__ out, const float *__restrict__ ws_acc, const float2 *__restrict__ ws_ml,
     const int32_t *__restrict__ ws_prefix, const int32_t *__restrict__ context_lens,
-    int num_seqs, int num_kv_heads, int group, int block_size, int waves, int q_len) {
+    int num_seqs, int num_kv_heads, int group, int block_size, int waves, int q_len,
+    int window, float *__restrict__ lse) {
     constexpr int DPL = D / kWave;
     const int num_q_heads = num_kv_heads * group;
     const int qi = blockIdx.x / num_q_heads;
@@ -210,17 +226,19 @@ __global__ __launch_bounds__(kWave *W) void stream_reduce_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    const int nb = (context_lens[b] + block_size - 1) / block_size;
+    const int nb = window_blocks(context_lens[b], window, block_size);
     T *o = out + ((static_cast<int64_t>(b) * q_len + qi) * num_q_heads + h) * D + lane * DPL;
+    float *lse_row = lse ? lse + (static_cast<int64_t>(b) * q_len + qi) * num_q_heads + h : nullptr;
 
     __shared__ float s_max[W];
     __shared__ float s_num[W][D];
     __shared__ float s_den[W];
 
-    if (nb <= 0) {  // empty context: O = 0
+    if (nb <= 0) {  // empty context: O = 0, log-sum-exp -inf
         if (wave == 0)
 #pragma unroll
             for (int d = 0; d < DPL; ++d) o[d] = static_cast<T>(0.f);
+        if (lse_row && tid == 0) *lse_row = kNegInf;
         return;
     }
     const int total = num_kv_heads * ws_prefix[num_seqs];
@@ -250,6 +268,7 @@ __global__ __launch_bounds__(kWave *W) void stream_reduce_kernel(
         if (wave == 0)
 #pragma unroll
             for (int d = 0; d < DPL; ++d) o[d] = static_cast<T>(0.f);
+        if (lse_row && tid == 0) *lse_row = kNegInf;
         return;
     }
     for (int p = wave; p < n; p += W) {
@@ -282,6 +301,8 @@ __global__ __launch_bounds__(kWave *W) void stream_reduce_kernel(
             for (int d = 0; d < DPL; ++d) num[d] += s_num[w][lane * DPL + d];
         }
     }
+    // log-sum-exp of the scores in natural units: M and den are in log2 units
+    if (lse_row && lane == 0) *lse_row = (M + log2f(den)) * 0.69314718055994531f;
     if constexpr (sizeof(T) == 2) {
         if constexpr (DPL % 2 == 0) {
 #pragma unroll
@@ -304,16 +325,17 @@ template <typename T, int D>
 hipError_t enqueue_stream_reduce(T *out, const float *ws_acc, const float2 *ws_ml,
                                  const int32_t *ws_prefix, const int32_t *context_lens,
                                  int num_seqs, int num_q_heads, int num_kv_heads, int group,
-                                 int block_size, int waves, hipStream_t stream, int q_len = 1) {
+                                 int block_size, int waves, hipStream_t stream, int q_len = 1,
+                                 int window = 0, float *lse = nullptr) {
     const dim3 grid(num_q_heads * q_len, num_seqs);
     if (static_cast<int64_t>(num_seqs) * num_q_heads * q_len < 2048)
         hipLaunchKernelGGL((stream_reduce_kernel<T, D, 4>), grid, dim3(kWave * 4), 0, stream, out,
                            ws_acc, ws_ml, ws_prefix, context_lens, num_seqs, num_kv_heads, group,
-                           block_size, waves, q_len);
+                           block_size, waves, q_len, window, lse);
     else
         hipLaunchKernelGGL((stream_reduce_kernel<T, D, 1>), grid, dim3(kWave), 0, stream, out,
                            ws_acc, ws_ml, ws_prefix, context_lens, num_seqs, num_kv_heads, group,
-                           block_size, waves, q_len);
+                           block_size, waves, q_len, window, lse);
     return hipGetLastError();
 }
 

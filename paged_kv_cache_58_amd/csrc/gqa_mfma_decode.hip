@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
     const void *__restrict__ v_cache, const uint8_t *__restrict__ k_scale,
     const uint8_t *__restrict__ v_scale, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, float scale_log2, int num_seqs, int num_kv_heads,
-    int group, int q_len, int max_blocks, int nshares) {
+    int group, int q_len, int max_blocks, int nshares, int window) {
     using TL = MTile<MX>;
     static_assert((NBUF & (NBUF - 1)) == 0 && NBUF >= 2 && NBUF <= 4, "ring depth 2 or 4");
     const int lane = threadIdx.x & (kWave - 1);
@@ -183,7 +183,8 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
     const uint32_t ids_lds[2] = {lds_offset(&s_ids[0][0]), lds_offset(&s_ids[1][0])};
 
     ShareSpan sp;
-    if (!find_share(sid, nshares, num_seqs, num_kv_heads, kMBS, context_lens, ws_prefix, lane, sp))
+    if (!find_share(sid, nshares, num_seqs, num_kv_heads, kMBS, context_lens, ws_prefix, lane, sp,
+                    window))
         return;
     const int x1 = sp.x1;
     int b = sp.b, nbb = sp.nbb, g = sp.g, blk_start = sp.blk;
@@ -221,9 +222,12 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
         const int nblk = min(nbb - blk_start, x1 - x);
         const int ctx = context_lens[b];
         const int32_t *bt_row = block_tables + static_cast<int64_t>(b) * max_blocks;
+        // the window's first token and block (0 and 0 without a window)
+        const int wstart = window_start(ctx, window);
+        const int wblk = blk_start + wstart / kMBS;  // table index of this segment's first block
 
         auto fetch_ids = [&](int m) {
-            const int e = min(blk_start + kWave * m + lane, max_blocks - 1);
+            const int e = min(wblk + kWave * m + lane, max_blocks - 1);
             dma4(bt_row, static_cast<uint32_t>(e) * 4u, ids_lds[m & 1]);
         };
         fetch_ids(0);
@@ -248,7 +252,7 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
             }
             lim[ct] = live[ct] ? ctx - q_len + 1 + qi[ct] : ctx;
         }
-        // blocks ending at or before this token are visible to every column
+        // blocks from the window's start to this token are visible to every column
         const int all_visible = ctx - q_len + 1;
         // This lane's DMA sources inside one block's tile.
         uint32_t dma_off[TL::kDma];
@@ -314,7 +318,7 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
 
         auto compute_block = [&](int n) {
             const uint32_t kslot = ring_lds + (n & (NBUF - 1)) * TL::kSlotB;
-            const int tok0 = (blk_start + n) * kMBS;
+            const int tok0 = (wblk + n) * kMBS;
             const int valid = ctx - tok0;  // tokens of this block in context
 
             // ---- scores S^T[token 4 quad + i, column 16 ct + col] ----
@@ -366,7 +370,8 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
             }
 
             // ---- online softmax per column; probabilities rounded to bf16 ----
-            const bool full = tok0 + kMBS <= all_visible;  // no column masks a token of this block
+            // no column masks a token of this block
+            const bool full = tok0 + kMBS <= all_visible && tok0 >= wstart;
             float p[NT][4];
             uint32_t p01[NT], p23[NT];
 #pragma unroll
@@ -378,7 +383,9 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        x[i] = (tok0 + 4 * quad + i < lim[ct]) ? s[ct][i] * scale_log2 : kNegInf;
+                        x[i] = (tok0 + 4 * quad + i < lim[ct] && tok0 + 4 * quad + i >= wstart)
+                                   ? s[ct][i] * scale_log2
+                                   : kNegInf;
                 }
                 float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
                 bm = fmaxf(bm, __shfl_xor(bm, 16));
@@ -480,7 +487,7 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
             g = 0;
             do {
                 ++b;
-                nbb = (context_lens[b] + kMBS - 1) / kMBS;
+                nbb = window_blocks(context_lens[b], window, kMBS);
             } while (nbb == 0);
         }
         wait_lds();  // every LDS read of this segment is done before the next one's DMA
@@ -502,13 +509,13 @@ pa_status enqueue_gqa_mfma(const DecodeShape &s, const DecodeArgs &a, const Deco
                        static_cast<const uint8_t *>(a.k_scale),
                        static_cast<const uint8_t *>(a.v_scale), a.block_tables, a.context_lens,
                        scale_log2, s.num_seqs, s.num_kv_heads, p.group, s.q_len,
-                       s.max_blocks_per_seq, waves);
+                       s.max_blocks_per_seq, waves, s.window);
     pa_status st = hip_status(hipGetLastError(), why, "partition launch");
     if (st != PA_OK) return st;
     return hip_status(enqueue_stream_reduce<uint16_t, kMD>(
                           static_cast<uint16_t *>(a.out), acc, ml, prefix, a.context_lens,
                           s.num_seqs, s.num_q_heads, s.num_kv_heads, p.group, kMBS, waves, stream,
-                          s.q_len),
+                          s.q_len, s.window, a.lse),
                       why, "reduce launch");
 }
 

@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
     float *__restrict__ ws_acc, float2 *__restrict__ ws_ml, int32_t *__restrict__ ws_prefix,
     const T *__restrict__ q, const T *__restrict__ k_cache, const T *__restrict__ v_cache,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
-    float scale_log2, int num_seqs, int num_kv_heads, int max_blocks, int nshares) {
+    float scale_log2, int num_seqs, int num_kv_heads, int max_blocks, int nshares, int window) {
     using C = Cfg<T, D, G>;
     constexpr int CPL = C::kCPL;
     constexpr int DPL = C::kDPL;
@@ -201,7 +201,8 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
 
     // ---- this wave's share of the global block order -------------------------
     ShareSpan sp;
-    if (!find_share(sid, nshares, num_seqs, num_kv_heads, kBS, context_lens, ws_prefix, lane, sp))
+    if (!find_share(sid, nshares, num_seqs, num_kv_heads, kBS, context_lens, ws_prefix, lane, sp,
+                    window))
         return;
     const int x1 = sp.x1;
     int b = sp.b, nbb = sp.nbb, g = sp.g, blk_start = sp.blk;
@@ -224,11 +225,14 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
         // ======== segment (b, g): blocks [blk_start, blk_start + nblk) ========
         const int nblk = min(nbb - blk_start, x1 - x);
         const int ctx = context_lens[b];
+        // the window's first token and block (0 and 0 without a window)
+        const int wstart = window_start(ctx, window);
+        const int wblk = blk_start + wstart / kBS;  // table index of this segment's first block
         const int32_t *bt_row = block_tables + static_cast<int64_t>(b) * max_blocks;
 
-        // block ids, 64 per LDS buffer; chunk m holds entries blk_start + 64 m + lane
+        // block ids, 64 per LDS buffer; chunk m holds entries wblk + 64 m + lane
         auto fetch_ids = [&](int m) {
-            const int e = min(blk_start + kWave * m + lane, max_blocks - 1);
+            const int e = min(wblk + kWave * m + lane, max_blocks - 1);
             dma4(bt_row, static_cast<uint32_t>(e) * 4u, ids_lds[m & 1]);
         };
         fetch_ids(0);
@@ -297,11 +301,15 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
 
         auto compute_block = [&](int n) {
             const uint4 *slot = s_ring + (n & (NBUF - 1)) * SLOT_U4;
-            const int tok0 = (blk_start + n) * kBS;
-            const bool partial = tok0 + kBS > ctx;  // only the sequence's last block
+            const int tok0 = (wblk + n) * kBS;
+            // only the sequence's last block, and the window's first, hold tokens
+            // outside [wstart, ctx); V rows below wstart are real data and get
+            // weight 0, rows at or past ctx are zeroed below
+            const bool partial = tok0 + kBS > ctx || tok0 < wstart;
             bool valid[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) valid[j] = !partial || (tok0 + 2 * tp + j < ctx);
+            for (int j = 0; j < 2; ++j)
+                valid[j] = !partial || (tok0 + 2 * tp + j < ctx && tok0 + 2 * tp + j >= wstart);
 
             // ---- scores for the G heads of both tokens ---------------------
             uint4 kr[2][CPL];
@@ -458,7 +466,7 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
             g = 0;
             do {
                 ++b;
-                nbb = (context_lens[b] + kBS - 1) / kBS;
+                nbb = window_blocks(context_lens[b], window, kBS);
             } while (nbb == 0);
         }
         wait_lds();  // every LDS read of this segment is done before the next one's DMA
@@ -479,12 +487,14 @@ pa_status enqueue_grouped(const DecodeShape &s, const DecodeArgs &a, const Decod
     hipLaunchKernelGGL(kernel, dim3(groups), dim3(kWave * kGroupWaves), 0, stream, acc, ml, prefix,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k_cache),
                        static_cast<const T *>(a.v_cache), a.block_tables, a.context_lens,
-                       scale_log2, s.num_seqs, s.num_kv_heads, s.max_blocks_per_seq, waves);
+                       scale_log2, s.num_seqs, s.num_kv_heads, s.max_blocks_per_seq, waves,
+                       s.window);
     pa_status st = hip_status(hipGetLastError(), why, "partition launch");
     if (st != PA_OK) return st;
     return hip_status(enqueue_stream_reduce<T, D>(static_cast<T *>(a.out), acc, ml, prefix,
                                                   a.context_lens, s.num_seqs, s.num_q_heads,
-                                                  s.num_kv_heads, G, kBS, waves, stream),
+                                                  s.num_kv_heads, G, kBS, waves, stream, 1,
+                                                  s.window, a.lse),
                       why, "reduce launch");
 }
 

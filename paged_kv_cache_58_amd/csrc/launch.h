@@ -35,6 +35,15 @@ pa_status launch_copy_blocks(void *pool, int64_t block_bytes, const int32_t *src
                              const int32_t *dst, int32_t num_pairs, hipStream_t stream,
                              std::string *why);
 
+// Per-token attention mass of each KV head's group: scores[b, g, t] =
+// sum over the group's query heads h of exp(scale q_h . k_t - lse[b, h]).
+pa_status launch_attention_scores(float *scores, const void *q, const void *k_cache,
+                                  const int32_t *block_tables, const int32_t *context_lens,
+                                  const float *lse, float scale, int32_t window, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_blocks_per_seq, int32_t max_context, pa_dtype dtype,
+                                  hipStream_t stream, std::string *why);
+
 // Latent (576/512) decode on MFMA, followed by the same stream-K reduce.
 pa_status launch_latent_decode(const DecodeShape &s, const DecodeArgs &a,
                                const DecodePlan &plan, hipStream_t stream, std::string *why);

@@ -131,6 +131,11 @@ pa_status plan_decode(const DecodeShape &s, DecodePlan *plan, std::string *why) 
     DecodePlan p{};
     p.group = G;
     if (s.q_len < 1) return fail(PA_ERR_SHAPE, why, "decode: q_len must be >= 1");
+    if (s.window < 0) return fail(PA_ERR_SHAPE, why, "decode: window must be >= 0");
+    if (s.window > 0 && (s.latent || s.q_len > 1 || s.mxfp8))
+        return fail(PA_ERR_UNSUPPORTED, why,
+                    "decode: a sliding window runs single-query grouped decode on bf16 or fp32 "
+                    "caches");
     if (s.q_len > 1 && (s.latent || (!s.mxfp8 && s.dtype != PA_BF16) || s.head_dim_k != 128 ||
                         s.head_dim_v != 128 || s.block_size != 16 ||
                         (int64_t)G * s.q_len > 16 * kMaxColTiles))

@@ -97,6 +97,7 @@ struct DecodeShape {
     bool mxfp8;   // MXFP8 caches (dtype is then that of q and out)
     pa_dtype dtype;
     int32_t q_len = 1;  // new query tokens per sequence, causal among themselves
+    int32_t window = 0; // > 0: attend only to the last `window` tokens (sliding window)
 };
 
 // Most (query, head) columns one KV head's work may carry on the matrix-core
@@ -142,6 +143,7 @@ struct DecodeArgs {
     int32_t num_blocks;
     void *workspace;
     size_t workspace_bytes;
+    float *lse = nullptr;  // optional [num_seqs, q_len, num_q_heads] log-sum-exp output
 };
 
 // Pointer, alignment, scale and workspace checks against a plan.

@@ -1,0 +1,91 @@
+"""GPU parity of pa_decode_ex (sliding window, exported log-sum-exp) and
+pa_attention_scores against the oracle (runs on an MI355X through the C ABI)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_58_amd as pa
+from tests.gpu_util import compare, say, to_device
+from workloads import custom_spec, make_workload
+
+pytestmark = pytest.mark.gpu
+
+LSE_TOL = {"f32": 1e-4, "bf16": 1e-2}  # bf16: accumulated from bf16-rounded weights
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(autouse=True, params=["valu", "mfma"])
+def grouped_path(request, monkeypatch):
+    monkeypatch.setenv("PA_GQA_MFMA", "1" if request.param == "mfma" else "0")
+    return request.param
+
+
+CASES = [
+    # dtype, head dim, q heads, kv heads, window, contexts
+    ("bf16", 128, 64, 8, 0, [1, 17, 300, 1025]),
+    ("bf16", 128, 64, 8, 256, [1, 17, 300, 1025, 4000]),
+    ("bf16", 128, 32, 32, 33, [5, 33, 34, 700]),
+    ("bf16", 128, 16, 2, 1, [1, 2, 100]),
+    ("f32", 64, 8, 2, 100, [50, 101, 513]),
+    ("bf16", 128, 8, 4, 4096, [0, 10, 5000]),
+]
+
+
+@pytest.mark.parametrize("dtype,D,hq,hkv,window,ctx", CASES)
+def test_decode_ex_window_and_lse(dev, dtype, D, hq, hkv, window, ctx):
+    say(f"case: decode_ex {dtype} d={D} hq={hq} hkv={hkv} window={window} ctx={ctx}")
+    w = make_workload(custom_spec(len(ctx), hq, hkv, D, 16, dtype, ctx=ctx))
+    d = to_device(w, dev)
+    out = torch.empty_like(d.q)
+    lse = torch.empty((len(ctx), hq), dtype=torch.float32, device=dev)
+    pa.decode_ex(out, d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, w.scale,
+                 d.workspace, window=window, lse=lse)
+    ref_o, ref_lse = oracle.decode_window(w.q, w.k_cache, w.v_cache, w.block_tables,
+                                          w.context_lens, w.scale, window=window)
+    compare(out, ref_o, dtype)
+    got = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(got), fin)
+    err = np.abs(got[fin] - ref_lse[fin]).max() if fin.any() else 0.0
+    say(f"  lse max |delta| {err:.2e}")
+    assert err <= LSE_TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,D,hq,hkv,window,ctx", [CASES[1], CASES[3], CASES[4]])
+def test_attention_scores(dev, dtype, D, hq, hkv, window, ctx):
+    say(f"case: attention scores {dtype} hq={hq} hkv={hkv} window={window} ctx={ctx}")
+    w = make_workload(custom_spec(len(ctx), hq, hkv, D, 16, dtype, ctx=ctx))
+    d = to_device(w, dev)
+    _, ref_lse = oracle.decode_window(w.q, w.k_cache, w.v_cache, w.block_tables,
+                                      w.context_lens, w.scale, window=window)
+    maxc = int(w.block_tables.shape[1] * 16)
+    scores = torch.full((len(ctx), hkv, maxc), 7.0, dtype=torch.float32, device=dev)
+    lse_d = torch.from_numpy(ref_lse.astype(np.float32)).to(dev)
+    pa.attention_scores(scores, d.q, d.k_cache, d.block_tables, d.context_lens, lse_d, w.scale,
+                        window=window)
+    ref = oracle.attention_scores(w.q, w.k_cache, w.block_tables, w.context_lens,
+                                  ref_lse.astype(np.float32).astype(np.float64), w.scale,
+                                  window=window, max_context=maxc)
+    got = scores.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    err = np.abs(got - ref).max()
+    say(f"  scores max |delta| {err:.2e}")
+    assert np.allclose(got, ref, rtol=1e-4, atol=1e-5)
+    # end to end: the GPU's own lse, each KV head's scores sum to G
+    lse = torch.empty((len(ctx), hq), dtype=torch.float32, device=dev)
+    out = torch.empty_like(d.q)
+    pa.decode_ex(out, d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, w.scale,
+                 d.workspace, window=window, lse=lse)
+    pa.attention_scores(scores, d.q, d.k_cache, d.block_tables, d.context_lens, lse, w.scale,
+                        window=window)
+    sums = scores.sum(dim=2).cpu().numpy()
+    G = hq // hkv
+    assert np.allclose(sums, G, rtol=2e-2)
