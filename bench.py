@@ -143,6 +143,34 @@ def multi_oracle_check(w, L1, got, q_host, decode_bytes, args, oracle, mx):
     return d, cpu
 
 
+def window_oracle_check(w, L1, got, window, decode_bytes, args, oracle):
+    """Oracle check of a sliding-window run on a sample of sequences (all
+    heads), also timed as the CPU leg."""
+    import numpy as np
+
+    spec = w.spec
+    seqs = sample_seqs(spec)
+    hk, hv = w.k_cache.copy(), w.v_cache.copy()
+    oracle.append(hk, hv, w.k_new, w.v_new, w.slot_mapping)
+    t_c = time.perf_counter()
+    ref, _ = oracle.decode_window(w.q[seqs], hk, hv, w.block_tables[seqs], L1[seqs], w.scale,
+                                  window=window)
+    cpu_s = time.perf_counter() - t_c
+    d = np.abs(got[seqs] - ref)
+    att = np.minimum(L1, window)
+    frac = float(att[seqs].sum()) / float(att.sum())
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = {"value": round(decode_bytes * frac / cpu_s / 1e9, 3), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"numpy oracle windowed decode of {len(seqs)} of the {spec.num_seqs} "
+                         f"sequences ({frac:.1%} of the attended tokens), fp64, {cpu_s:.2f} s "
+                         f"wall; GB/s over that sample's share of the bytes",
+               "tokens_per_s": round(len(seqs) / cpu_s, 3)}
+        log(f"[bench] oracle (window sample): {cpu_s:.2f}s")
+    return d, cpu
+
+
 def mx_oracle_check(w, L1, got, decode_bytes, args, oracle):
     """Oracle check of an MXFP8 run on a sample of sequences: the oracle
     quantizes those sequences' rows (and the appended token) into its own
@@ -219,6 +247,8 @@ def main() -> int:
                     help="cache format: the workload's dtype, or MXFP8 (bf16 d=128 shapes)")
     ap.add_argument("--q-len", type=int, default=1,
                     help="query tokens per sequence (pa_decode_multi when > 1)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window in tokens (pa_decode_ex; 0 = the whole context)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter scaling)")
@@ -260,6 +290,10 @@ def main() -> int:
     if Q > 1 and (spec.dtype != "bf16" or spec.mla or spec.head_dim_k != 128):
         log(f"--q-len > 1 runs the bf16 head-dim-128 workloads, not {args.config}")
         return 2
+    W = args.window
+    if W and (mx or Q > 1 or spec.mla):
+        log("--window runs the single-query grouped workloads on their own caches")
+        return 2
     q_host = w.q if Q == 1 else workloads.multi_query(w, Q)
     q = to_dev(q_host)
     k_new, v_new = to_dev(w.k_new), to_dev(w.v_new)
@@ -274,7 +308,12 @@ def main() -> int:
         def append():
             pa.cache_append(kc, vc, k_new, v_new, sm)
 
-        if Q == 1:
+        if Q == 1 and W:
+            ws = pa.alloc_workspace(q, kc, bt, head_dim_v=spec.head_dim_v)
+
+            def decode():
+                pa.decode_ex(out, q, kc, vc, bt, cl, w.scale, ws, window=W)
+        elif Q == 1:
             ws = pa.alloc_workspace(q, kc, bt, head_dim_v=spec.head_dim_v)
 
             def decode():
@@ -343,7 +382,9 @@ def main() -> int:
     ms_per_step = total_ms / K
 
     # accounting over the context actually attended (ctx + 1)
-    w_after = workloads.Workload(**{**w.__dict__, "context_lens": L1})
+    # accounting over the tokens attended (the window's, with --window)
+    L_att = np.minimum(L1, W) if W else L1
+    w_after = workloads.Workload(**{**w.__dict__, "context_lens": L_att.astype(np.int32)})
     decode_bytes = (workloads.algorithmic_bytes_mxfp8 if mx else workloads.algorithmic_bytes)(w_after)
     # q and O scale with the queries per sequence; the cache is read once
     qo_bytes = spec.num_seqs * spec.num_q_heads * (spec.head_dim_k + spec.head_dim_v) * spec.elt
@@ -376,7 +417,9 @@ def main() -> int:
     import oracle
 
     got = out.float().cpu().numpy().astype(np.float64)
-    if Q > 1:
+    if W:
+        d, cpu = window_oracle_check(w, L1, got, W, decode_bytes, args, oracle)
+    elif Q > 1:
         d, cpu = multi_oracle_check(w, L1, got, q_host, decode_bytes, args, oracle, mx)
     elif mx:
         d, cpu = mx_oracle_check(w, L1, got, decode_bytes, args, oracle)
@@ -384,7 +427,8 @@ def main() -> int:
         d, cpu = native_oracle_check(w, L1, got, decode_bytes, args, oracle)
     max_err = float(d.max())
 
-    traffic = load_traffic(args.config + ("_mxfp8" if mx else ""), decode_bytes) if Q == 1 else None
+    traffic = (load_traffic(args.config + ("_mxfp8" if mx else ""), decode_bytes)
+               if Q == 1 and not W else None)
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -400,8 +444,10 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.config] + (
                        ", KV cache in MXFP8 (E4M3 + E8M0 per 32 values)" if mx else "") + (
-                       f", {Q} causal query tokens per sequence" if Q > 1 else ""),
-                   "name": spec.name + ("-mxfp8" if mx else "") + (f"-q{Q}" if Q > 1 else ""),
+                       f", {Q} causal query tokens per sequence" if Q > 1 else "") + (
+                       f", sliding window of {W} tokens" if W else ""),
+                   "name": spec.name + ("-mxfp8" if mx else "") + (f"-q{Q}" if Q > 1 else "") +
+                           (f"-w{W}" if W else ""),
                    "kv_format": args.kv_format,
                    "global_batch": spec.num_seqs, "seq_len": int(L1.max()),
                    "mean_context": float(L1.mean()), "parallelism": "single GPU"},

@@ -226,3 +226,54 @@ def test_decode_multi_workspace_size():
     assert pa.decode_multi_workspace_size(100, 1, 64, 8, 128, 16, 513) == one
     assert pa.decode_multi_workspace_size(100, 9, 64, 8, 128, 16, 513) == 0
     assert _decode_multi(B=0, out=None, q=None, ws=None, wsb=0) == 0
+
+
+def _decode_ex(**kw):
+    a = dict(out=FAKE, lse=None, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, scale=0.125, window=64,
+             B=4, hq=64, hkv=8, d=128, bs=16, nb=100, mb=16, dtype=pa.PA_BF16, ws=FAKE,
+             wsb=1 << 30)
+    a.update(kw)
+    return pa.lib().pa_decode_ex(a["out"], a["lse"], a["q"], a["k"], a["v"], a["bt"], a["cl"],
+                                 a["scale"], a["window"], a["B"], a["hq"], a["hkv"], a["d"],
+                                 a["bs"], a["nb"], a["mb"], a["dtype"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(window=-1), 2),
+    (dict(v=None), 1),
+    (dict(q=None), 1),
+    (dict(lse=FAKE + 2), 7),
+    (dict(d=96), 4),
+    (dict(wsb=1024), 5),
+])
+def test_decode_ex_rejects(kw, status):
+    assert _decode_ex(**kw) == status
+
+
+def _scores(**kw):
+    a = dict(sc=FAKE, q=FAKE, k=FAKE, bt=FAKE, cl=FAKE, lse=FAKE, scale=0.1, window=0, B=4,
+             hq=64, hkv=8, d=128, bs=16, mb=16, maxc=256, dtype=pa.PA_BF16)
+    a.update(kw)
+    return pa.lib().pa_attention_scores(a["sc"], a["q"], a["k"], a["bt"], a["cl"], a["lse"],
+                                        a["scale"], a["window"], a["B"], a["hq"], a["hkv"], a["d"],
+                                        a["bs"], a["mb"], a["maxc"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lse=None), 1),
+    (dict(sc=None), 1),
+    (dict(dtype=5), 3),
+    (dict(maxc=257), 2),          # beyond max_blocks * block_size
+    (dict(hq=60), 2),
+    (dict(d=96), 4),
+    (dict(bs=32, maxc=256), 4),
+    (dict(hq=136, hkv=8), 4),     # group of 17
+    (dict(q=FAKE + 8), 7),
+])
+def test_attention_scores_rejects(kw, status):
+    assert _scores(**kw) == status
+
+
+def test_attention_scores_noop_cases():
+    assert _scores(B=0, sc=None, q=None) == 0
+    assert _scores(maxc=0, sc=None) == 0
