@@ -66,7 +66,7 @@ constexpr int kMD = 128;              // head dim (K and V)
 constexpr int kMKSteps = kMD / 32;    // score k-steps
 constexpr int kMDimTiles = kMD / 16;  // 16-dim tiles of the output
 constexpr float kMSlack = 8.0f;       // lazy-rescale threshold, log2 units
-constexpr float kMFloor = -3.0e38f;   // finite stand-in for a running max of -inf
+constexpr float kMFloor = -3.0e38f;   // running max before any visible token (finite)
 constexpr int kMGroupWaves = 4;
 
 // Per-format tile geometry of one (block, KV head).
@@ -276,12 +276,17 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
         }
         drain_vmem();  // q and the first ids have landed; the ring's accounting starts empty
 
-        float m_run[NT];  // running max of the lane's column (scaled, log2 units)
+        // running max of the lane's column (scaled, log2 units).  It starts at a
+        // finite floor, not -inf: with several queries (or a window) a block can
+        // be masked for some columns only, and the rescale branch below is taken
+        // by the whole wave, so a column that has seen no visible token yet must
+        // get alpha = 1 and weights 0 there, never exp2(-inf + inf).
+        float m_run[NT];
         float l_run[NT];  // this lane's share of the column's running sum
         f32x4_t acc[NT][kMDimTiles];
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
-            m_run[ct] = kNegInf;
+            m_run[ct] = kMFloor;
             l_run[ct] = 0.f;
 #pragma unroll
             for (int t = 0; t < kMDimTiles; ++t) acc[ct][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -390,23 +395,17 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
                 float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
                 bm = fmaxf(bm, __shfl_xor(bm, 16));
                 bm = fmaxf(bm, __shfl_xor(bm, 32));
-                // A column that has seen no visible token yet keeps m_run = -inf
-                // (with several queries a block can be masked for some columns
-                // only).  The branch below is taken by the whole wave, so both
-                // maxima are clamped to a finite floor: such a column then gets
-                // alpha = 1 and weights 0, never exp2(-inf + inf).
                 if (__builtin_amdgcn_ballot_w64(bm > m_run[ct] + kMSlack) != 0) {
                     const float m_new = fmaxf(m_run[ct], bm);
                     const float alpha =
-                        exp2_fast(fmaxf(m_run[ct], kMFloor) - fmaxf(m_new, kMFloor));
+                        exp2_fast(m_run[ct] - m_new);
                     l_run[ct] *= alpha;
                     m_run[ct] = m_new;
 #pragma unroll
                     for (int t = 0; t < kMDimTiles; ++t) acc[ct][t] *= alpha;
                 }
-                const float m_e = fmaxf(m_run[ct], kMFloor);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) p[ct][i] = exp2_fast(x[i] - m_e);
+                for (int i = 0; i < 4; ++i) p[ct][i] = exp2_fast(x[i] - m_run[ct]);
                 p01[ct] = pack_bf16(p[ct][0], p[ct][1]);
                 p23[ct] = pack_bf16(p[ct][2], p[ct][3]);
                 l_run[ct] += (bf16_lo(p01[ct]) + bf16_hi(p01[ct])) + (bf16_lo(p23[ct]) + bf16_hi(p23[ct]));
@@ -472,7 +471,8 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
             l_tot += __shfl_xor(l_tot, 32);
             if (live[ct]) {
                 const int64_t row = slot_row + 16 * ct + col;
-                if (quad == 0) ws_ml[row] = make_float2(m_run[ct], l_tot);
+                // a column with no visible token in the segment reports max -inf
+                if (quad == 0) ws_ml[row] = make_float2(l_tot > 0.f ? m_run[ct] : kNegInf, l_tot);
                 float *dst = ws_acc + row * kMD + 4 * quad;
 #pragma unroll
                 for (int t = 0; t < kMDimTiles; ++t)
