@@ -121,13 +121,34 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
     return v;
 }
 
-// Blocks each work-group of the stream takes: an equal share of all
-// (sequence, KV head, block) work, and at least kMinShare so that tiny
-// batches do not split into fragments that cost more to merge than to run.
+// Blocks each stream share takes: an equal part of all (sequence, segment,
+// block) work, and at least kMinShare so that tiny batches do not split into
+// fragments that cost more to merge than to run.
 constexpr int kMinShare = 16;
 __host__ __device__ __forceinline__ int stream_share(int total, int waves) {
     const int r = (total + waves - 1) / waves;
     return r > kMinShare ? r : kMinShare;
+}
+
+// Waves per team of the grouped partition kernels: a team shares one stream
+// share, each of its waves streaming one KV head of the same blocks, so that
+// at any time neighbouring head slices of a block's token rows are read
+// together (longer runs of consecutive bytes per row than one wave's 256).
+// The largest power of two that divides both the KV head count and the waves
+// of a work-group (a team never spans two work-groups), for grouped heads
+// (group > 1); with one query head per KV head (MHA) shares of about a
+// segment's length already put neighbouring heads of a sequence on
+// neighbouring waves, and teams measured slower there, so each wave streams
+// its own share (1).  PA_TEAM_HEADS caps it.
+inline int team_heads(int num_kv_heads, int waves_per_group, int group) {
+    int cap = group > 1 ? waves_per_group : 1;
+    if (const char *env = std::getenv("PA_TEAM_HEADS")) {
+        const int v = std::atoi(env);
+        if (v >= 1 && v < cap) cap = v;
+    }
+    int t = 1;
+    while (2 * t <= cap && waves_per_group % (2 * t) == 0 && num_kv_heads % (2 * t) == 0) t *= 2;
+    return t;
 }
 
 // Sliding window (per-layer local attention): with window w > 0 the query of
@@ -144,30 +165,32 @@ __host__ __device__ __forceinline__ int window_blocks(int L, int window, int bs)
     return (L + bs - 1) / bs - window_first_block(L, window, bs);
 }
 
-// Where stream share `sid` of `nshares` lies in the global (sequence, KV
-// head, block) order of a batch of bs-token blocks (the blocks of each
-// sequence's window): blocks [x0, x1), the first of them block `blk` of
-// the window of segment (b, g), sequence b having nbb such blocks.  Share 0
-// also stores the per-sequence block prefix sums (num_seqs + 1 entries) that
-// the reduce reads.  Uniform over the wave; returns false for a share past
-// the end of the work.
+// Where stream share `sid` of `nshares` lies in the global (sequence,
+// segment, block) order of a batch of bs-token blocks (the blocks of each
+// sequence's window), each sequence holding `segs` segments: blocks [x0, x1),
+// the first of them block `blk` of the window of segment (b, g), sequence b
+// having nbb such blocks.  A segment is one KV head, or one chunk of KV heads
+// that a team of waves streams together (one head per wave).  Share 0 also
+// stores the per-sequence block prefix sums (num_seqs + 1 entries) that the
+// reduce reads, if `writer`.  Uniform over the wave; returns false for a
+// share past the end of the work.
 struct ShareSpan {
     int x0, x1, b, nbb, g, blk;
 };
-__device__ __forceinline__ bool find_share(int sid, int nshares, int num_seqs, int num_kv_heads,
-                                           int bs, const int32_t *__restrict__ context_lens,
+__device__ __forceinline__ bool find_share(int sid, int nshares, int num_seqs, int segs, int bs,
+                                           const int32_t *__restrict__ context_lens,
                                            int32_t *__restrict__ ws_prefix, int lane,
-                                           ShareSpan &sp, int window = 0) {
+                                           ShareSpan &sp, int window = 0, bool writer = true) {
     int seq_blocks_total = 0;
     for (int base = 0; base < num_seqs; base += kWave) {
         const int bb = base + lane;
         const int nb = bb < num_seqs ? window_blocks(context_lens[bb], window, bs) : 0;
         const int incl = wave_incl_scan(nb, lane);
-        if (sid == 0 && bb < num_seqs) ws_prefix[bb] = seq_blocks_total + incl - nb;
+        if (sid == 0 && writer && bb < num_seqs) ws_prefix[bb] = seq_blocks_total + incl - nb;
         seq_blocks_total += __builtin_amdgcn_readlane(incl, kWave - 1);
     }
-    if (sid == 0 && lane == 0) ws_prefix[num_seqs] = seq_blocks_total;
-    const int total = num_kv_heads * seq_blocks_total;
+    if (sid == 0 && writer && lane == 0) ws_prefix[num_seqs] = seq_blocks_total;
+    const int total = segs * seq_blocks_total;
     const int share = stream_share(total, nshares);
     const int64_t x0l = static_cast<int64_t>(sid) * share;
     if (x0l >= total) return false;
@@ -183,7 +206,7 @@ __device__ __forceinline__ bool find_share(int sid, int nshares, int num_seqs, i
         const int nb = bb < num_seqs ? window_blocks(context_lens[bb], window, bs) : 0;
         const int incl = wave_incl_scan(nb, lane);
         const bool past = bb < num_seqs &&
-                          static_cast<int64_t>(num_kv_heads) * (carry + incl) > sp.x0;
+                          static_cast<int64_t>(segs) * (carry + incl) > sp.x0;
         const uint64_t hit = __builtin_amdgcn_ballot_w64(past);
         if (hit != 0) {
             const int f = __builtin_ctzll(hit);
@@ -194,16 +217,19 @@ __device__ __forceinline__ bool find_share(int sid, int nshares, int num_seqs, i
         }
         carry += __builtin_amdgcn_readlane(incl, kWave - 1);
     }
-    sp.g = (sp.x0 - num_kv_heads * cb) / sp.nbb;
-    sp.blk = (sp.x0 - num_kv_heads * cb) - sp.g * sp.nbb;
+    sp.g = (sp.x0 - segs * cb) / sp.nbb;
+    sp.blk = (sp.x0 - segs * cb) - sp.g * sp.nbb;
     return true;
 }
 
 // ---------------------------------------------------------------------------
 // Reduce over the stream-K partial slots of each (sequence, query, query
-// head).  A segment (sequence, KV head g) has C = group * q_len columns, column
-// i * group + h % group for query i and head h; slot row (s * C + column)
-// holds that column's partial of the segment from stream share s:
+// head).  KV head g of sequence b has C = group * q_len columns, column
+// i * group + h % group for query i and head h.  The partition kernels'
+// stream shares run over (sequence, head chunk, block) with NC = Hkv /
+// team_heads chunks of team_heads heads per sequence (team_heads = 1: one
+// head per segment); share s leaves the partial of head g = ch * team_heads
+// + hw in slot s + b * NC + ch, row ((slot * team_heads + hw) * C + column):
 // O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s, M = max_s m_s
 // (O = 0 when no slot saw a token: an empty context).  One work-group of W
 // waves per (query, query head, sequence), blockIdx.x = i * Hq + h; wave w
@@ -213,8 +239,8 @@ template <typename T, int D, int W>
 __global__ __launch_bounds__(kWave *W) void stream_reduce_kernel(
     T *__restrict__ out, const float *__restrict__ ws_acc, const float2 *__restrict__ ws_ml,
     const int32_t *__restrict__ ws_prefix, const int32_t *__restrict__ context_lens,
-    int num_seqs, int num_kv_heads, int group, int block_size, int waves, int q_len,
-    int window, float *__restrict__ lse) {
+    int num_seqs, int num_kv_heads, int group, int block_size, int nshares, int team_heads,
+    int q_len, int window, float *__restrict__ lse) {
     constexpr int DPL = D / kWave;
     const int num_q_heads = num_kv_heads * group;
     const int qi = blockIdx.x / num_q_heads;
@@ -241,16 +267,21 @@ __global__ __launch_bounds__(kWave *W) void stream_reduce_kernel(
         if (lse_row && tid == 0) *lse_row = kNegInf;
         return;
     }
-    const int total = num_kv_heads * ws_prefix[num_seqs];
-    const int share = stream_share(total, waves);
-    const int k = b * num_kv_heads + g;
-    const int seg_lo = num_kv_heads * ws_prefix[b] + g * nb;
+    const int nchunks = num_kv_heads / team_heads;
+    const int ch = g / team_heads;
+    const int hw = g - ch * team_heads;
+    const int total = nchunks * ws_prefix[num_seqs];
+    const int share = stream_share(total, nshares);
+    const int seg_lo = nchunks * ws_prefix[b] + ch * nb;
     const int w0 = seg_lo / share;
     const int n = (seg_lo + nb - 1) / share - w0 + 1;  // partial slots of this segment
-    const int64_t first = (static_cast<int64_t>(w0) + k) * ncols + hh;  // row of slot w0 + k
+    // row of slot w0 + b * NC + ch; consecutive slots are team_heads * C rows apart
+    const int64_t first =
+        ((static_cast<int64_t>(w0) + b * nchunks + ch) * team_heads + hw) * ncols + hh;
+    const int64_t stride = static_cast<int64_t>(team_heads) * ncols;
 
     float M = kNegInf;
-    for (int p = tid; p < n; p += kWave * W) M = fmaxf(M, ws_ml[first + static_cast<int64_t>(p) * ncols].x);
+    for (int p = tid; p < n; p += kWave * W) M = fmaxf(M, ws_ml[first + p * stride].x);
     for (int sh = 32; sh >= 1; sh >>= 1) M = fmaxf(M, __shfl_xor(M, sh));
     if constexpr (W > 1) {
         if (lane == 0) s_max[wave] = M;
@@ -272,7 +303,7 @@ __global__ __launch_bounds__(kWave *W) void stream_reduce_kernel(
         return;
     }
     for (int p = wave; p < n; p += W) {
-        const int64_t r = first + static_cast<int64_t>(p) * ncols;
+        const int64_t r = first + p * stride;
         const float2 mp = ws_ml[r];
         const float wgt = exp2_fast(mp.x - M);
         den = fmaf(wgt, mp.y, den);
@@ -325,17 +356,17 @@ template <typename T, int D>
 hipError_t enqueue_stream_reduce(T *out, const float *ws_acc, const float2 *ws_ml,
                                  const int32_t *ws_prefix, const int32_t *context_lens,
                                  int num_seqs, int num_q_heads, int num_kv_heads, int group,
-                                 int block_size, int waves, hipStream_t stream, int q_len = 1,
-                                 int window = 0, float *lse = nullptr) {
+                                 int block_size, int nshares, int team_heads, hipStream_t stream,
+                                 int q_len = 1, int window = 0, float *lse = nullptr) {
     const dim3 grid(num_q_heads * q_len, num_seqs);
     if (static_cast<int64_t>(num_seqs) * num_q_heads * q_len < 2048)
         hipLaunchKernelGGL((stream_reduce_kernel<T, D, 4>), grid, dim3(kWave * 4), 0, stream, out,
                            ws_acc, ws_ml, ws_prefix, context_lens, num_seqs, num_kv_heads, group,
-                           block_size, waves, q_len, window, lse);
+                           block_size, nshares, team_heads, q_len, window, lse);
     else
         hipLaunchKernelGGL((stream_reduce_kernel<T, D, 1>), grid, dim3(kWave), 0, stream, out,
                            ws_acc, ws_ml, ws_prefix, context_lens, num_seqs, num_kv_heads, group,
-                           block_size, waves, q_len, window, lse);
+                           block_size, nshares, team_heads, q_len, window, lse);
     return hipGetLastError();
 }
 

@@ -17,7 +17,9 @@
 // The VALU then has only the softmax of 4 scores per lane to do, instead of
 // G dot products per token and the lane reductions behind them.
 //
-// gfx950 mapping, one wave64 per stream share (4 per work-group, one per SIMD):
+// gfx950 mapping, one wave64 per KV head of a stream share (4 per work-group,
+// one per SIMD; a team of up to 4 waves streams neighbouring heads of one
+// share):
 //  * K and V tiles of a block (16 rows of 256 bytes each) stream HBM -> LDS
 //    with global_load_lds_dwordx4 into a ring of NBUF slots, as in the VALU
 //    kernel.  Chunk c (16 bytes) of row t is stored at chunk c ^ t: the
@@ -136,10 +138,12 @@ __device__ __forceinline__ void wait_mblocks(int later) {
     wait_vmem<0>();
 }
 
-// Partition kernel: the stream-K schedule and partial-slot layout of the
-// VALU grouped kernel (slot row (share + b * Hkv + g) * C + column, fp32
-// accumulator of D dims plus (max, sum) in log2 units).  MX selects MXFP8
-// caches (k_scale, v_scale used); otherwise the caches are bf16.
+// Partition kernel: the stream-K schedule (teams of team_heads waves, one KV
+// head each, sharing a share of the (sequence, head chunk, block) order) and
+// partial-slot layout of the VALU grouped kernel (slot share + b * NC + ch,
+// row (slot * team_heads + hw) * C + column, fp32 accumulator of D dims plus
+// (max, sum) in log2 units).  MX selects MXFP8 caches (k_scale, v_scale
+// used); otherwise the caches are bf16.
 //
 // Columns: with q_len new query tokens per sequence (causal among
 // themselves, as in the masked attention of "Étape 2: Attention avec KV
@@ -154,13 +158,15 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
     const void *__restrict__ v_cache, const uint8_t *__restrict__ k_scale,
     const uint8_t *__restrict__ v_scale, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, float scale_log2, int num_seqs, int num_kv_heads,
-    int group, int q_len, int max_blocks, int nshares, int window) {
+    int group, int q_len, int max_blocks, int nshares, int team_heads, int window) {
     using TL = MTile<MX>;
     static_assert((NBUF & (NBUF - 1)) == 0 && NBUF >= 2 && NBUF <= 4, "ring depth 2 or 4");
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int sid = blockIdx.x * kMGroupWaves + wave;
-    if (sid >= nshares) return;  // uniform over the wave; waves never wait on each other
+    const int sid = (blockIdx.x * kMGroupWaves + wave) / team_heads;  // this wave's team and share
+    const int hw = wave % team_heads;                                  // its head within a chunk
+    const int nchunks = num_kv_heads / team_heads;
+    if (sid >= nshares) return;  // uniform over the team; waves never wait on each other
     const int col = lane & 15;
     const int quad = lane >> 4;
     const int num_q_heads = num_kv_heads * group;
@@ -183,11 +189,11 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
     const uint32_t ids_lds[2] = {lds_offset(&s_ids[0][0]), lds_offset(&s_ids[1][0])};
 
     ShareSpan sp;
-    if (!find_share(sid, nshares, num_seqs, num_kv_heads, kMBS, context_lens, ws_prefix, lane, sp,
-                    window))
+    if (!find_share(sid, nshares, num_seqs, nchunks, kMBS, context_lens, ws_prefix, lane, sp,
+                    window, hw == 0))
         return;
     const int x1 = sp.x1;
-    int b = sp.b, nbb = sp.nbb, g = sp.g, blk_start = sp.blk;
+    int b = sp.b, nbb = sp.nbb, ch = sp.g, blk_start = sp.blk;
 
     const char *kbase = static_cast<const char *>(k_cache);
     const char *vbase = static_cast<const char *>(v_cache);
@@ -218,7 +224,8 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
     }
 
     for (int x = sp.x0;;) {
-        // ======== segment (b, g): blocks [blk_start, blk_start + nblk) ========
+        // ======== segment (b, ch), head g: blocks [blk_start, blk_start + nblk) ========
+        const int g = ch * team_heads + hw;
         const int nblk = min(nbb - blk_start, x1 - x);
         const int ctx = context_lens[b];
         const int32_t *bt_row = block_tables + static_cast<int64_t>(b) * max_blocks;
@@ -464,7 +471,8 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
 
         // ---- this segment's partial: unnormalised acc, running max and sum ----
         const int64_t slot_row =
-            (static_cast<int64_t>(sid) + static_cast<int64_t>(b) * num_kv_heads + g) * ncols;
+            ((static_cast<int64_t>(sid) + static_cast<int64_t>(b) * nchunks + ch) * team_heads + hw) *
+            ncols;
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
             float l_tot = l_run[ct] + __shfl_xor(l_run[ct], 16);
@@ -483,8 +491,8 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
         x += nblk;
         if (x >= x1) break;
         blk_start = 0;
-        if (++g == num_kv_heads) {
-            g = 0;
+        if (++ch == nchunks) {
+            ch = 0;
             do {
                 ++b;
                 nbb = window_blocks(context_lens[b], window, kMBS);
@@ -503,19 +511,21 @@ pa_status enqueue_gqa_mfma(const DecodeShape &s, const DecodeArgs &a, const Deco
     int32_t *prefix = reinterpret_cast<int32_t *>(ws + p.prefix_offset);
     const auto kernel = gqa_mfma_partition_kernel<MX, NBUF, NT>;
     const int waves = stream_waves(kernel, kWave * kMGroupWaves, 1, kStreamWavesMax, kMGroupWaves);
-    const int groups = (waves + kMGroupWaves - 1) / kMGroupWaves;
+    const int th = team_heads(s.num_kv_heads, kMGroupWaves, p.group);
+    const int nshares = waves / th > 0 ? waves / th : 1;
+    const int groups = (nshares * th + kMGroupWaves - 1) / kMGroupWaves;
     hipLaunchKernelGGL(kernel, dim3(groups), dim3(kWave * kMGroupWaves), 0, stream, acc, ml,
                        prefix, static_cast<const uint16_t *>(a.q), a.k_cache, a.v_cache,
                        static_cast<const uint8_t *>(a.k_scale),
                        static_cast<const uint8_t *>(a.v_scale), a.block_tables, a.context_lens,
                        scale_log2, s.num_seqs, s.num_kv_heads, p.group, s.q_len,
-                       s.max_blocks_per_seq, waves, s.window);
+                       s.max_blocks_per_seq, nshares, th, s.window);
     pa_status st = hip_status(hipGetLastError(), why, "partition launch");
     if (st != PA_OK) return st;
     return hip_status(enqueue_stream_reduce<uint16_t, kMD>(
                           static_cast<uint16_t *>(a.out), acc, ml, prefix, a.context_lens,
-                          s.num_seqs, s.num_q_heads, s.num_kv_heads, p.group, kMBS, waves, stream,
-                          s.q_len, s.window, a.lse),
+                          s.num_seqs, s.num_q_heads, s.num_kv_heads, p.group, kMBS, nshares, th,
+                          stream, s.q_len, s.window, a.lse),
                       why, "reduce launch");
 }
 

@@ -13,9 +13,10 @@
 // attention kernel is the modification described in "Modification de
 // l'Attention" of the KV-sparsity article).
 //
-// gfx950 mapping (each wave64 streams its own share of the blocks; a
-// work-group holds kGroupWaves such independent waves, which the hardware
-// places one per SIMD):
+// gfx950 mapping (each wave64 streams one KV head of a share of the blocks;
+// a work-group holds kGroupWaves such waves, which the hardware places one
+// per SIMD, and the waves of a team stream neighbouring heads of the same
+// share without synchronising):
 //  * A 16-token cache block of one KV head is 16 rows of D elements.  Lane
 //    (tp = lane / 8, c = lane % 8) owns rows 2tp and 2tp+1, 16-byte chunks
 //    c, c+8, ...: every load is 16 bytes wide and each group of 8 lanes reads
@@ -149,24 +150,30 @@ constexpr int group_waves() {
 // ---------------------------------------------------------------------------
 // Split-context partition kernel, stream-K schedule.
 //
-// All (sequence b, KV head g, cache block) work items are laid out in one
-// global order (b, then g, then block) and cut into nshares equal shares;
-// wave w of work-group k streams share s = kGroupWaves k + w, which may cross
-// from one (b, g) "segment" to
-// the next.  For each segment it touches it leaves (acc, max, sum) of the G
-// query heads in partial slot w + (b * Hkv + g); the slots of one segment are
-// therefore consecutive, from w0 + k to w1 + k where w0 and w1 are the first
-// and last shares that overlap it.  Every work-group finds its share from
-// the context lengths alone; work-group 0 also stores the per-sequence block
-// prefix sums for the reduce.  Launched with one work-group per resident
-// wave slot, so every wave streams for the whole kernel.
+// The waves of a work-group form teams of TH (team_heads) waves; the KV
+// heads of a sequence form NC = Hkv / TH chunks of TH heads.  All (sequence
+// b, chunk ch, cache block) work items are laid out in one global order (b,
+// then ch, then block) and cut into nshares equal shares; team s streams
+// share s, which may cross from one (b, ch) "segment" to the next, wave hw of
+// the team taking KV head g = ch TH + hw of every block.  The team's waves do
+// not synchronise: they start together and do the same work, so they read
+// neighbouring head slices of the same token rows at about the same time.
+// For each segment a share touches, each wave leaves (acc, max, sum) of its G
+// query heads in partial slot s + (b NC + ch), row (slot TH + hw) G + head;
+// the slots of one segment are therefore consecutive, from w0 + k to w1 + k
+// (k = b NC + ch) where w0 and w1 are the first and last shares that overlap
+// it.  Every team finds its share from the context lengths alone; team 0
+// also stores the per-sequence block prefix sums for the reduce.  Launched
+// with one work-group per resident slot, so every wave streams for the
+// whole kernel.  TH = 1 is one share per wave.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int G, int NBUF, int kGroupWaves = group_waves<T, D, G, NBUF>()>
 __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
     float *__restrict__ ws_acc, float2 *__restrict__ ws_ml, int32_t *__restrict__ ws_prefix,
     const T *__restrict__ q, const T *__restrict__ k_cache, const T *__restrict__ v_cache,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
-    float scale_log2, int num_seqs, int num_kv_heads, int max_blocks, int nshares, int window) {
+    float scale_log2, int num_seqs, int num_kv_heads, int max_blocks, int nshares, int team_heads,
+    int window) {
     using C = Cfg<T, D, G>;
     constexpr int CPL = C::kCPL;
     constexpr int DPL = C::kDPL;
@@ -177,8 +184,10 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int sid = blockIdx.x * kGroupWaves + wave;  // this wave's share
-    if (sid >= nshares) return;  // uniform over the wave; waves never wait on each other
+    const int sid = (blockIdx.x * kGroupWaves + wave) / team_heads;  // this wave's team and share
+    const int hw = wave % team_heads;                                 // its head within a chunk
+    const int nchunks = num_kv_heads / team_heads;
+    if (sid >= nshares) return;  // uniform over the team; waves never wait on each other
     const int tp = lane >> 3;
     const int c = lane & 7;
     constexpr int LPH = 8 / G;                // lanes of a token pair per head
@@ -199,13 +208,13 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
     int32_t(*s_ids)[kWave] = s_ids_all[wave];
     float *s_alpha = s_alpha_all[wave];
 
-    // ---- this wave's share of the global block order -------------------------
+    // ---- this team's share of the global block order -------------------------
     ShareSpan sp;
-    if (!find_share(sid, nshares, num_seqs, num_kv_heads, kBS, context_lens, ws_prefix, lane, sp,
-                    window))
+    if (!find_share(sid, nshares, num_seqs, nchunks, kBS, context_lens, ws_prefix, lane, sp,
+                    window, hw == 0))
         return;
     const int x1 = sp.x1;
-    int b = sp.b, nbb = sp.nbb, g = sp.g, blk_start = sp.blk;
+    int b = sp.b, nbb = sp.nbb, ch = sp.g, blk_start = sp.blk;
 
     const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * C::kRowBytes;
     const int64_t blk_stride = kBS * row_stride;
@@ -222,7 +231,8 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
     const uint32_t pv_sel = (kEB == 2 && DPL == 1 && (lane & 1)) ? 0x07060302u : 0x05040100u;
 
     for (int x = sp.x0;;) {
-        // ======== segment (b, g): blocks [blk_start, blk_start + nblk) ========
+        // ======== segment (b, ch), head g: blocks [blk_start, blk_start + nblk) ========
+        const int g = ch * team_heads + hw;
         const int nblk = min(nbb - blk_start, x1 - x);
         const int ctx = context_lens[b];
         // the window's first token and block (0 and 0 without a window)
@@ -447,7 +457,8 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
         // ---- this segment's partial: unnormalised acc, running max and sum ----
         const float l_tot = sum_over_tp(l_run);
         const int64_t slot_row =
-            (static_cast<int64_t>(sid) + static_cast<int64_t>(b) * num_kv_heads + g) * G;
+            ((static_cast<int64_t>(sid) + static_cast<int64_t>(b) * nchunks + ch) * team_heads + hw) *
+            G;
         if (tp == 0 && head_writer) ws_ml[slot_row + hc] = make_float2(m_run, l_tot);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -462,8 +473,8 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
         if (x >= x1) break;
         // next segment in the global order; sequences with no blocks hold none
         blk_start = 0;
-        if (++g == num_kv_heads) {
-            g = 0;
+        if (++ch == nchunks) {
+            ch = 0;
             do {
                 ++b;
                 nbb = window_blocks(context_lens[b], window, kBS);
@@ -483,18 +494,20 @@ pa_status enqueue_grouped(const DecodeShape &s, const DecodeArgs &a, const Decod
     const auto kernel = grouped_partition_kernel<T, D, G, NBUF>;
     constexpr int kGroupWaves = group_waves<T, D, G, NBUF>();
     const int waves = stream_waves(kernel, kWave * kGroupWaves, 1, kStreamWavesMax, kGroupWaves);
-    const int groups = (waves + kGroupWaves - 1) / kGroupWaves;
+    const int th = team_heads(s.num_kv_heads, kGroupWaves, G);
+    const int nshares = waves / th > 0 ? waves / th : 1;
+    const int groups = (nshares * th + kGroupWaves - 1) / kGroupWaves;
     hipLaunchKernelGGL(kernel, dim3(groups), dim3(kWave * kGroupWaves), 0, stream, acc, ml, prefix,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k_cache),
                        static_cast<const T *>(a.v_cache), a.block_tables, a.context_lens,
-                       scale_log2, s.num_seqs, s.num_kv_heads, s.max_blocks_per_seq, waves,
+                       scale_log2, s.num_seqs, s.num_kv_heads, s.max_blocks_per_seq, nshares, th,
                        s.window);
     pa_status st = hip_status(hipGetLastError(), why, "partition launch");
     if (st != PA_OK) return st;
     return hip_status(enqueue_stream_reduce<T, D>(static_cast<T *>(a.out), acc, ml, prefix,
                                                   a.context_lens, s.num_seqs, s.num_q_heads,
-                                                  s.num_kv_heads, G, kBS, waves, stream, 1,
-                                                  s.window, a.lse),
+                                                  s.num_kv_heads, G, kBS, nshares, th, stream,
+                                                  1, s.window, a.lse),
                       why, "reduce launch");
 }
 

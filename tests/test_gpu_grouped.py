@@ -160,6 +160,21 @@ def test_stream_split_does_not_change_result(dev, waves, ring, monkeypatch):
     say(f"  {compare(d.decode(), oracle.decode_workload(w), 'bf16')}")
 
 
+@pytest.mark.parametrize("team", ["1", "2", "4"])
+@pytest.mark.parametrize("waves", ["3", "5", "300"])
+def test_head_teams_do_not_change_result(dev, team, waves, monkeypatch):
+    """Teams of 1, 2 or 4 waves (one KV head each) sharing a stream share, with
+    share counts that are not multiples of a team (3 and 5 waves leave one
+    team), over empty, one-token, block-edge and long contexts."""
+    say(f"case: teams of {team}, {waves} stream waves")
+    monkeypatch.setenv("PA_TEAM_HEADS", team)
+    monkeypatch.setenv("PA_STREAM_WAVES", waves)
+    w = make_workload(custom_spec(6, 64, 8, 128, 16, "bf16", ctx=[1, 700, 0, 2049, 16, 95]),
+                      seed=21)
+    d = to_device(w, dev)
+    say(f"  {compare(d.decode(), oracle.decode_workload(w), 'bf16')}")
+
+
 @pytest.mark.parametrize("dtype,D,hq,hkv", [("bf16", 128, 64, 8), ("f32", 64, 4, 2),
                                             ("bf16", 64, 16, 4)])
 def test_long_segments_refill_block_ids(dev, dtype, D, hq, hkv, monkeypatch):
