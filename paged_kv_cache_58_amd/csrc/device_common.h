@@ -83,9 +83,16 @@ __device__ __forceinline__ void wait_vmem() {
 __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // One global_load_lds_dword: lane l's 4 bytes at sbase + voff land in LDS at
-// m0 + 4 * l (used for the block ids of a segment).
+// m0 + 4 * l (used for the block ids of a segment).  The compiler does not
+// look inside inline assembly for hazards, and a vector memory instruction
+// may read an SGPR only 5 wait states after a VALU instruction wrote it (as
+// v_readlane does when a spilled base pointer is reloaded right before):
+// hence the s_nop 4.  This load runs once per 64 blocks; the hot-loop loads
+// (dma16) go without it, and a static test checks the compiled kernels for
+// the pattern instead.
 __device__ __forceinline__ void dma4(const void *sbase, uint32_t voff, uint32_t lds) {
-    asm volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+    asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds)
+                 : "memory");
 }
 
 // s_waitcnt the compiler itself understands (it then knows its own loads,

@@ -14,26 +14,36 @@
 // Here all query heads share one K/V row, so each block is a dense
 // contraction and runs on the matrix cores (v_mfma_f32_32x32x16_bf16).
 //  * A work-group has NW = 1, 2 or 4 waves, one per SIMD, and covers 32 NW
-//    heads (the query heads, padded).  The latent is streamed in units of 32
-//    tokens (half a 64-token block, 36 KB) by global_load_lds_dwordx4 into a
-//    four-slot LDS ring: two units are in flight while one is read, by
-//    every wave, from LDS (deeper read-ahead only stalled the in-order waves
-//    at issue).  Rows past the context are zero-filled instead of fetched.
+//    heads (the query heads, padded).  Each sequence is cut into parts of
+//    near-equal size, one work-group per part, so a work-group streams one
+//    stretch of one sequence (split-KV partitions; the log-sum-exp reduce
+//    merges a sequence's parts).  The latent is streamed in units of 32
+//    tokens (half a 64-token block, 36 KB) by global_load_lds_dwordx4 into
+//    an LDS ring of four main regions (dims 0..511) and three RoPE regions
+//    (dims 512..575): while unit u is being consumed, units u + 2 and u + 3
+//    are in flight.
 //  * Scores: wave w computes S^T[token, head] = L[token, :] . Q^T for heads
 //    32w..32w+31; the latent rows are the A operand (16 contiguous bytes per
 //    lane) and q sits in registers as the B operand for the whole segment.
 //    A lane's S^T accumulator holds 16 of the unit's 32 tokens for one head
-//    (the other 16 sit in lane ^ 32), so the running max is an in-lane max
-//    and one lane exchange, and the probabilities, rounded to bf16, come out
-//    in the B-operand layout of O^T[dim, head] += V^T[dim, token] .
-//    P^T[token, head].  They go to LDS (8 KB per unit), with the rescale
-//    factors of heads whose running max moved.
+//    (the other 16 sit in lane ^ 32, one v_permlane32_swap away), so the
+//    running max is an in-lane max and one lane exchange, and the
+//    probabilities, rounded to bf16, come out in the B-operand layout of
+//    O^T[dim, head] += V^T[dim, token] . P^T[token, head].  They go to LDS
+//    (8 KB per unit, two buffers), with the rescale factors of heads whose
+//    running max moved.
 //  * Values: wave w accumulates O^T for dims 512 w / NW .. + 512 / NW - 1 of
 //    every head, as (16 / NW) x NW register-blocked 32 x 32 tiles held in the
 //    accumulation registers (256 per lane).  Each V^T fragment (transposed
 //    reads, ds_read_b64_tr_b16) feeds NW products and each P^T fragment
 //    16 / NW, so the LDS traffic per product stays well under what the
-//    matrix core consumes.
+//    matrix core consumes (a wave reading every dim itself would issue four
+//    times the transposed reads, which run at about a quarter of the rate of
+//    16-byte reads).
+//  * Software pipeline, one barrier per unit: the value products of unit u
+//    run beside the score products of unit u + 1, and the softmax of unit
+//    u + 1 beside the rest of them, so the matrix core has work while the
+//    vector unit takes the exponentials.
 //  * LDS layout of a unit: the first 64 16-byte chunks of every row (dims
 //    0..511) in a 32 KB region of 1 KB rows, the 8 RoPE chunks in a 4 KB
 //    region of 128-byte rows.  Chunk c of main row t sits at c ^ swm(t),
@@ -41,6 +51,7 @@
 //    row-wise and transposed reads on distinct banks.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "device_common.h"
@@ -127,6 +138,13 @@ __device__ __forceinline__ void mfma_v_last(f32x16_t &c0, f32x16_t &c1, bf16x8_t
         "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
         : "+v"(c0), "+v"(c1) : "v"(a0), "v"(a1), "v"(b0), "v"(b1) : "memory");
 }
+// The last product of a score chain, then the fence.
+__device__ __forceinline__ void mfma_v_fence(f32x16_t &c, bf16x8_t a, bf16x8_t b) {
+    asm volatile(
+        "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+        "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+        : "+v"(c) : "v"(a), "v"(b) : "memory");
+}
 __device__ __forceinline__ void mfma_a(f32x16_t &c, bf16x8_t a, bf16x8_t b) {
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b) : "memory");
 }
@@ -151,13 +169,25 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
     constexpr int HT = NW;              // head tiles (of 32) in the work-group
     constexpr int DT = kDimTiles / NW;  // output dim tiles per wave
     static_assert(DT * HT == 16, "16 accumulator tiles per wave");
-    constexpr int kVR = 4;              // V^T operands read ahead
+    constexpr int kVR = 3;              // V^T operands read ahead
+    constexpr int kRA = 4;              // score A operands read ahead
+    constexpr int kNV = 2 * DT;         // value steps (of HT products) per unit
+    // of them beside the score chain (half; a quarter with two waves, whose
+    // wider value steps overflowed the registers there), the rest beside the softmax
+    constexpr int kVA = NW == 2 ? kNV / 4 : kNV / 2;
 
-    __shared__ __attribute__((aligned(16))) uint4 s_ring[kSlots][kUnitB / 16];
-    __shared__ __attribute__((aligned(16))) u32x4_t s_p[HT][2][kWave];  // P^T fragments
-    __shared__ float s_alpha[HT * kHeads];  // rescale factor of each head this unit
-    __shared__ __attribute__((aligned(16))) int32_t s_flag[4];  // head tile ht rescaled
+    // Ring: main regions (dims 0..511 of 32 rows) for units u % 4, RoPE
+    // regions (dims 512..575) for units u % 3: while step u runs, unit u's
+    // main region (values), unit u + 1's main and RoPE regions (scores) and
+    // units u + 2 and u + 3 (streaming in) are live, and unit u's RoPE rows
+    // are not needed any more.  That leaves room for two probability buffers.
+    __shared__ __attribute__((aligned(16))) uint4 s_main[kSlots][kUnitMainB / 16];
+    __shared__ __attribute__((aligned(16))) uint4 s_rope[3][(kUnitB - kUnitMainB) / 16];
+    __shared__ __attribute__((aligned(16))) u32x4_t s_p[2][HT][2][kWave];  // P^T fragments of unit u in [u & 1]
+    __shared__ float s_alpha[2][HT * kHeads];  // rescale factor of each head, unit u in [u & 1]
+    __shared__ __attribute__((aligned(16))) int32_t s_flag[2][4];  // head tile ht rescaled in unit u
     __shared__ __attribute__((aligned(16))) int32_t s_ids[2][kWave];
+    __shared__ __attribute__((aligned(16))) uint4 s_sink[kWave];  // target of padding loads
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -168,52 +198,87 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
     const int head = wave * kHeads + l31;  // this lane's head in the scores
     const bool head_ok = head < num_heads;
 
-    // ---- this work-group's share of the global block order (b, block) ----
-    int seq_blocks_total = 0;
+    // ---- this work-group's part: a sequence-aligned split ------------------
+    // Sequence b (nb_b blocks) is cut into k_b = ceil(nb_b / P) parts of
+    // near-equal size, P the smallest part size for which every part gets a
+    // work-group (sum of k_b <= gridDim.x; the host launches at least one
+    // work-group per sequence).  Work-group j takes part j - K_b of the
+    // sequence b with K_b <= j < K_b + k_b, K_b the number of parts of the
+    // sequences before b, so each work-group streams one segment of one
+    // sequence: a change of segment inside a work-group (partial store, q
+    // reload, refilling the ring) costs about as much as a dozen units.  Its
+    // partial goes to slot j; work-group 0 stores K_b (num_seqs + 1 entries)
+    // for the reduce.
+    auto seq_blocks = [&](int bb) {
+        return bb < num_seqs ? (context_lens[bb] + kLBS - 1) / kLBS : 0;
+    };
+    int total = 0, most = 0;  // blocks of all sequences; of the longest
     for (int base = 0; base < num_seqs; base += kWave) {
-        const int bb = base + lane;
-        const int nb = bb < num_seqs ? (context_lens[bb] + kLBS - 1) / kLBS : 0;
-        const int incl = wave_incl_scan(nb, lane);
-        if (blockIdx.x == 0 && wave == 0 && bb < num_seqs)
-            ws_prefix[bb] = seq_blocks_total + incl - nb;
-        seq_blocks_total += __builtin_amdgcn_readlane(incl, kWave - 1);
+        const int nb = seq_blocks(base + lane);
+        total += __builtin_amdgcn_readlane(wave_incl_scan(nb, lane), kWave - 1);
+        int m = nb;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) m = max(m, __shfl_xor(m, d));
+        most = max(most, m);
     }
-    if (blockIdx.x == 0 && tid == 0) ws_prefix[num_seqs] = seq_blocks_total;
-    const int total = seq_blocks_total;
-    const int share = stream_share(total, static_cast<int>(gridDim.x));
-    const int64_t x0l = static_cast<int64_t>(blockIdx.x) * share;
-    if (x0l >= total) return;  // uniform over the work-group
-    const int x0 = static_cast<int>(x0l);
-    const int x1 = min(x0 + share, total);
-
-    int b = 0, nbb = 0, cb = 0;
-    for (int base = 0, carry = 0;; base += kWave) {
+    if (total == 0) return;  // every context empty: the reduce writes zeros
+    const int grid = static_cast<int>(gridDim.x);
+    auto parts = [&](int P) {  // sum over the sequences of ceil(nb_b / P)
+        int k_all = 0;
+        for (int base = 0; base < num_seqs; base += kWave) {
+            const int nb = seq_blocks(base + lane);
+            k_all += __builtin_amdgcn_readlane(wave_incl_scan((nb + P - 1) / P, lane), kWave - 1);
+        }
+        return k_all;
+    };
+    // parts(P) only falls as P grows, and parts(most) <= num_seqs <= grid
+    int lo = max(1, (total + grid - 1) / grid), hi = max(most, lo);
+    while (lo < hi) {
+        const int mid = (lo + hi) / 2;
+        if (parts(mid) <= grid) hi = mid;
+        else lo = mid + 1;
+    }
+    const int P = lo;
+    int b = -1, part = 0, k_b = 1, nb_b = 0;
+    for (int base = 0, carry = 0; base < num_seqs; base += kWave) {
         const int bb = base + lane;
-        const int nb = bb < num_seqs ? (context_lens[bb] + kLBS - 1) / kLBS : 0;
-        const int incl = wave_incl_scan(nb, lane);
-        const uint64_t hit = __builtin_amdgcn_ballot_w64(bb < num_seqs && carry + incl > x0);
-        if (hit != 0) {
+        const int nb = seq_blocks(bb);
+        const int k = (nb + P - 1) / P;
+        const int incl = wave_incl_scan(k, lane);
+        if (blockIdx.x == 0 && wave == 0 && bb < num_seqs) ws_prefix[bb] = carry + incl - k;
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(bb < num_seqs && carry + incl > static_cast<int>(blockIdx.x));
+        if (b < 0 && hit != 0) {
             const int f = __builtin_ctzll(hit);
             b = base + f;
-            nbb = __builtin_amdgcn_readlane(nb, f);
-            cb = carry + __builtin_amdgcn_readlane(incl, f) - nbb;
-            break;
+            k_b = __builtin_amdgcn_readlane(k, f);
+            nb_b = __builtin_amdgcn_readlane(nb, f);
+            part = static_cast<int>(blockIdx.x) - (carry + __builtin_amdgcn_readlane(incl, f) - k_b);
         }
         carry += __builtin_amdgcn_readlane(incl, kWave - 1);
+        if (blockIdx.x == 0 && wave == 0 && lane == 0 && base + kWave >= num_seqs)
+            ws_prefix[num_seqs] = carry;
     }
-    int blk_start = x0 - cb;
+    if (b < 0) return;  // a work-group past the last part (uniform)
+    const int blk_start = part * nb_b / k_b;
+    const int seg_blocks = (part + 1) * nb_b / k_b - blk_start;
 
-    const uint32_t ring_lds = lds_offset(s_ring);
+    // the main regions start zeroed (rows past a context are never fetched)
+    for (int i = tid; i < kSlots * kUnitMainB / 16; i += NW * kWave)
+        (&s_main[0][0])[i] = make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t main_lds = lds_offset(s_main);
+    const uint32_t rope_lds = lds_offset(s_rope);
     const uint32_t ids_lds[2] = {lds_offset(&s_ids[0][0]), lds_offset(&s_ids[1][0])};
+    auto main_slot = [&](int u) { return main_lds + (u % kSlots) * kUnitMainB; };
+    auto rope_slot = [&](int u) { return rope_lds + (u % 3) * (kUnitB - kUnitMainB); };
 
-    // ---- per-lane LDS addresses (bytes, relative to a ring slot) ----------
+    // ---- per-lane LDS addresses (bytes, relative to a region) -------------
     // S^T A operand: unit row l31, chunk 2 ks + hk.  swm of that row is
     // swm(lane & 15) and the xor touches the low 4 chunk bits only, so the
-    // byte offset in a row is 256 (ks >> 3) + (32 (ks & 7) ^ qx) with
+    // byte offset in a main row is 256 (ks >> 3) + (32 (ks & 7) ^ qx) with
     // qx = 16 (hk ^ swm).  RoPE rows likewise: offset 32 (ks - 32) ^ rx.
     const uint32_t qrow = l31 * kMainRowB;
     const uint32_t qx = 16u * static_cast<uint32_t>(hk ^ swm(lane & 15));
-    const uint32_t rrow = kUnitMainB + l31 * kRopeRowB;
+    const uint32_t rrow = l31 * kRopeRowB;
     const uint32_t rx = 16u * static_cast<uint32_t>(hk ^ swr(l31));
     // V^T A operand by transposed reads.  16-lane group g = lane >> 4 reads
     // rows tb + (i >> 2), i = lane & 15, dims 32 dt + 16 (g & 1) + 4 (i & 3),
@@ -233,12 +298,13 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
             vy[qq] = 16u * static_cast<uint32_t>(c0 ^ swm(trow));
         }
     }
-    // P^T fragment (head tile ht, k-step s) of this lane: 16 bytes
-    const uint32_t p_lds = lds_offset(&s_p[0][0][0]) + 16 * lane;
+    // P^T fragment (buffer, head tile ht, k-step s) of this lane: 16 bytes
+    const uint32_t p_lds = lds_offset(&s_p[0][0][0][0]) + 16 * lane;
+    constexpr uint32_t kPBuf = HT * 2 * kWave * 16;
 
-    for (int x = x0;;) {
-        // ======== segment: sequence b, blocks [blk_start, blk_start + nblk) ========
-        const int nblk = min(nbb - blk_start, x1 - x);
+    {
+        // ======== the segment: sequence b, blocks [blk_start, blk_start + nblk) ========
+        const int nblk = seg_blocks;
         const int ctx = context_lens[b];
         const int32_t *bt_row = block_tables + static_cast<int64_t>(b) * max_blocks;
         auto fetch_ids = [&](int m) {
@@ -276,39 +342,43 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
 
         // Units of this segment: 32-token halves of its blocks that hold at
         // least one context token (only a sequence's last block can end
-        // early, so unit u is half u & 1 of block u >> 1).
+        // early, so unit u is half u & 1 of block u >> 1).  Tokens at or past
+        // seg_lim belong to no unit of the segment.
         const int seg_tok0 = blk_start * kLBS;
-        const int nunits =
-            (min(ctx, (blk_start + nblk) * kLBS) - seg_tok0 + kUnitTok - 1) / kUnitTok;
+        const int seg_lim = min(ctx, (blk_start + nblk) * kLBS);
+        const int nunits = (seg_lim - seg_tok0 + kUnitTok - 1) / kUnitTok;
 
-        // DMA of unit u into ring slot u % 4: this wave's rows i = wave + NW k,
-        // k < kPer, of the unit's 36 (32 main rows, 4 groups of 8 RoPE rows).
-        // Main rows at or past the context are zero-filled instead (NaN in the
-        // V operand would survive a zero probability); RoPE rows only feed
+        // DMA of unit u: this wave's rows i = wave + NW k, k < kPer, of the
+        // unit's 36 (32 main rows, 4 groups of 8 RoPE rows).  A main row at or
+        // past the context is not fetched: its load reads the unit's first
+        // row into s_sink instead (selected, not branched, so every wave has
+        // exactly kPer loads per unit in flight and the vmcnt waits below stay
+        // exact), and the slot keeps what it held, which is finite: the main
+        // regions start zeroed and later hold only fetched rows of the
+        // context.  The probabilities of those tokens are exactly 0, so they
+        // contribute exactly 0 (a NaN there would not).  RoPE rows only feed
         // scores, which are masked.
         constexpr int kPer = (kDmaPerUnit + NW - 1) / NW;
         auto unit_src = [&](int u, int pb) {
             return reinterpret_cast<const char *>(latent) + static_cast<int64_t>(pb) * kBlockB +
                    (u & 1) * kUnitTok * kRowB;
         };
-        auto issue_row = [&](int u, const char *src, int k) {
+        // live = false (a unit past the segment's last): the same kPer loads,
+        // from the pool's first row into s_sink, so every step has kPer loads.
+        auto issue_row = [&](int u, const char *src, int k, bool live) {
             const int i = wave + NW * k;
             if (i >= kDmaPerUnit) return;
-            const uint32_t slot = ring_lds + (u % kSlots) * kUnitB;
             // recomputed per row rather than kept live across the loop
             int ln = lane;
             asm volatile("" : "+v"(ln));
             if (i < kUnitTok) {  // main region: row i, lane = swizzled chunk
-                if (i < ctx - (seg_tok0 + u * kUnitTok)) {
-                    dma16(src, i * kRowB + ((ln ^ swm(i)) * 16), slot + i * kMainRowB);
-                } else {
-                    *(__attribute__((address_space(3))) u32x4_t *)(uintptr_t)(
-                        slot + i * kMainRowB + ln * 16) = u32x4_t{0, 0, 0, 0};
-                }
+                const bool fetch = live && i < ctx - (seg_tok0 + u * kUnitTok);  // uniform
+                dma16(src, fetch ? i * kRowB + ((ln ^ swm(i)) * 16) : ln * 16,
+                      fetch ? main_slot(u) + i * kMainRowB : lds_offset(s_sink));
             } else {             // RoPE region: 8 rows x 8 chunks
                 const int t = 8 * (i - kUnitTok) + (ln >> 3);
-                dma16(src, t * kRowB + (kMainChunks + ((ln & 7) ^ swr(t))) * 16,
-                      slot + kUnitMainB + (i - kUnitTok) * 1024);
+                dma16(src, live ? t * kRowB + (kMainChunks + ((ln & 7) ^ swr(t))) * 16 : ln * 16,
+                      live ? rope_slot(u) + (i - kUnitTok) * 1024 : lds_offset(s_sink));
             }
         };
         // Block ids come in chunks of 64 through s_ids; wave 0 fetches chunk
@@ -320,177 +390,220 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
         };
         auto unit_id = [&](int u) { return s_ids[((u >> 1) >> 6) & 1][(u >> 1) & (kWave - 1)]; };
 
+        // A operand of score k-step ks of unit u (the compiler keeps the lane's
+        // 12 row offsets live; the V^T reads below recompute theirs at each use,
+        // where an empty asm hides the lane's terms, to stay in the register
+        // budget)
+        auto qk_read = [&](int u, int ks) {
+            const uint32_t x = ks < kMainKSteps ? qx : rx;
+            const uint32_t addr =
+                ks < kMainKSteps ? main_slot(u) + qrow + 256 * (ks >> 3) + ((32u * (ks & 7)) ^ x)
+                                 : rope_slot(u) + rrow + ((32u * (ks - kMainKSteps)) ^ x);
+            return ds_read_b128(addr);
+        };
         // V^T operand (k-step s, this wave's dim tile dt, half qq) of unit u
         auto pv_read = [&](int u, int s, int dt, int qq) {
             const int dg = DT * wave + dt;  // global dim tile
-            return ds_read_tr(ring_lds + (u % kSlots) * kUnitB + (16 * s) * kMainRowB +
-                              256 * (dg >> 2) + vrow[qq] + ((64u * (dg & 3)) ^ vy[qq]));
+            uint32_t y = vy[qq];
+            asm volatile("" : "+v"(y));
+            return ds_read_tr(main_slot(u) + (16 * s) * kMainRowB + 256 * (dg >> 2) + vrow[qq] +
+                              ((64u * (dg & 3)) ^ y));
         };
 
-        // ---- scores and probabilities of unit u for this wave's 32 heads ----
-        auto scores = [&](int u, int un, const char *srcn) {
-            const uint32_t slot = ring_lds + (u % kSlots) * kUnitB;
+        // The score chain of unit u over k-steps [k0, k1) into s (A operands
+        // read kRA steps ahead); before each product f(ks) runs, pinned there
+        // by the products' memory clobber.
+        bf16x8_t xa[kRA];
+        auto score_steps = [&](f32x16_t &s, int u, int k0, int k1, auto &&f) {
+#pragma unroll
+            for (int ks = k0; ks < k1; ++ks) {
+                f(ks);
+                const int r = ks % kRA;
+                if (ks == 0) mfma_v0(s, xa[r], qf[ks]);
+                else if (ks + 1 < kKSteps) mfma_v(s, xa[r], qf[ks]);
+                else mfma_v_fence(s, xa[r], qf[ks]);
+                if (ks + kRA < kKSteps) xa[r] = qk_read(u, ks + kRA);
+            }
+        };
+        auto score_prefetch = [&](int u) {
+#pragma unroll
+            for (int ks = 0; ks < kRA; ++ks) xa[ks] = qk_read(u, ks);
+        };
+
+        // Softmax of unit u from its raw scores s, in pieces 0..11: the running
+        // max and sum of this lane's head and the P^T fragments of this wave's
+        // head tile into buffer u & 1, with the rescale factor when the max
+        // moved.  Register j of s: token 8 (j >> 2) + 4 hk + (j & 3) of the
+        // unit; tokens at or past seg_lim are masked, so the score chain that
+        // runs past a segment's last unit changes nothing here.
+        bool moved = false;
+        float bmax = kNegInf;
+        uint32_t w4[4];
+        auto softmax_piece = [&](f32x16_t &s, int u, int piece) {
             const int tok0 = seg_tok0 + u * kUnitTok;
-            // S^T = L . Q^T: 32 tokens x 32 heads, in two accumulator chains
-            // (even and odd k-steps)
-            auto qk_read = [&](int ks) {
-                const uint32_t addr =
-                    ks < kMainKSteps
-                        ? slot + qrow + 256 * (ks >> 3) + ((32u * (ks & 7)) ^ qx)
-                        : slot + rrow + ((32u * (ks - kMainKSteps)) ^ rx);
-                return ds_read_b128(addr);
-            };
-            bf16x8_t xa[kQD];
+            if (piece < 2) {
+                float lmax = piece == 0 ? kNegInf : bmax;
 #pragma unroll
-            for (int ks = 0; ks < kQD; ++ks) xa[ks] = qk_read(ks);
-            f32x16_t sa, sb;
-#pragma unroll
-            for (int ks = 0; ks < kKSteps; ++ks) {
-                const int r = ks % kQD;
-                if (ks < 2) {
-                    mfma_v0(ks ? sb : sa, xa[r], qf[ks]);
-                } else if (ks + 2 < kKSteps) {
-                    mfma_v(ks & 1 ? sb : sa, xa[r], qf[ks]);
-                } else if (ks + 1 == kKSteps) {
-                    mfma_v_last(sa, sb, xa[(ks - 1) % kQD], xa[r], qf[ks - 1], qf[ks]);
-                }
-                if (ks + kQD < kKSteps && ks + 2 < kKSteps) xa[r] = qk_read(ks + kQD);
-                // this wave's DMA rows of unit un, spread over 9 points of the
-                // chain so that each issues in the shadow of the products
-                if ((ks & 3) == 3 && un >= 0) {
-                    constexpr int kStep = (kPer + 8) / 9;
-#pragma unroll
-                    for (int k = (ks >> 2) * kStep; k < ((ks >> 2) + 1) * kStep && k < kPer; ++k)
-                        issue_row(un, srcn, k);
-                }
-            }
-            // online softmax: reg j holds token 8 (j >> 2) + 4 hk + (j & 3) of
-            // the unit for this lane's head
-            float lmax = kNegInf;
-            if (tok0 + kUnitTok <= ctx) {  // every unit but a sequence's last
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    sa[j] = (sa[j] + sb[j]) * scale_log2;
-                    lmax = fmaxf(lmax, sa[j]);
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
+                for (int j = 8 * piece; j < 8 * piece + 8; ++j) {
                     const int tk = tok0 + 8 * (j >> 2) + 4 * hk + (j & 3);
-                    sa[j] = tk < ctx ? (sa[j] + sb[j]) * scale_log2 : kNegInf;
-                    lmax = fmaxf(lmax, sa[j]);
+                    s[j] = tk < seg_lim ? s[j] * scale_log2 : kNegInf;
+                    lmax = fmaxf(lmax, s[j]);
                 }
-            }
-            const float bmax = fmaxf(lmax, __shfl_xor(lmax, 32));
-            const bool moved = __builtin_amdgcn_ballot_w64(bmax > m_run + kLSlack) != 0;
-            if (moved) {
-                const float m_new = fmaxf(m_run, bmax);
-                const float alpha = exp2_fast(m_run - m_new);
-                l_run *= alpha;
-                m_run = m_new;
-                if (hk == 0) s_alpha[head] = alpha;
-            }
-            if (lane == 0) s_flag[wave] = moved && u > 0;  // u = 0: the accumulators are zero
-            // P^T B-operand fragment of k-step s (tokens 16 s ..): k = 8 hk + jj
-            // is S^T reg 8 s + jj
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                uint32_t w4[4];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    w4[v] = pack_bf16(exp2_fast(sa[8 * s + 2 * v] - m_run),
-                                      exp2_fast(sa[8 * s + 2 * v + 1] - m_run));
-                    l_run += bf16_lo(w4[v]) + bf16_hi(w4[v]);
+                bmax = lmax;
+            } else if (piece == 2) {
+                // the other 16 tokens of this head sit in lane ^ 32
+                const auto r = __builtin_amdgcn_permlane32_swap(as_u(bmax), as_u(bmax), false, false);
+                bmax = fmaxf(as_f(r[0]), as_f(r[1]));
+            } else if (piece == 3) {
+                moved = __builtin_amdgcn_ballot_w64(bmax > m_run + kLSlack) != 0;
+                if (moved) {
+                    const float m_new = fmaxf(m_run, bmax);
+                    const float alpha = exp2_fast(m_run - m_new);
+                    l_run *= alpha;
+                    m_run = m_new;
+                    if (hk == 0) s_alpha[u & 1][head] = alpha;
                 }
-                s_p[wave][s][lane] = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
-            }
-        };
-
-        // ---- O^T += V^T . P^T for this wave's dims, every head, unit u ------
-        // V^T operand i = DT s + dt (k-step s, dim tile dt) sits in ring slot
-        // i % kVR of vlo / vhi; the first kVR are read before the barrier.
-        auto values = [&](int u, s16x4_t (&vlo)[kVR], s16x4_t (&vhi)[kVR]) {
-            // rescale the heads whose running max moved (rare); tile by tile
-            // through VGPRs so that at most one tile is out of the
-            // accumulation registers at a time
-            const u32x4_t fl = *(const __attribute__((address_space(3))) u32x4_t *)(
-                uintptr_t)lds_offset(s_flag);
-            if (__builtin_expect((fl[0] | fl[1] | fl[2] | fl[3]) != 0, 0)) {
-                float alpha[HT];
-#pragma unroll
-                for (int ht = 0; ht < HT; ++ht)
-                    alpha[ht] = fl[ht] != 0 ? s_alpha[ht * kHeads + l31] : 1.0f;
-                acc_fence(acc);
-#pragma unroll
-                for (int t = 0; t < 16; ++t) {
-                    f32x16_t x = acc[t];
-                    asm volatile("" : "+v"(x));
-                    x *= alpha[t % HT];
-                    asm volatile("" : "+v"(x));
-                    acc[t] = x;
-                    asm volatile("" : "+a"(acc[t]));
-                }
-                asm volatile("s_nop 2" ::: "memory");
-            }
-            bf16x8_t pb[HT];
-#pragma unroll
-            for (int i = 0; i < 2 * DT; ++i) {
-                const int s = i / DT, dt = i % DT;
-                if (dt == 0) {
-#pragma unroll
-                    for (int ht = 0; ht < HT; ++ht)
-                        pb[ht] = ds_read_b128(p_lds + (ht * 2 + s) * kWave * 16);
-                }
-                const int r = i % kVR;
-                const bf16x8_t va = __builtin_bit_cast(
-                    bf16x8_t, __builtin_shufflevector(vlo[r], vhi[r], 0, 1, 2, 3, 4, 5, 6, 7));
-                if (i + kVR < 2 * DT) {
-                    vlo[r] = pv_read(u, (i + kVR) / DT, (i + kVR) % DT, 0);
-                    vhi[r] = pv_read(u, (i + kVR) / DT, (i + kVR) % DT, 1);
-                }
-#pragma unroll
-                for (int ht = 0; ht < HT; ++ht) mfma_a(acc[dt * HT + ht], va, pb[ht]);
+                if (lane == 0) s_flag[u & 1][wave] = moved && u > 0;  // u = 0: nothing to rescale
+            } else {
+                // pieces 4..11: probabilities 2 v, 2 v + 1 of k-step v >> 2
+                const int v = piece - 4, sv = v >> 2, e = v & 3;
+                w4[e] = pack_bf16(exp2_fast(s[2 * v] - m_run), exp2_fast(s[2 * v + 1] - m_run));
+                l_run += bf16_lo(w4[e]) + bf16_hi(w4[e]);
+                if (e == 3)
+                    *(__attribute__((address_space(3))) u32x4_t *)(uintptr_t)(
+                        p_lds + (u & 1) * kPBuf + (wave * 2 + sv) * kWave * 16) =
+                        u32x4_t{w4[0], w4[1], w4[2], w4[3]};
             }
         };
 
-        for (int u = 0; u < nunits && u < kAhead; ++u) {
-            refill_ids(u);
-            const char *src = unit_src(u, __builtin_amdgcn_readfirstlane(unit_id(u)));
-            for (int k = 0; k < kPer; ++k) issue_row(u, src, k);
-        }
-        for (int u = 0; u < nunits; ++u) {
-            // unit un streams in during this step; its block id is read before
-            // the barrier, whose LDS wait covers the read
-            const int un = u + kAhead < nunits ? u + kAhead : -1;
-            const int idn = un >= 0 ? unit_id(un) : 0;
-            // this wave's rows of unit u have landed once at most the units
-            // issued after it are outstanding
-            const int later = min(nunits - 1 - u, kAhead - 1);
-            if (later >= 2 && 2 * kPer <= 63) wait_vmem<(2 * kPer <= 63 ? 2 * kPer : 0)>();
-            else if (later >= 1 && kPer <= 63) wait_vmem<(kPer <= 63 ? kPer : 0)>();
-            else wait_vmem<0>();
-            __syncthreads();  // every wave's rows landed; unit u - 1 is no longer read
-            if (un >= 0) refill_ids(un);
-            scores(u, un, un >= 0 ? unit_src(un, __builtin_amdgcn_readfirstlane(idn)) : nullptr);
-            // the first V^T operands go out before the barrier
-            s16x4_t vlo[kVR], vhi[kVR];
+        // O^T += V^T P^T for this wave's dims, every head, unit u, in 2 DT value
+        // steps of HT products (V^T operand i = DT s + dt sits in slot i % kVR).
+        s16x4_t vlo[kVR], vhi[kVR];
+        bf16x8_t pb[HT];
+        auto value_prefetch = [&](int u) {
 #pragma unroll
             for (int i = 0; i < kVR; ++i) {
                 vlo[i] = pv_read(u, i / DT, i % DT, 0);
                 vhi[i] = pv_read(u, i / DT, i % DT, 1);
             }
-            __syncthreads();  // every wave's probabilities and rescale flags are in LDS
-            values(u, vlo, vhi);
+        };
+        auto value_step = [&](int u, int i) {
+            const int s = i / DT, dt = i % DT;
+            if (dt == 0) {
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht)
+                    pb[ht] = ds_read_b128(p_lds + (u & 1) * kPBuf + (ht * 2 + s) * kWave * 16);
+            }
+            const int r = i % kVR;
+            const bf16x8_t va = __builtin_bit_cast(
+                bf16x8_t, __builtin_shufflevector(vlo[r], vhi[r], 0, 1, 2, 3, 4, 5, 6, 7));
+            if (i + kVR < 2 * DT) {
+                vlo[r] = pv_read(u, (i + kVR) / DT, (i + kVR) % DT, 0);
+                vhi[r] = pv_read(u, (i + kVR) / DT, (i + kVR) % DT, 1);
+            }
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) mfma_a(acc[dt * HT + ht], va, pb[ht]);
+        };
+        // rescale of the accumulators for unit u when a running max moved (rare);
+        // tile by tile through VGPRs so that at most one tile is out of the
+        // accumulation registers at a time
+        auto rescale = [&](int u) {
+            const u32x4_t fl = *(const __attribute__((address_space(3))) u32x4_t *)(
+                uintptr_t)lds_offset(&s_flag[u & 1][0]);
+            if (__builtin_expect((fl[0] | fl[1] | fl[2] | fl[3]) != 0, 0)) {
+                float alpha[HT];
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht)
+                    alpha[ht] = fl[ht] != 0 ? s_alpha[u & 1][ht * kHeads + l31] : 1.0f;
+                acc_fence(acc);
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    f32x16_t xv = acc[t];
+                    asm volatile("" : "+v"(xv));
+                    xv *= alpha[t % HT];
+                    asm volatile("" : "+v"(xv));
+                    acc[t] = xv;
+                    asm volatile("" : "+a"(acc[t]));
+                }
+                asm volatile("s_nop 2" ::: "memory");
+            }
+        };
+
+        // ---- the software pipeline --------------------------------------------
+        // Step u: the value products of unit u beside the score products of
+        // unit u + 1, then the softmax of unit u + 1 beside the rest of unit
+        // u's value products.  Unit u + 3 streams into the regions units
+        // u - 1 (main) and u (RoPE) used.  One barrier per step: every wave's
+        // rows of unit u + 1 have landed, every wave's probabilities of unit u
+        // are in buffer u & 1, and every wave is done with step u - 1.  Past
+        // the segment's last unit the score chain runs over stale LDS and its
+        // tokens are all masked (one code path for every step keeps the
+        // register allocation in budget).
+        const char *pool = reinterpret_cast<const char *>(latent);
+        for (int u = 0; u < 3; ++u) {
+            const bool live = u < nunits;
+            if (live) refill_ids(u);
+            const char *src = live ? unit_src(u, __builtin_amdgcn_readfirstlane(unit_id(u))) : pool;
+            for (int k = 0; k < kPer; ++k) issue_row(u, src, k, live);
+        }
+        {  // unit 0's scores and softmax, alone
+            // units 1 and 2 (loads issued after unit 0's; vmcnt holds at most
+            // 63, and waiting for fewer outstanding loads is safe)
+            wait_vmem<(2 * kPer < 63 ? 2 * kPer : 63)>();
+            __syncthreads();
+            f32x16_t s;
+            score_prefetch(0);
+            score_steps(s, 0, 0, kKSteps, [](int) {});
+#pragma unroll
+            for (int piece = 0; piece < 12; ++piece) softmax_piece(s, 0, piece);
+        }
+
+        for (int u = 0; u < nunits; ++u) {
+            const int u1 = u + 1, u3 = u + 3;
+            const bool has_u3 = u3 < nunits;
+            wait_vmem<kPer>();  // this wave's rows of unit u + 1 have landed (unit u + 2's may not)
+            const int id3 = has_u3 ? unit_id(u3) : 0;
+            __syncthreads();
+            if (has_u3) refill_ids(u3);
+            const char *src3 = has_u3 ? unit_src(u3, __builtin_amdgcn_readfirstlane(id3)) : pool;
+            rescale(u);
+            score_prefetch(u1);
+            value_prefetch(u);
+            // value steps j < kVA beside the 36 score products of unit u + 1
+            // (step j before product ks with j * 36 / kVA in [ks, ks + 1)), then
+            // the softmax of unit u + 1 in 12 pieces beside the other kNV - kVA
+            // and this wave's DMA rows of unit u + 3
+            f32x16_t s;
+            score_steps(s, u1, 0, kKSteps, [&](int ks) {
+#pragma unroll
+                for (int j = (ks * kVA + kKSteps - 1) / kKSteps;
+                     j < ((ks + 1) * kVA + kKSteps - 1) / kKSteps; ++j)
+                    value_step(u, j);
+            });
+            // (the DMA rows of unit u + 3 go beside the softmax: rows k with
+            // k * 12 / kPer in [piece, piece + 1), each exactly once; beside the
+            // score products they overflowed the register budget)
+            constexpr int kVB = kNV - kVA;
+#pragma unroll
+            for (int piece = 0; piece < 12; ++piece) {
+                softmax_piece(s, u1, piece);
+#pragma unroll
+                for (int k = (piece * kPer + 11) / 12; k < ((piece + 1) * kPer + 11) / 12; ++k)
+                    issue_row(u3, src3, k, has_u3);
+#pragma unroll
+                for (int j = (piece * kVB + 11) / 12; j < ((piece + 1) * kVB + 11) / 12; ++j)
+                    value_step(u, kVA + j);
+            }
         }
 
         // ---- this segment's partial -----------------------------------------
-        // Slot blockIdx.x + b: (max, sum) per head from the score waves; the
+        // Slot blockIdx.x: (max, sum) per head from the score waves; the
         // accumulator tiles of this wave in register order, so every store
         // writes 1 KB of consecutive bytes.
         const float l_tot = l_run + __shfl_xor(l_run, 32);
         acc_fence(acc);
         {
-            const int64_t slot = static_cast<int64_t>(blockIdx.x) + b;
+            const int64_t slot = blockIdx.x;
             if (hk == 0) ws_ml[slot * (HT * kHeads) + head] = make_float2(m_run, l_tot);
             f32x4_t *dst = reinterpret_cast<f32x4_t *>(ws_acc) + slot * (16 * HT * 4 * kWave) +
                            (DT * wave) * (HT * 4 * kWave) + lane;
@@ -505,16 +618,6 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
                             f32x4_t{t[4 * qd], t[4 * qd + 1], t[4 * qd + 2], t[4 * qd + 3]};
                     }
         }
-
-        x += nblk;
-        if (x >= x1) break;
-        blk_start = 0;
-        do {
-            ++b;
-            nbb = (context_lens[b] + kLBS - 1) / kLBS;
-        } while (nbb == 0);
-        wait_lds();
-        __syncthreads();  // every wave is done with this segment's LDS and ids
     }
 }
 
@@ -527,7 +630,7 @@ template <int NW>
 __global__ __launch_bounds__(NW *kWave) void latent_reduce_kernel(
     uint16_t *__restrict__ out, const float *__restrict__ ws_acc, const float2 *__restrict__ ws_ml,
     const int32_t *__restrict__ ws_prefix, const int32_t *__restrict__ context_lens,
-    int num_seqs, int num_heads, int waves) {
+    int num_seqs, int num_heads) {
     constexpr int HT = NW;
     const int dg = blockIdx.x;
     const int b = blockIdx.y;
@@ -543,11 +646,9 @@ __global__ __launch_bounds__(NW *kWave) void latent_reduce_kernel(
         for (int qd = 0; qd < 4; ++qd) *reinterpret_cast<uint2 *>(o + 8 * qd) = make_uint2(0, 0);
         return;
     }
-    const int share = stream_share(ws_prefix[num_seqs], waves);
-    const int seg_lo = ws_prefix[b];
-    const int w0 = seg_lo / share;
-    const int n = (seg_lo + nb - 1) / share - w0 + 1;  // partial slots of this sequence
-    const int64_t first = static_cast<int64_t>(w0) + b;  // slot of w0
+    // the sequence's parts: slots ws_prefix[b] .. ws_prefix[b + 1] - 1
+    const int64_t first = ws_prefix[b];
+    const int n = ws_prefix[b + 1] - ws_prefix[b];
 
     float M = kNegInf;
     for (int p = 0; p < n; ++p) M = fmaxf(M, ws_ml[(first + p) * (HT * kHeads) + head].x);
@@ -578,7 +679,9 @@ pa_status enqueue_latent(const DecodeShape &s, const DecodeArgs &a, const Decode
     float2 *ml = reinterpret_cast<float2 *>(ws + p.ml_offset);
     int32_t *prefix = reinterpret_cast<int32_t *>(ws + p.prefix_offset);
     const auto kernel = latent_partition_kernel<NW>;
-    const int waves = stream_waves(kernel, NW * kWave, 1, kLatentWavesMax);
+    // one work-group per resident slot, and at least one per sequence (each
+    // work-group streams a part of one sequence)
+    const int waves = std::max(stream_waves(kernel, NW * kWave, 1, kLatentWavesMax), s.num_seqs);
     hipLaunchKernelGGL(kernel, dim3(waves), dim3(NW * kWave), 0, stream, acc, ml, prefix,
                        static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k_cache),
                        a.block_tables, a.context_lens, scale_log2, s.num_seqs, s.num_q_heads,
@@ -587,7 +690,7 @@ pa_status enqueue_latent(const DecodeShape &s, const DecodeArgs &a, const Decode
     if (st != PA_OK) return st;
     hipLaunchKernelGGL(latent_reduce_kernel<NW>, dim3(kDimTiles, s.num_seqs), dim3(NW * kWave), 0,
                        stream, static_cast<uint16_t *>(a.out), acc, ml, prefix, a.context_lens,
-                       s.num_seqs, s.num_q_heads, waves);
+                       s.num_seqs, s.num_q_heads);
     return hip_status(hipGetLastError(), why, "latent reduce launch");
 }
 

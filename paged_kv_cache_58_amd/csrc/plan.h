@@ -111,9 +111,11 @@ constexpr int kMaxColTiles = 4;
 //    each holding the G heads of one KV group; plus the per-sequence block
 //    prefix sums (num_seqs + 1 int32) the partition kernel leaves for the
 //    reduce.
-//  * latent: stream-K as well, with one work-group per CU; slots =
-//    kLatentWavesMax + num_seqs, each holding latent_waves(num_q_heads) * 32
-//    heads (the query heads, padded).  There the accumulator of a slot is
+//  * latent: each sequence cut into parts of near-equal size, one
+//    work-group per part (at least one per CU, at least one per sequence);
+//    slots = kLatentWavesMax + num_seqs (more than the work-groups), each
+//    holding latent_waves(num_q_heads) * 32 heads (the query heads,
+//    padded); the prefix array holds the parts per sequence (num_seqs + 1).  There the accumulator of a slot is
 //    stored in the partition kernel's register order, HT = latent_waves
 //    head tiles: float4 index ((dt * HT + ht) * 4 + qd) * 64 + lane holds
 //    dims 32 dt + 8 qd + 4 (lane >> 5) .. + 3 of head 32 ht + (lane & 31).

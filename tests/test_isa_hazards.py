@@ -1,4 +1,6 @@
-"""Static check of the matrix-core hazards in the latent decode kernel.
+"""Static checks of hazards that the compiler does not cover in inline assembly.
+
+1. Matrix-core hazards in the latent decode kernel.
 
 The latent kernel issues its v_mfma instructions from inline assembly (to pin
 the output accumulators to the accumulation registers), so the compiler's
@@ -16,6 +18,13 @@ code, the two hazards the source relies on avoiding:
 Wait states are counted as one per instruction, s_nop N as N + 1.  The scan
 stops at labels and branches, so it covers each basic block on its own; the
 kernel keeps every product chain and its fence inside one block.
+
+2. The LDS-DMA loads of every kernel (global_load_lds, issued from inline
+assembly with an SGPR base): a vector memory instruction may read an SGPR
+only 5 wait states after a VALU instruction wrote it.  The compiler inserts
+that for its own loads, not inside asm; it bites when register pressure makes
+the compiler spill a base pointer to a VGPR lane and reload it with
+v_readlane right before the load (a stale base is an out-of-bounds address).
 """
 from __future__ import annotations
 
@@ -23,6 +32,7 @@ import os
 import re
 import shutil
 import subprocess
+import sys
 
 import pytest
 
@@ -176,3 +186,86 @@ def test_checker_catches_planted_hazards():
            ("s_nop", "7"), ("s_nop", "7"), ("s_nop", "7"), ("s_nop", "7"),
            ("v_add_f32_e32", "v30, v10, v11")]]
     assert not check(ok)
+
+
+# ---- 2. VALU-written SGPR read by an LDS-DMA load ---------------------------
+
+VALU_SGPR_TO_VMEM = 5
+_SREG = re.compile(r"\bs\[(\d+):(\d+)\]|\bs(\d+)\b")
+
+
+def _sregs(text: str) -> set[int]:
+    out = set()
+    for m in _SREG.finditer(text):
+        if m.group(1):
+            out.update(range(int(m.group(1)), int(m.group(2)) + 1))
+        else:
+            out.add(int(m.group(3)))
+    return out
+
+
+def sgpr_dma_hazards(lines: list[str]) -> list[str]:
+    """Each global_load_lds whose SGPR operands a VALU instruction wrote fewer
+    than VALU_SGPR_TO_VMEM wait states before (within its basic block)."""
+    problems = []
+    text = [l.split(";", 1)[0].strip() for l in lines]
+    for i, l in enumerate(text):
+        if not l.startswith("global_load_lds"):
+            continue
+        ops = l.split(None, 1)[1] if " " in l else ""
+        need = _sregs(ops.split(",", 1)[1] if "," in ops else "")
+        ws = 0
+        for j in range(i - 1, -1, -1):
+            p = text[j]
+            if not p:
+                continue
+            if p.endswith(":") or p.startswith(".") or p.startswith("s_cbranch") or p == "s_branch":
+                break
+            if ws >= VALU_SGPR_TO_VMEM:
+                break
+            mn = p.split()[0]
+            if _is_valu(mn) and " " in p and _sregs(p.split(None, 1)[1].split(",", 1)[0]) & need:
+                problems.append(f"{p} -> {l} after {ws} wait states")
+            ws += _wait_states(mn, p.split(None, 1)[1] if " " in p else "")
+    return problems
+
+
+@pytest.fixture(scope="module")
+def all_kernel_asm(tmp_path_factory):
+    if not os.path.exists(HIPCC):
+        pytest.skip("hipcc not found")
+    sys.path.insert(0, ROOT)
+    from paged_kv_cache_58_amd import build as B
+    out_dir = tmp_path_factory.mktemp("isa_all")
+    procs = {}
+    for src in B.SOURCES:
+        if src in B.HOST_ONLY or not src.endswith(".hip"):
+            continue
+        out = out_dir / (src + ".s")
+        cmd = [HIPCC, *B.DEVICE, *B.COMMON, *B.EXTRA.get(src, []), "-x", "hip", "-S",
+               "--cuda-device-only", os.path.join(B.CSRC, src), "-o", str(out)]
+        procs[src] = (subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE), out)
+    asm = {}
+    for src, (p, out) in procs.items():
+        _, err = p.communicate()
+        assert p.returncode == 0, err.decode()
+        asm[src] = out.read_text()
+    return asm
+
+
+def test_lds_dma_sgpr_operands_settled(all_kernel_asm):
+    assert any("global_load_lds_dwordx4" in a for a in all_kernel_asm.values())
+    problems = []
+    for src, text in all_kernel_asm.items():
+        problems += [f"{src}: {p}" for p in sgpr_dma_hazards(text.splitlines())]
+    assert not problems, "\n".join(problems[:20])
+
+
+def test_sgpr_checker_catches_planted_hazard():
+    bad = ["v_readlane_b32 s7, v248, 26", "s_mov_b32 m0, 0x25400",
+           "global_load_lds_dword v0, s[6:7]"]
+    assert sgpr_dma_hazards(bad)
+    ok = ["v_readlane_b32 s7, v248, 26", "s_nop 4", "global_load_lds_dword v0, s[6:7]"]
+    assert not sgpr_dma_hazards(ok)
+    salu = ["s_add_u32 s6, s6, s8", "global_load_lds_dwordx4 v1, s[6:7] nt"]
+    assert not sgpr_dma_hazards(salu)
