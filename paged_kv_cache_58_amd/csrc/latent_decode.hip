@@ -199,68 +199,86 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
     const bool head_ok = head < num_heads;
 
     // ---- this work-group's part: a sequence-aligned split ------------------
-    // Sequence b (nb_b blocks) is cut into k_b = ceil(nb_b / P) parts of
-    // near-equal size, P the smallest part size for which every part gets a
-    // work-group (sum of k_b <= gridDim.x; the host launches at least one
-    // work-group per sequence).  Work-group j takes part j - K_b of the
-    // sequence b with K_b <= j < K_b + k_b, K_b the number of parts of the
-    // sequences before b, so each work-group streams one segment of one
-    // sequence: a change of segment inside a work-group (partial store, q
-    // reload, refilling the ring) costs about as much as a dozen units.  Its
-    // partial goes to slot j; work-group 0 stores K_b (num_seqs + 1 entries)
-    // for the reduce.
-    auto seq_blocks = [&](int bb) {
-        return bb < num_seqs ? (context_lens[bb] + kLBS - 1) / kLBS : 0;
+    // Sequence b (nu_b = ceil(ctx_b / 32) units of 32 tokens) is cut into
+    // k_b = ceil(nu_b / P) parts of near-equal size, P the smallest part size
+    // for which every part gets a work-group (sum of k_b <= gridDim.x; the
+    // host launches at least one work-group per sequence).  Work-group j
+    // takes part j - K_b of the sequence b with K_b <= j < K_b + k_b, K_b the
+    // number of parts of the sequences before b, so each work-group streams
+    // one stretch of one sequence: a change of segment inside a work-group
+    // (partial store, q reload, refilling the ring) costs about as much as a
+    // dozen units, and units rather than 64-token blocks keep the parts
+    // within one unit of each other.  Its partial goes to slot j; work-group
+    // 0 stores K_b (num_seqs + 1 entries) for the reduce.  The unit counts of
+    // the first 256 sequences stay in registers for the search.
+    auto seq_units = [&](int bb) {
+        return bb < num_seqs ? (context_lens[bb] + kUnitTok - 1) / kUnitTok : 0;
     };
-    int total = 0, most = 0;  // blocks of all sequences; of the longest
-    for (int base = 0; base < num_seqs; base += kWave) {
-        const int nb = seq_blocks(base + lane);
-        total += __builtin_amdgcn_readlane(wave_incl_scan(nb, lane), kWave - 1);
-        int m = nb;
+    constexpr int kCached = 4;
+    int nu_c[kCached];
+#pragma unroll
+    for (int r = 0; r < kCached; ++r) nu_c[r] = seq_units(r * kWave + lane);
+    // f(first sequence of the chunk, this lane's unit count) for every chunk of 64 sequences
+    auto each_chunk = [&](auto &&f) {
+#pragma unroll
+        for (int r = 0; r < kCached; ++r)
+            if (r * kWave < num_seqs) f(r * kWave, nu_c[r]);
+        for (int base = kCached * kWave; base < num_seqs; base += kWave) f(base, seq_units(base + lane));
+    };
+    auto wave_sum = [&](int v) { return __builtin_amdgcn_readlane(wave_incl_scan(v, lane), kWave - 1); };
+    int total = 0, most = 0;  // units of all sequences; of the longest
+    each_chunk([&](int, int nu) {
+        total += wave_sum(nu);
+        int m = nu;
 #pragma unroll
         for (int d = 1; d < kWave; d <<= 1) m = max(m, __shfl_xor(m, d));
         most = max(most, m);
-    }
+    });
     if (total == 0) return;  // every context empty: the reduce writes zeros
     const int grid = static_cast<int>(gridDim.x);
-    auto parts = [&](int P) {  // sum over the sequences of ceil(nb_b / P)
+    auto parts = [&](int P) {  // sum over the sequences of ceil(nu_b / P)
         int k_all = 0;
-        for (int base = 0; base < num_seqs; base += kWave) {
-            const int nb = seq_blocks(base + lane);
-            k_all += __builtin_amdgcn_readlane(wave_incl_scan((nb + P - 1) / P, lane), kWave - 1);
-        }
+        each_chunk([&](int, int nu) { k_all += wave_sum((nu + P - 1) / P); });
         return k_all;
     };
-    // parts(P) only falls as P grows, and parts(most) <= num_seqs <= grid
-    int lo = max(1, (total + grid - 1) / grid), hi = max(most, lo);
+    // parts(P) only falls as P grows; parts(most) <= num_seqs <= grid, and
+    // parts(P) <= total / P + num_seqs, so P = ceil(total / (grid - num_seqs))
+    // fits too when grid > num_seqs
+    int lo = max(1, (total + grid - 1) / grid), hi = most;
+    if (grid > num_seqs) hi = min(hi, (total + grid - num_seqs - 1) / (grid - num_seqs));
+    hi = max(hi, lo);
     while (lo < hi) {
         const int mid = (lo + hi) / 2;
         if (parts(mid) <= grid) hi = mid;
         else lo = mid + 1;
     }
     const int P = lo;
-    int b = -1, part = 0, k_b = 1, nb_b = 0;
-    for (int base = 0, carry = 0; base < num_seqs; base += kWave) {
+    int b = -1, part = 0, k_b = 1, nu_b = 0, carry = 0;
+    each_chunk([&](int base, int nu) {
         const int bb = base + lane;
-        const int nb = seq_blocks(bb);
-        const int k = (nb + P - 1) / P;
+        const int k = (nu + P - 1) / P;
         const int incl = wave_incl_scan(k, lane);
         if (blockIdx.x == 0 && wave == 0 && bb < num_seqs) ws_prefix[bb] = carry + incl - k;
-        const uint64_t hit = __builtin_amdgcn_ballot_w64(bb < num_seqs && carry + incl > static_cast<int>(blockIdx.x));
+        const uint64_t hit =
+            __builtin_amdgcn_ballot_w64(bb < num_seqs && carry + incl > static_cast<int>(blockIdx.x));
         if (b < 0 && hit != 0) {
             const int f = __builtin_ctzll(hit);
             b = base + f;
             k_b = __builtin_amdgcn_readlane(k, f);
-            nb_b = __builtin_amdgcn_readlane(nb, f);
+            nu_b = __builtin_amdgcn_readlane(nu, f);
             part = static_cast<int>(blockIdx.x) - (carry + __builtin_amdgcn_readlane(incl, f) - k_b);
         }
         carry += __builtin_amdgcn_readlane(incl, kWave - 1);
-        if (blockIdx.x == 0 && wave == 0 && lane == 0 && base + kWave >= num_seqs)
-            ws_prefix[num_seqs] = carry;
-    }
+    });
+    if (blockIdx.x == 0 && tid == 0) ws_prefix[num_seqs] = carry;
     if (b < 0) return;  // a work-group past the last part (uniform)
-    const int blk_start = part * nb_b / k_b;
-    const int seg_blocks = (part + 1) * nb_b / k_b - blk_start;
+    // this part: units [seg_u0, seg_u1) of sequence b; unit u of the segment
+    // is half (h0 + u) & 1 of block blk_start + ((h0 + u) >> 1)
+    const int seg_u0 = part * nu_b / k_b;
+    const int seg_u1 = (part + 1) * nu_b / k_b;
+    const int blk_start = seg_u0 >> 1;
+    const int h0 = seg_u0 & 1;
+    const int seg_blocks = ((seg_u1 - 1) >> 1) - blk_start + 1;
 
     // the main regions start zeroed (rows past a context are never fetched)
     for (int i = tid; i < kSlots * kUnitMainB / 16; i += NW * kWave)
@@ -303,7 +321,7 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
     constexpr uint32_t kPBuf = HT * 2 * kWave * 16;
 
     {
-        // ======== the segment: sequence b, blocks [blk_start, blk_start + nblk) ========
+        // ======== the segment: sequence b, units [seg_u0, seg_u1) ========
         const int nblk = seg_blocks;
         const int ctx = context_lens[b];
         const int32_t *bt_row = block_tables + static_cast<int64_t>(b) * max_blocks;
@@ -340,13 +358,13 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
 #pragma unroll
         for (int t = 0; t < 16; ++t) acc[t] = f32x16_t{};
 
-        // Units of this segment: 32-token halves of its blocks that hold at
-        // least one context token (only a sequence's last block can end
-        // early, so unit u is half u & 1 of block u >> 1).  Tokens at or past
-        // seg_lim belong to no unit of the segment.
-        const int seg_tok0 = blk_start * kLBS;
-        const int seg_lim = min(ctx, (blk_start + nblk) * kLBS);
-        const int nunits = (seg_lim - seg_tok0 + kUnitTok - 1) / kUnitTok;
+        // Units of this segment: 32-token halves of blocks, each holding at
+        // least one context token (unit u is half (h0 + u) & 1 of block
+        // blk_start + ((h0 + u) >> 1)).  Tokens at or past seg_lim belong to
+        // no unit of the segment.
+        const int seg_tok0 = seg_u0 * kUnitTok;
+        const int seg_lim = min(ctx, seg_u1 * kUnitTok);
+        const int nunits = seg_u1 - seg_u0;
 
         // DMA of unit u: this wave's rows i = wave + NW k, k < kPer, of the
         // unit's 36 (32 main rows, 4 groups of 8 RoPE rows).  A main row at or
@@ -361,7 +379,7 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
         constexpr int kPer = (kDmaPerUnit + NW - 1) / NW;
         auto unit_src = [&](int u, int pb) {
             return reinterpret_cast<const char *>(latent) + static_cast<int64_t>(pb) * kBlockB +
-                   (u & 1) * kUnitTok * kRowB;
+                   ((h0 + u) & 1) * kUnitTok * kRowB;
         };
         // live = false (a unit past the segment's last): the same kPer loads,
         // from the pool's first row into s_sink, so every step has kPer loads.
@@ -384,11 +402,14 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
         // Block ids come in chunks of 64 through s_ids; wave 0 fetches chunk
         // c + 1 when the first unit of chunk c is issued.
         auto refill_ids = [&](int u) {
-            const int n = u >> 1;
-            if (wave == 0 && (u & 1) == 0 && (n & (kWave - 1)) == 0 && n > 0 && n + kWave < nblk)
+            const int n = (h0 + u) >> 1;
+            if (wave == 0 && ((h0 + u) & 1) == 0 && (n & (kWave - 1)) == 0 && n > 0 && n + kWave < nblk)
                 fetch_ids((n >> 6) + 1);
         };
-        auto unit_id = [&](int u) { return s_ids[((u >> 1) >> 6) & 1][(u >> 1) & (kWave - 1)]; };
+        auto unit_id = [&](int u) {
+            const int n = (h0 + u) >> 1;  // block of unit u, from blk_start
+            return s_ids[(n >> 6) & 1][n & (kWave - 1)];
+        };
 
         // A operand of score k-step ks of unit u (the compiler keeps the lane's
         // 12 row offsets live; the V^T reads below recompute theirs at each use,
