@@ -489,7 +489,7 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
                 // pieces 4..11: probabilities 2 v, 2 v + 1 of k-step v >> 2
                 const int v = piece - 4, sv = v >> 2, e = v & 3;
                 w4[e] = pack_bf16(exp2_fast(s[2 * v] - m_run), exp2_fast(s[2 * v + 1] - m_run));
-                l_run += bf16_lo(w4[e]) + bf16_hi(w4[e]);
+                l_run = dot2_bf16(w4[e], 0x3F803F80u, l_run);  // + both rounded values (bf16 1, 1)
                 if (e == 3)
                     *(__attribute__((address_space(3))) u32x4_t *)(uintptr_t)(
                         p_lds + (u & 1) * kPBuf + (wave * 2 + sv) * kWave * 16) =
