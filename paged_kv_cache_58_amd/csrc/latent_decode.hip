@@ -188,6 +188,7 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
     __shared__ __attribute__((aligned(16))) int32_t s_flag[2][4];  // head tile ht rescaled in unit u
     __shared__ __attribute__((aligned(16))) int32_t s_ids[2][kWave];
     __shared__ __attribute__((aligned(16))) uint4 s_sink[kWave];  // target of padding loads
+    __shared__ float s_l[HT * kHeads];  // each head's running sum, for the partial
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -617,36 +618,54 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
             }
         }
 
-        // ---- this segment's partial -----------------------------------------
-        // Slot blockIdx.x: (max, sum) per head from the score waves; the
-        // accumulator tiles of this wave in register order, so every store
-        // writes 1 KB of consecutive bytes.
+        // ---- this part's partial ---------------------------------------------
+        // Slot blockIdx.x: (max, sum) per head in fp32 from the score waves,
+        // and the part's output normalised by its own sum, acc / l, rounded to
+        // bf16 (as split-KV kernels commonly hand their partial outputs over in
+        // the output type): half the bytes of fp32 accumulators, for one more
+        // rounding of the order of the output's own.  The tiles of this wave
+        // go out in register order, so every store writes 1 KB of consecutive
+        // bytes.
         const float l_tot = l_run + __shfl_xor(l_run, 32);
+        if (hk == 0) s_l[head] = l_tot;
+        __syncthreads();  // every head's sum is in s_l
         acc_fence(acc);
         {
             const int64_t slot = blockIdx.x;
             if (hk == 0) ws_ml[slot * (HT * kHeads) + head] = make_float2(m_run, l_tot);
-            f32x4_t *dst = reinterpret_cast<f32x4_t *>(ws_acc) + slot * (16 * HT * 4 * kWave) +
-                           (DT * wave) * (HT * 4 * kWave) + lane;
+            u32x4_t *dst = reinterpret_cast<u32x4_t *>(ws_acc) + slot * (16 * HT * 2 * kWave) +
+                           (DT * wave) * (HT * 2 * kWave) + lane;
+            float inv[HT];
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                const float l = s_l[ht * kHeads + l31];
+                inv[ht] = l > 0.f ? 1.0f / l : 0.f;
+            }
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                 for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-                    for (int qd = 0; qd < 4; ++qd) {
+                    for (int h = 0; h < 2; ++h) {
                         const f32x16_t &t = acc[dt * HT + ht];
-                        dst[((dt * HT + ht) * 4 + qd) * kWave] =
-                            f32x4_t{t[4 * qd], t[4 * qd + 1], t[4 * qd + 2], t[4 * qd + 3]};
+                        const float r = inv[ht];
+                        dst[((dt * HT + ht) * 2 + h) * kWave] = u32x4_t{
+                            pack_bf16(t[8 * h] * r, t[8 * h + 1] * r),
+                            pack_bf16(t[8 * h + 2] * r, t[8 * h + 3] * r),
+                            pack_bf16(t[8 * h + 4] * r, t[8 * h + 5] * r),
+                            pack_bf16(t[8 * h + 6] * r, t[8 * h + 7] * r)};
                     }
         }
     }
 }
 
-// Log-sum-exp merge of a sequence's partial slots (the same merge rule as the
-// grouped path), reading the register-ordered tiles: work-group (dim tile
-// dg, b) writes dims 32 dg .. + 31 of every head; thread t = 64 ht + lane
-// always sees head 32 ht + (lane & 31), and float4 qd of its tile holds dims
-// 32 dg + 8 qd + 4 (lane >> 5) .. + 3.
+// Log-sum-exp merge of a sequence's parts, O = sum_p 2^(m_p - M) l_p O_p /
+// sum_p 2^(m_p - M) l_p (the merge rule of the grouped path, with each part's
+// output already divided by its l_p), reading the register-ordered bf16 tiles:
+// work-group (dim tile dg, b) writes dims 32 dg .. + 31 of every head; thread
+// t = 64 ht + lane always sees head 32 ht + (lane & 31), and 16-byte half h
+// of its tile holds dims 32 dg + 8 qd + 4 (lane >> 5) .. + 3 for qd = 2 h,
+// 2 h + 1.
 template <int NW>
 __global__ __launch_bounds__(NW *kWave) void latent_reduce_kernel(
     uint16_t *__restrict__ out, const float *__restrict__ ws_acc, const float2 *__restrict__ ws_ml,
@@ -671,18 +690,27 @@ __global__ __launch_bounds__(NW *kWave) void latent_reduce_kernel(
     const int64_t first = ws_prefix[b];
     const int n = ws_prefix[b + 1] - ws_prefix[b];
 
+    // part p holds its normalised output O_p (bf16) and (m_p, l_p): the merge
+    // weight is 2^(m_p - M) l_p
     float M = kNegInf;
     for (int p = 0; p < n; ++p) M = fmaxf(M, ws_ml[(first + p) * (HT * kHeads) + head].x);
     f32x4_t num[4] = {};
     float den = 0.f;
     for (int p = 0; p < n; ++p) {
         const float2 mp = ws_ml[(first + p) * (HT * kHeads) + head];
-        const float wgt = exp2_fast(mp.x - M);
-        den = fmaf(wgt, mp.y, den);
-        const f32x4_t *a = reinterpret_cast<const f32x4_t *>(ws_acc) +
-                           (first + p) * (16 * HT * 4 * kWave) + ((dg * HT + ht) * 4) * kWave + lane;
+        const float wgt = exp2_fast(mp.x - M) * mp.y;
+        den += wgt;
+        const u32x4_t *a = reinterpret_cast<const u32x4_t *>(ws_acc) +
+                           (first + p) * (16 * HT * 2 * kWave) + ((dg * HT + ht) * 2) * kWave + lane;
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd) num[qd] += wgt * a[qd * kWave];
+        for (int h = 0; h < 2; ++h) {
+            const u32x4_t v = a[h * kWave];  // dims 8 (2 h + i / 2) + 4 (lane >> 5) .. of this tile
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                num[2 * h + (i >> 1)][2 * (i & 1)] += wgt * bf16_lo(v[i]);
+                num[2 * h + (i >> 1)][2 * (i & 1) + 1] += wgt * bf16_hi(v[i]);
+            }
+        }
     }
 #pragma unroll
     for (int qd = 0; qd < 4; ++qd) {
