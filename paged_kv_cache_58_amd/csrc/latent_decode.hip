@@ -665,51 +665,75 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
 // work-group (dim tile dg, b) writes dims 32 dg .. + 31 of every head; thread
 // t = 64 ht + lane always sees head 32 ht + (lane & 31), and 16-byte half h
 // of its tile holds dims 32 dg + 8 qd + 4 (lane >> 5) .. + 3 for qd = 2 h,
-// 2 h + 1.
+// 2 h + 1.  The kernel is a few memory round trips long, so every load of a
+// batch of kBatch parts is issued before any is used (parts past the last
+// re-read the last one and weigh 0), and batches merge by the running max.
 template <int NW>
 __global__ __launch_bounds__(NW *kWave) void latent_reduce_kernel(
     uint16_t *__restrict__ out, const float *__restrict__ ws_acc, const float2 *__restrict__ ws_ml,
     const int32_t *__restrict__ ws_prefix, const int32_t *__restrict__ context_lens,
     int num_seqs, int num_heads) {
     constexpr int HT = NW;
+    constexpr int kBatch = 8;
     const int dg = blockIdx.x;
     const int b = blockIdx.y;
     const int t = threadIdx.x;
     const int ht = t / kWave, lane = t & (kWave - 1);
     const int head = ht * kHeads + (lane & 31);
     if (head >= num_heads) return;
-    const int nb = (context_lens[b] + kLBS - 1) / kLBS;
+    // the sequence's parts are slots ws_prefix[b] .. ws_prefix[b + 1] - 1; the
+    // prefix is read together with the length (it is in bounds, and written
+    // by the partition whenever some context is non-empty)
+    const int ctx = context_lens[b];
+    const int first = ws_prefix[b];
+    const int n = ws_prefix[b + 1] - first;
+    asm volatile("" ::"s"(ctx), "s"(first), "s"(n));  // one round trip for the three
     uint16_t *o = out + (static_cast<int64_t>(b) * num_heads + head) * kDV + 32 * dg +
                   4 * (lane >> 5);
-    if (nb <= 0) {  // empty context: O = 0
+    if (ctx <= 0) {  // empty context: O = 0
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) *reinterpret_cast<uint2 *>(o + 8 * qd) = make_uint2(0, 0);
         return;
     }
-    // the sequence's parts: slots ws_prefix[b] .. ws_prefix[b + 1] - 1
-    const int64_t first = ws_prefix[b];
-    const int n = ws_prefix[b + 1] - ws_prefix[b];
 
     // part p holds its normalised output O_p (bf16) and (m_p, l_p): the merge
     // weight is 2^(m_p - M) l_p
-    float M = kNegInf;
-    for (int p = 0; p < n; ++p) M = fmaxf(M, ws_ml[(first + p) * (HT * kHeads) + head].x);
+    float M = kNegInf, den = 0.f;
     f32x4_t num[4] = {};
-    float den = 0.f;
-    for (int p = 0; p < n; ++p) {
-        const float2 mp = ws_ml[(first + p) * (HT * kHeads) + head];
-        const float wgt = exp2_fast(mp.x - M) * mp.y;
-        den += wgt;
-        const u32x4_t *a = reinterpret_cast<const u32x4_t *>(ws_acc) +
-                           (first + p) * (16 * HT * 2 * kWave) + ((dg * HT + ht) * 2) * kWave + lane;
+    for (int p0 = 0; p0 < n; p0 += kBatch) {
+        float2 mp[kBatch];
+        u32x4_t v[kBatch][2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const u32x4_t v = a[h * kWave];  // dims 8 (2 h + i / 2) + 4 (lane >> 5) .. of this tile
+        for (int j = 0; j < kBatch; ++j) {
+            const int64_t slot = first + min(p0 + j, n - 1);
+            mp[j] = ws_ml[slot * (HT * kHeads) + head];
+            const u32x4_t *a = reinterpret_cast<const u32x4_t *>(ws_acc) +
+                               slot * (16 * HT * 2 * kWave) + ((dg * HT + ht) * 2) * kWave + lane;
+            v[j][0] = a[0];  // dims 8 (2 h + i / 2) + 4 (lane >> 5) .. of this tile, h = 0, 1
+            v[j][1] = a[kWave];
+        }
+        float bm = kNegInf;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                num[2 * h + (i >> 1)][2 * (i & 1)] += wgt * bf16_lo(v[i]);
-                num[2 * h + (i >> 1)][2 * (i & 1) + 1] += wgt * bf16_hi(v[i]);
-            }
+        for (int j = 0; j < kBatch; ++j)
+            if (p0 + j < n) bm = fmaxf(bm, mp[j].x);
+        if (bm > M) {  // the first batch, or a larger max: rescale what is merged
+            const float c = exp2_fast(M - bm);
+            den *= c;
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) num[qd] *= c;
+            M = bm;
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const float wgt = p0 + j < n && mp[j].y > 0.f ? exp2_fast(mp[j].x - M) * mp[j].y : 0.f;
+            den += wgt;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    num[2 * h + (i >> 1)][2 * (i & 1)] += wgt * bf16_lo(v[j][h][i]);
+                    num[2 * h + (i >> 1)][2 * (i & 1) + 1] += wgt * bf16_hi(v[j][h][i]);
+                }
         }
     }
 #pragma unroll
