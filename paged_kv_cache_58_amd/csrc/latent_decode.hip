@@ -170,7 +170,7 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
     constexpr int DT = kDimTiles / NW;  // output dim tiles per wave
     static_assert(DT * HT == 16, "16 accumulator tiles per wave");
     constexpr int kVR = 3;              // V^T operands read ahead
-    constexpr int kRA = 4;              // score A operands read ahead
+    constexpr int kRA = 3;              // score A operands read ahead
     constexpr int kNV = 2 * DT;         // value steps (of HT products) per unit
     // of them beside the score chain (half; a quarter with two waves, whose
     // wider value steps overflowed the registers there), the rest beside the softmax
@@ -369,35 +369,48 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
 
         // DMA of unit u: this wave's rows i = wave + NW k, k < kPer, of the
         // unit's 36 (32 main rows, 4 groups of 8 RoPE rows).  A main row at or
-        // past the context is not fetched: its load reads the unit's first
-        // row into s_sink instead (selected, not branched, so every wave has
-        // exactly kPer loads per unit in flight and the vmcnt waits below stay
-        // exact), and the slot keeps what it held, which is finite: the main
-        // regions start zeroed and later hold only fetched rows of the
-        // context.  The probabilities of those tokens are exactly 0, so they
-        // contribute exactly 0 (a NaN there would not).  RoPE rows only feed
-        // scores, which are masked.
+        // past the context goes into s_sink instead of the slot: only the
+        // destination is selected (not branched, so every wave has exactly
+        // kPer loads per unit in flight and the vmcnt waits below stay exact),
+        // and the source row still lies inside the unit's block.  The slot
+        // keeps what it held, which is finite: the main regions start zeroed
+        // and later hold only fetched rows of the context.  The probabilities
+        // of those tokens are exactly 0, so they contribute exactly 0 (a NaN
+        // there would not).  RoPE rows only feed scores, which are masked.
+        // A unit past the segment's last (not live) loads the same rows of the
+        // pool's first block into s_sink, so every step has kPer loads.
+        // Since wave < NW and NW k is a multiple of NW, swm(i) = (wave << 2) ^
+        // swm(NW k): one lane term serves every row of the wave, and the
+        // wave's row offset goes into the unit's source and destination.
         constexpr int kPer = (kDmaPerUnit + NW - 1) / NW;
-        auto unit_src = [&](int u, int pb) {
-            return reinterpret_cast<const char *>(latent) + static_cast<int64_t>(pb) * kBlockB +
-                   ((h0 + u) & 1) * kUnitTok * kRowB;
+        const uint32_t ln_w = static_cast<uint32_t>(lane) ^ (static_cast<uint32_t>(wave) << 2);
+        struct UnitDma {
+            const char *src;  // the unit's first row + wave rows
+            uint32_t dst;     // the unit's main slot + wave rows
+            int nfetch;       // rows of the unit in the context, minus wave (uniform)
+            bool live;
         };
-        // live = false (a unit past the segment's last): the same kPer loads,
-        // from the pool's first row into s_sink, so every step has kPer loads.
-        auto issue_row = [&](int u, const char *src, int k, bool live) {
-            const int i = wave + NW * k;
-            if (i >= kDmaPerUnit) return;
-            // recomputed per row rather than kept live across the loop
-            int ln = lane;
-            asm volatile("" : "+v"(ln));
-            if (i < kUnitTok) {  // main region: row i, lane = swizzled chunk
-                const bool fetch = live && i < ctx - (seg_tok0 + u * kUnitTok);  // uniform
-                dma16(src, fetch ? i * kRowB + ((ln ^ swm(i)) * 16) : ln * 16,
-                      fetch ? main_slot(u) + i * kMainRowB : lds_offset(s_sink));
-            } else {             // RoPE region: 8 rows x 8 chunks
-                const int t = 8 * (i - kUnitTok) + (ln >> 3);
-                dma16(src, live ? t * kRowB + (kMainChunks + ((ln & 7) ^ swr(t))) * 16 : ln * 16,
-                      live ? rope_slot(u) + (i - kUnitTok) * 1024 : lds_offset(s_sink));
+        const char *pool = reinterpret_cast<const char *>(latent);
+        auto unit_dma = [&](int u, bool live, int pb) {
+            UnitDma d;
+            d.src = (live ? pool + static_cast<int64_t>(pb) * kBlockB + ((h0 + u) & 1) * kUnitTok * kRowB
+                          : pool) + wave * kRowB;
+            d.dst = main_slot(u) + wave * kMainRowB;
+            d.nfetch = (live ? min(kUnitTok, ctx - (seg_tok0 + u * kUnitTok)) : 0) - wave;
+            d.live = live;
+            return d;
+        };
+        auto issue_row = [&](int u, const UnitDma &d, int k) {
+            if (NW * k >= kDmaPerUnit) return;  // (wave < NW: then i >= 36 too)
+            if (NW * k < kUnitTok) {            // main region: row i, lane = swizzled chunk
+                const uint32_t off =
+                    ((ln_w ^ static_cast<uint32_t>(swm(NW * k))) << 4) + NW * k * kRowB;
+                dma16(d.src, off, NW * k < d.nfetch ? d.dst + NW * k * kMainRowB : lds_offset(s_sink));
+            } else {                            // RoPE region: 8 rows x 8 chunks
+                const int r = wave + NW * k - kUnitTok;
+                const int t = 8 * r + (lane >> 3);
+                const uint32_t off = (t - wave) * kRowB + (kMainChunks + ((lane & 7) ^ swr(t))) * 16;
+                dma16(d.src, off, d.live ? rope_slot(u) + r * 1024 : lds_offset(s_sink));
             }
         };
         // Block ids come in chunks of 64 through s_ids; wave 0 fetches chunk
@@ -466,11 +479,18 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
             if (piece < 2) {
                 float lmax = piece == 0 ? kNegInf : bmax;
 #pragma unroll
-                for (int j = 8 * piece; j < 8 * piece + 8; ++j) {
-                    const int tk = tok0 + 8 * (j >> 2) + 4 * hk + (j & 3);
-                    s[j] = tk < seg_lim ? s[j] * scale_log2 : kNegInf;
-                    lmax = fmaxf(lmax, s[j]);
+                for (int j = 8 * piece; j < 8 * piece + 8; ++j) s[j] *= scale_log2;
+                // only a unit that reaches the segment's limit (its last, or
+                // one past it) holds tokens to mask (uniform)
+                if (__builtin_expect(tok0 + kUnitTok > seg_lim, 0)) {
+#pragma unroll
+                    for (int j = 8 * piece; j < 8 * piece + 8; ++j) {
+                        const int tk = tok0 + 8 * (j >> 2) + 4 * hk + (j & 3);
+                        s[j] = tk < seg_lim ? s[j] : kNegInf;
+                    }
                 }
+#pragma unroll
+                for (int j = 8 * piece; j < 8 * piece + 8; ++j) lmax = fmaxf(lmax, s[j]);
                 bmax = lmax;
             } else if (piece == 2) {
                 // the other 16 tokens of this head sit in lane ^ 32
@@ -561,12 +581,11 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
         // the segment's last unit the score chain runs over stale LDS and its
         // tokens are all masked (one code path for every step keeps the
         // register allocation in budget).
-        const char *pool = reinterpret_cast<const char *>(latent);
         for (int u = 0; u < 3; ++u) {
             const bool live = u < nunits;
             if (live) refill_ids(u);
-            const char *src = live ? unit_src(u, __builtin_amdgcn_readfirstlane(unit_id(u))) : pool;
-            for (int k = 0; k < kPer; ++k) issue_row(u, src, k, live);
+            const UnitDma d = unit_dma(u, live, live ? __builtin_amdgcn_readfirstlane(unit_id(u)) : 0);
+            for (int k = 0; k < kPer; ++k) issue_row(u, d, k);
         }
         {  // unit 0's scores and softmax, alone
             // units 1 and 2 (loads issued after unit 0's; vmcnt holds at most
@@ -587,7 +606,7 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
             const int id3 = has_u3 ? unit_id(u3) : 0;
             __syncthreads();
             if (has_u3) refill_ids(u3);
-            const char *src3 = has_u3 ? unit_src(u3, __builtin_amdgcn_readfirstlane(id3)) : pool;
+            const UnitDma d3 = unit_dma(u3, has_u3, __builtin_amdgcn_readfirstlane(id3));
             rescale(u);
             score_prefetch(u1);
             value_prefetch(u);
@@ -611,7 +630,7 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
                 softmax_piece(s, u1, piece);
 #pragma unroll
                 for (int k = (piece * kPer + 11) / 12; k < ((piece + 1) * kPer + 11) / 12; ++k)
-                    issue_row(u3, src3, k, has_u3);
+                    issue_row(u3, d3, k);
 #pragma unroll
                 for (int j = (piece * kVB + 11) / 12; j < ((piece + 1) * kVB + 11) / 12; ++j)
                     value_step(u, kVA + j);
