@@ -172,9 +172,10 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
     constexpr int kVR = 3;              // V^T operands read ahead
     constexpr int kRA = 3;              // score A operands read ahead
     constexpr int kNV = 2 * DT;         // value steps (of HT products) per unit
-    // of them beside the score chain (half; a quarter with two waves, whose
-    // wider value steps overflowed the registers there), the rest beside the softmax
-    constexpr int kVA = NW == 2 ? kNV / 4 : kNV / 2;
+    // of them beside the score chain, the rest beside the softmax: none with
+    // four waves (measured 1-2% faster than half), a quarter with two waves
+    // (whose wider value steps overflowed the registers there), half with one
+    constexpr int kVA = NW == 4 ? 0 : NW == 2 ? kNV / 4 : kNV / 2;
 
     // Ring: main regions (dims 0..511 of 32 rows) for units u % 4, RoPE
     // regions (dims 512..575) for units u % 3: while step u runs, unit u's
