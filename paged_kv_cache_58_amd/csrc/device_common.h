@@ -259,7 +259,12 @@ __global__ __launch_bounds__(kWave *W) void stream_reduce_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    const int nb = window_blocks(context_lens[b], window, block_size);
+    // the length and the prefix sums are read in one round trip (the prefix is
+    // in bounds, and written by the partition whenever a context is non-empty)
+    const int ctx = context_lens[b];
+    const int pre_all = ws_prefix[num_seqs], pre_b = ws_prefix[b];
+    asm volatile("" ::"s"(ctx), "s"(pre_all), "s"(pre_b));
+    const int nb = window_blocks(ctx, window, block_size);
     T *o = out + ((static_cast<int64_t>(b) * q_len + qi) * num_q_heads + h) * D + lane * DPL;
     float *lse_row = lse ? lse + (static_cast<int64_t>(b) * q_len + qi) * num_q_heads + h : nullptr;
 
@@ -277,15 +282,42 @@ __global__ __launch_bounds__(kWave *W) void stream_reduce_kernel(
     const int nchunks = num_kv_heads / team_heads;
     const int ch = g / team_heads;
     const int hw = g - ch * team_heads;
-    const int total = nchunks * ws_prefix[num_seqs];
+    const int total = nchunks * pre_all;
     const int share = stream_share(total, nshares);
-    const int seg_lo = nchunks * ws_prefix[b] + ch * nb;
+    const int seg_lo = nchunks * pre_b + ch * nb;
     const int w0 = seg_lo / share;
     const int n = (seg_lo + nb - 1) / share - w0 + 1;  // partial slots of this segment
     // row of slot w0 + b * NC + ch; consecutive slots are team_heads * C rows apart
     const int64_t first =
         ((static_cast<int64_t>(w0) + b * nchunks + ch) * team_heads + hw) * ncols + hh;
     const int64_t stride = static_cast<int64_t>(team_heads) * ncols;
+
+    // This wave merges slots p = wave + W j, j < nw, kBatch at a time; the
+    // first batch's loads (which need no weight) go out with the max pass, so
+    // a short segment costs one round trip after the prefix.
+    constexpr int kBatch = 8;
+    const int nw = n > wave ? (n - wave + W - 1) / W : 0;
+    float2 bml[kBatch];
+    float bacc[kBatch][DPL];
+    auto load_batch = [&](int j0) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int64_t r = first + static_cast<int64_t>(wave + W * min(j0 + j, nw - 1)) * stride;
+            bml[j] = ws_ml[r];
+            const float *a = ws_acc + r * D + lane * DPL;
+            if constexpr (DPL % 2 == 0) {
+#pragma unroll
+                for (int d = 0; d < DPL; d += 2) {
+                    const float2 v = *reinterpret_cast<const float2 *>(a + d);
+                    bacc[j][d] = v.x;
+                    bacc[j][d + 1] = v.y;
+                }
+            } else {
+                bacc[j][0] = a[0];
+            }
+        }
+    };
+    if (nw > 0) load_batch(0);
 
     float M = kNegInf;
     for (int p = tid; p < n; p += kWave * W) M = fmaxf(M, ws_ml[first + p * stride].x);
@@ -309,21 +341,16 @@ __global__ __launch_bounds__(kWave *W) void stream_reduce_kernel(
         if (lse_row && tid == 0) *lse_row = kNegInf;
         return;
     }
-    for (int p = wave; p < n; p += W) {
-        const int64_t r = first + p * stride;
-        const float2 mp = ws_ml[r];
-        const float wgt = exp2_fast(mp.x - M);
-        den = fmaf(wgt, mp.y, den);
-        const float *a = ws_acc + r * D + lane * DPL;
-        if constexpr (DPL % 2 == 0) {
+    for (int j0 = 0; j0 < nw; j0 += kBatch) {
+        if (j0 > 0) load_batch(j0);
 #pragma unroll
-            for (int d = 0; d < DPL; d += 2) {
-                const float2 v = *reinterpret_cast<const float2 *>(a + d);
-                num[d] = fmaf(wgt, v.x, num[d]);
-                num[d + 1] = fmaf(wgt, v.y, num[d + 1]);
+        for (int j = 0; j < kBatch; ++j) {
+            if (j0 + j < nw) {  // (past nw the batch re-read this wave's last slot)
+                const float wgt = exp2_fast(bml[j].x - M);
+                den = fmaf(wgt, bml[j].y, den);
+#pragma unroll
+                for (int d = 0; d < DPL; ++d) num[d] = fmaf(wgt, bacc[j][d], num[d]);
             }
-        } else {
-            num[0] = fmaf(wgt, a[0], num[0]);
         }
     }
     if constexpr (W > 1) {
