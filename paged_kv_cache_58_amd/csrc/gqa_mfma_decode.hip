@@ -245,14 +245,23 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
         bf16x8_t qb[NT][kMKSteps];
         // tokens below lim[ct] are visible to this lane's column of tile ct
         int lim[NT];
+        // Every q load is issued before any is settled (the empty asm makes the
+        // compiler wait for a load there, so settling each one after its own
+        // load would cost a memory round trip per load).
+        u32x4_t qv[NT][kMKSteps];
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
             const uint16_t *qr =
                 q + ((static_cast<int64_t>(b) * q_len + qi[ct]) * num_q_heads + g * group + hh[ct]) *
                         kMD + 8 * quad;
 #pragma unroll
+            for (int j = 0; j < kMKSteps; ++j) qv[ct][j] = *reinterpret_cast<const u32x4_t *>(qr + 32 * j);
+        }
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+#pragma unroll
             for (int j = 0; j < kMKSteps; ++j) {
-                u32x4_t v = *reinterpret_cast<const u32x4_t *>(qr + 32 * j);
+                u32x4_t v = qv[ct][j];
                 asm volatile("" : "+v"(v));
                 if (!live[ct]) v = u32x4_t{0u, 0u, 0u, 0u};
                 qb[ct][j] = __builtin_bit_cast(bf16x8_t, v);
