@@ -218,8 +218,16 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
     };
     constexpr int kCached = 4;
     int nu_c[kCached];
+    {
+        // every load first (clamped in bounds, num_seqs >= 1), so that they
+        // share one memory round trip, then the counts
+        int ctx_c[kCached];
 #pragma unroll
-    for (int r = 0; r < kCached; ++r) nu_c[r] = seq_units(r * kWave + lane);
+        for (int r = 0; r < kCached; ++r) ctx_c[r] = context_lens[min(r * kWave + lane, num_seqs - 1)];
+#pragma unroll
+        for (int r = 0; r < kCached; ++r)
+            nu_c[r] = r * kWave + lane < num_seqs ? (ctx_c[r] + kUnitTok - 1) / kUnitTok : 0;
+    }
     // f(first sequence of the chunk, this lane's unit count) for every chunk of 64 sequences
     auto each_chunk = [&](auto &&f) {
 #pragma unroll
