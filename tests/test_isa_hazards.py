@@ -1,6 +1,6 @@
 """Static checks of hazards that the compiler does not cover in inline assembly.
 
-1. Matrix-core hazards in the latent decode kernel.
+1. Matrix-core hazards in the latent decode kernel (2. LDS-DMA SGPR operands and 3. serialized loads, in every kernel, further down).
 
 The latent kernel issues its v_mfma instructions from inline assembly (to pin
 the output accumulators to the accumulation registers), so the compiler's
@@ -269,3 +269,52 @@ def test_sgpr_checker_catches_planted_hazard():
     assert not sgpr_dma_hazards(ok)
     salu = ["s_add_u32 s6, s6, s8", "global_load_lds_dwordx4 v1, s[6:7] nt"]
     assert not sgpr_dma_hazards(salu)
+
+
+# 3. Serialized loads.  An empty asm that takes a just-loaded value as an
+# operand makes the compiler wait for that load right there; with several
+# such loads in a row (one per q fragment, say) every load then costs a full
+# memory round trip before the next is issued.  Within a basic block, no
+# kernel may issue three or more global loads that way, each waited for
+# (vmcnt(0)) before the next one goes out.
+
+def serialized_load_chains(lines: list[str], n: int = 3) -> list[int]:
+    out, run, pending = [], 0, False
+    for l in lines:
+        t = l.split(";", 1)[0].strip()
+        if t.startswith(".LBB") or t.startswith("s_cbranch") or t == "s_branch" or t.startswith("s_branch "):
+            run, pending = 0, False
+            continue
+        if re.match(r"(global_load_dword|buffer_load_dword|flat_load_dword)", t):
+            if pending:
+                run = 0  # issued while another load was in flight: not serialized
+            pending = True
+        elif t.startswith("s_waitcnt") and "vmcnt(0)" in t and pending:
+            run += 1
+            pending = False
+            if run >= n:
+                out.append(run)
+    return out
+
+
+def test_no_serialized_load_chains(all_kernel_asm):
+    problems = []
+    for src, text in all_kernel_asm.items():
+        for m in re.finditer(r"^(_Z\w+):", text, re.M):
+            body = text[m.end():text.find(".Lfunc_end", m.end())].splitlines()
+            if serialized_load_chains(body):
+                problems.append(f"{src}: {m.group(1)}")
+    assert not problems, "\n".join(problems[:20])
+
+
+def test_chain_checker_catches_planted_chain():
+    serial = []
+    for k in range(4):
+        serial += [f"global_load_dwordx4 v[{4 * k}:{4 * k + 3}], v[0:1], off offset:{64 * k}",
+                   "s_waitcnt vmcnt(0)"]
+    assert serialized_load_chains(serial)
+    batched = [f"global_load_dwordx4 v[{4 * k}:{4 * k + 3}], v[0:1], off offset:{64 * k}"
+               for k in range(4)] + ["s_waitcnt vmcnt(3)", "s_waitcnt vmcnt(0)"]
+    assert not serialized_load_chains(batched)
+    split = serial[:2] + [".LBB0_3:"] + serial[2:4] + ["s_cbranch_scc1 .LBB0_4"] + serial[4:]
+    assert not serialized_load_chains(split)
