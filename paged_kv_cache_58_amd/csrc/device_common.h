@@ -188,10 +188,35 @@ __device__ __forceinline__ bool find_share(int sid, int nshares, int num_seqs, i
                                            const int32_t *__restrict__ context_lens,
                                            int32_t *__restrict__ ws_prefix, int lane,
                                            ShareSpan &sp, int window = 0, bool writer = true) {
+    // The block counts of the first kCached * 64 sequences are loaded once,
+    // every load before any is used (clamped in bounds, num_seqs >= 1), and
+    // serve both passes below: one memory round trip instead of one per
+    // chunk and pass.
+    constexpr int kCached = 4;
+    int nb_c[kCached];
+    {
+        int len_c[kCached];
+#pragma unroll
+        for (int r = 0; r < kCached; ++r) len_c[r] = context_lens[min(r * kWave + lane, num_seqs - 1)];
+#pragma unroll
+        for (int r = 0; r < kCached; ++r)
+            nb_c[r] = r * kWave + lane < num_seqs ? window_blocks(len_c[r], window, bs) : 0;
+    }
+    auto chunk_blocks = [&](int base) {  // this lane's block count in the chunk at base
+        const int bb = base + lane;
+        if (base < kCached * kWave) {
+            int v = nb_c[0];
+#pragma unroll
+            for (int r = 1; r < kCached; ++r)
+                if (base == r * kWave) v = nb_c[r];
+            return v;
+        }
+        return bb < num_seqs ? window_blocks(context_lens[bb], window, bs) : 0;
+    };
     int seq_blocks_total = 0;
     for (int base = 0; base < num_seqs; base += kWave) {
         const int bb = base + lane;
-        const int nb = bb < num_seqs ? window_blocks(context_lens[bb], window, bs) : 0;
+        const int nb = chunk_blocks(base);
         const int incl = wave_incl_scan(nb, lane);
         if (sid == 0 && writer && bb < num_seqs) ws_prefix[bb] = seq_blocks_total + incl - nb;
         seq_blocks_total += __builtin_amdgcn_readlane(incl, kWave - 1);
@@ -210,7 +235,7 @@ __device__ __forceinline__ bool find_share(int sid, int nshares, int num_seqs, i
     int cb = 0;
     for (int base = 0, carry = 0;; base += kWave) {
         const int bb = base + lane;
-        const int nb = bb < num_seqs ? window_blocks(context_lens[bb], window, bs) : 0;
+        const int nb = chunk_blocks(base);
         const int incl = wave_incl_scan(nb, lane);
         const bool past = bb < num_seqs &&
                           static_cast<int64_t>(segs) * (carry + incl) > sp.x0;
