@@ -30,17 +30,26 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
     const int32_t *__restrict__ slot_mapping, int64_t k_row_bytes, int64_t v_row_bytes) {
     using V = typename VecType<VEC>::type;
     const int64_t i = blockIdx.x;
-    const int32_t slot = slot_mapping[i];
-    if (slot < 0) return;  // -1: padding token, nothing to write
     const int nk = static_cast<int>(k_row_bytes / VEC);
     const int nv = static_cast<int>(v_row_bytes / VEC);
     const V *src_k = reinterpret_cast<const V *>(k + i * k_token_bytes);
+    const V *src_v = reinterpret_cast<const V *>(v + i * v_token_bytes);
+    // the token's first chunk of K and V is read before the slot is known
+    // (the source rows exist whatever the slot), so that both loads and the
+    // slot's share one memory round trip
+    const int e0 = threadIdx.x;
+    V k0{}, v0{};
+    if (e0 < nk) k0 = src_k[e0];
+    if (e0 < nv) v0 = src_v[e0];
+    const int32_t slot = slot_mapping[i];
+    if (slot < 0) return;  // -1: padding token, nothing to write
     V *dst_k = reinterpret_cast<V *>(k_cache + static_cast<int64_t>(slot) * k_row_bytes);
-    for (int e = threadIdx.x; e < nk; e += kAppendThreads) dst_k[e] = src_k[e];
+    if (e0 < nk) dst_k[e0] = k0;
+    for (int e = e0 + kAppendThreads; e < nk; e += kAppendThreads) dst_k[e] = src_k[e];
     if (nv > 0) {
-        const V *src_v = reinterpret_cast<const V *>(v + i * v_token_bytes);
         V *dst_v = reinterpret_cast<V *>(v_cache + static_cast<int64_t>(slot) * v_row_bytes);
-        for (int e = threadIdx.x; e < nv; e += kAppendThreads) dst_v[e] = src_v[e];
+        if (e0 < nv) dst_v[e0] = v0;
+        for (int e = e0 + kAppendThreads; e < nv; e += kAppendThreads) dst_v[e] = src_v[e];
     }
 }
 
