@@ -56,7 +56,7 @@ typedef enum pa_status {
     PA_ERR_NULL = 1,        /* a required pointer is NULL */
     PA_ERR_SHAPE = 2,       /* sizes inconsistent or out of range */
     PA_ERR_DTYPE = 3,       /* unknown dtype */
-    PA_ERR_UNSUPPORTED = 4, /* valid but outside the shapes this build runs */
+    PA_ERR_UNSUPPORTED = 4, /* valid but outside the shapes the library runs */
     PA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
     PA_ERR_HIP = 6,         /* the HIP runtime reported an error */
     PA_ERR_ALIGN = 7        /* a pointer or stride breaks the 16-byte alignment rule */
@@ -134,7 +134,7 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  *                  bytes, 256-byte aligned; its contents on entry do not matter
  *                  and on return are scratch.
  *
- * Shapes this build runs (anything else returns PA_ERR_UNSUPPORTED):
+ * Shapes the library runs (anything else returns PA_ERR_UNSUPPORTED):
  *   - head_dim_k == head_dim_v in {64, 128}, block_size 16,
  *     num_q_heads / num_kv_heads in {1, 2, 4, 8}, dtype PA_F32 or PA_BF16;
  *   - latent mode: head_dim_k 576, head_dim_v 512, num_kv_heads 1,
