@@ -175,6 +175,21 @@ def test_head_teams_do_not_change_result(dev, team, waves, monkeypatch):
     say(f"  {compare(d.decode(), oracle.decode_workload(w), 'bf16')}")
 
 
+@pytest.mark.parametrize("ctx0", [2048, 2304, 4000])
+def test_reduce_one_wave_rows_many_slots(dev, ctx0, monkeypatch):
+    """2048 (sequence, query head) rows, so that the reduce runs one wave per
+    row, and a first context whose segment the 16-block minimum shares cut
+    into 8, 9 or 16 partial slots (the reduce loads a wave's slots eight at a
+    time: one full batch, one slot more, two batches); the other contexts are
+    short, ragged and partly empty."""
+    say(f"case: one-wave reduce rows, first context {ctx0}")
+    monkeypatch.setenv("PA_STREAM_WAVES", "600")
+    ctx = [ctx0] + [(7 * i) % 40 for i in range(63)]
+    w = make_workload(custom_spec(64, 32, 4, 128, 16, "bf16", ctx=ctx), seed=23)
+    d = to_device(w, dev)
+    say(f"  {compare(d.decode(), oracle.decode_workload(w), 'bf16')}")
+
+
 @pytest.mark.parametrize("dtype,D,hq,hkv", [("bf16", 128, 64, 8), ("f32", 64, 4, 2),
                                             ("bf16", 64, 16, 4)])
 def test_long_segments_refill_block_ids(dev, dtype, D, hq, hkv, monkeypatch):

@@ -80,6 +80,18 @@ def test_latent_stream_split(dev, waves, monkeypatch):
     say(f"  {compare(d.decode(), oracle.decode_workload(w), 'bf16')}")
 
 
+@pytest.mark.parametrize("grid", ["8", "9", "17"])
+def test_latent_reduce_part_batches(dev, grid, monkeypatch):
+    """One sequence of 72 units cut into 8, 9 or 15 parts by 8, 9 or 17
+    work-groups (the reduce loads a sequence's parts eight at a time: one
+    full batch, one part more, two batches)."""
+    say(f"case: latent, 72 units over {grid} work-groups")
+    monkeypatch.setenv("PA_STREAM_WAVES", grid)
+    w = make_workload(_spec(128, [2304]), seed=24)
+    d = to_device(w, dev)
+    say(f"  {compare(d.decode(), oracle.decode_workload(w), 'bf16')}")
+
+
 def test_latent_append_then_decode(dev):
     say("case: latent append + decode(ctx + 1)")
     w = make_workload(_spec(128, [63, 64, 500]), seed=7)
