@@ -75,7 +75,8 @@ constexpr int kAhead = 2;                     // units in flight while one is co
 constexpr int kSlots = 4;                     // ring slots (a power of two keeps the
                                               // slot arithmetic in shifts and immediates)
 constexpr int kDmaPerUnit = kUnitB / 1024;    // 36: 32 main rows + 4 groups of 8 RoPE rows
-constexpr int kHeads = 32;                    // heads per wave in the scores (one tile)
+constexpr int kHeads = 32;                    // heads per score tile
+constexpr int kLatentNW = 4;                  // waves of a partition work-group, one per SIMD
 constexpr int kKSteps = kDK / 16;             // 36 k-steps of q . L
 constexpr int kMainKSteps = kDV / 16;         // the first 32 of them read the main region
 constexpr int kDimTiles = kDV / 32;           // 16 tiles of the output
@@ -148,34 +149,56 @@ __device__ __forceinline__ void mfma_v_fence(f32x16_t &c, bf16x8_t a, bf16x8_t b
 __device__ __forceinline__ void mfma_a(f32x16_t &c, bf16x8_t a, bf16x8_t b) {
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b) : "memory");
 }
-// Fence over the 16 output tiles (before the rescale and the final store).
-__device__ __forceinline__ void acc_fence(f32x16_t (&acc)[16]) {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
-                 : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]), "+a"(acc[4]),
-                   "+a"(acc[5]), "+a"(acc[6]), "+a"(acc[7]), "+a"(acc[8]), "+a"(acc[9]),
-                   "+a"(acc[10]), "+a"(acc[11]), "+a"(acc[12]), "+a"(acc[13]), "+a"(acc[14]),
-                   "+a"(acc[15])
-                 :: "memory");
+// Fence over the output tiles (before the rescale and the final store).
+template <int N>
+__device__ __forceinline__ void acc_fence(f32x16_t (&acc)[N]) {
+    static_assert(N == 4 || N == 8 || N == 16, "4, 8 or 16 output tiles");
+    if constexpr (N == 16) {
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]), "+a"(acc[4]),
+                       "+a"(acc[5]), "+a"(acc[6]), "+a"(acc[7]), "+a"(acc[8]), "+a"(acc[9]),
+                       "+a"(acc[10]), "+a"(acc[11]), "+a"(acc[12]), "+a"(acc[13]), "+a"(acc[14]),
+                       "+a"(acc[15])
+                     :: "memory");
+    } else if constexpr (N == 8) {
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]), "+a"(acc[4]),
+                       "+a"(acc[5]), "+a"(acc[6]), "+a"(acc[7])
+                     :: "memory");
+    } else {
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3])
+                     :: "memory");
+    }
 }
 
-template <int NW>
-__global__ __launch_bounds__(NW *kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int HT>
+__global__ __launch_bounds__(kLatentNW *kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws_ml,
                              int32_t *__restrict__ ws_prefix, const uint16_t *__restrict__ q,
                              const uint16_t *__restrict__ latent,
                              const int32_t *__restrict__ block_tables,
                              const int32_t *__restrict__ context_lens, float scale_log2,
                              int num_seqs, int num_heads, int max_blocks) {
-    constexpr int HT = NW;              // head tiles (of 32) in the work-group
+    // HT head tiles (of 32) in the work-group; its four waves (one per SIMD)
+    // split each tile's score contraction KS ways: wave w scores head tile
+    // w % HT over k-split w / HT, and accumulates every head tile's outputs
+    // for its DT output dim tiles.
+    constexpr int NW = kLatentNW;
+    constexpr int KS = NW / HT;
     constexpr int DT = kDimTiles / NW;  // output dim tiles per wave
-    static_assert(DT * HT == 16, "16 accumulator tiles per wave");
+    static_assert(NW % HT == 0, "head tiles divide the waves");
+    constexpr int kMainPer = kMainKSteps / KS;              // main k-steps of a split (multiple of 8)
+    constexpr int kRopePer = (kKSteps - kMainKSteps) / KS;  // RoPE k-steps of a split
+    constexpr int kKW = kMainPer + kRopePer;                // k-steps of a split
+    static_assert(kMainPer % 8 == 0 && kRopePer * KS == kKSteps - kMainKSteps, "k-step split");
+    constexpr int NA = DT * HT;         // output tiles per wave
     constexpr int kVR = 3;              // V^T operands read ahead
     constexpr int kRA = 3;              // score A operands read ahead
     constexpr int kNV = 2 * DT;         // value steps (of HT products) per unit
-    // of them beside the score chain, the rest beside the softmax: none with
-    // four waves (measured 1-2% faster than half), a quarter with two waves
-    // (whose wider value steps overflowed the registers there), half with one
-    constexpr int kVA = NW == 4 ? 0 : NW == 2 ? kNV / 4 : kNV / 2;
+    // of them beside the score chain, the rest beside the softmax: none
+    // (measured 1-2% faster than half beside the chain)
+    constexpr int kVA = 0;
 
     // Ring: main regions (dims 0..511 of 32 rows) for units u % 4, RoPE
     // regions (dims 512..575) for units u % 3: while step u runs, unit u's
@@ -190,6 +213,8 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
     __shared__ __attribute__((aligned(16))) int32_t s_ids[2][kWave];
     __shared__ __attribute__((aligned(16))) uint4 s_sink[kWave];  // target of padding loads
     __shared__ float s_l[HT * kHeads];  // each head's running sum, for the partial
+    // partial scores of the waves with k-split > 0, read by their tile's first wave
+    __shared__ __attribute__((aligned(16))) u32x4_t s_spart[KS > 1 ? (KS - 1) * HT * 4 * kWave : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -197,7 +222,9 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
     __builtin_assume(wave >= 0 && wave < NW);
     const int l31 = lane & 31;    // MFMA row (A) / column (B, C) of this lane
     const int hk = lane >> 5;     // which 8 of a 16-wide k-step this lane holds
-    const int head = wave * kHeads + l31;  // this lane's head in the scores
+    const int ht_w = wave % HT;            // this wave's head tile in the scores
+    const int ksplit = wave / HT;          // and its share of their contraction
+    const int head = ht_w * kHeads + l31;  // this lane's head in the scores
     const bool head_ok = head < num_heads;
 
     // ---- this work-group's part: a sequence-aligned split ------------------
@@ -343,19 +370,25 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
             fetch_ids(0);
             if (nblk > kWave) fetch_ids(1);
         }
-        // q^T B-operand fragments of this lane's head: dims 16 ks + 8 hk .. + 7
-        // for every k-step (zero for padding heads past num_heads).
-        bf16x8_t qf[kKSteps];
+        // q^T B-operand fragments of this lane's head: dims 16 kg + 8 hk .. + 7
+        // for the k-steps kg of this wave's split (zero for padding heads past
+        // num_heads): local step k < kMainPer is main step ksplit kMainPer + k,
+        // the others RoPE steps 32 + ksplit kRopePer + (k - kMainPer).
+        bf16x8_t qf[kKW];
         if (head_ok) {
             const uint4 *qr = reinterpret_cast<const uint4 *>(
                 q + (static_cast<int64_t>(b) * num_heads + head) * kDK + 8 * hk);
 #pragma unroll
-            for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = __builtin_bit_cast(bf16x8_t, qr[2 * ks]);
+            for (int k = 0; k < kKW; ++k) {
+                const int kg = k < kMainPer ? ksplit * kMainPer + k
+                                            : kMainKSteps + ksplit * kRopePer + (k - kMainPer);
+                qf[k] = __builtin_bit_cast(bf16x8_t, qr[2 * kg]);
+            }
 #pragma unroll
-            for (int ks = 0; ks < kKSteps; ++ks) settle(qf[ks]);
+            for (int k = 0; k < kKW; ++k) settle(qf[k]);
         } else {
 #pragma unroll
-            for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = bf16x8_t{};
+            for (int k = 0; k < kKW; ++k) qf[k] = bf16x8_t{};
         }
         drain_vmem();
         __syncthreads();  // ids landed for every wave; the previous segment is done
@@ -364,9 +397,9 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
         float l_run = 0.f;      // this lane's share of its running sum
         // O^T tile (dt, ht) = acc[dt * HT + ht]: dims 32 (DT wave + dt) +
         // 8 (j >> 2) + 4 hk + (j & 3) of head 32 ht + l31
-        f32x16_t acc[16];
+        f32x16_t acc[NA];
 #pragma unroll
-        for (int t = 0; t < 16; ++t) acc[t] = f32x16_t{};
+        for (int t = 0; t < NA; ++t) acc[t] = f32x16_t{};
 
         // Units of this segment: 32-token halves of blocks, each holding at
         // least one context token (unit u is half (h0 + u) & 1 of block
@@ -438,11 +471,14 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
         // 12 row offsets live; the V^T reads below recompute theirs at each use,
         // where an empty asm hides the lane's terms, to stay in the register
         // budget)
-        auto qk_read = [&](int u, int ks) {
-            const uint32_t x = ks < kMainKSteps ? qx : rx;
+        // (local step k of this wave's split; its main steps start at a
+        // multiple of 8, so their chunk term stays a constant)
+        const uint32_t qmain = static_cast<uint32_t>(ksplit * kMainPer / 8) * 256u;
+        auto qk_read = [&](int u, int k) {
             const uint32_t addr =
-                ks < kMainKSteps ? main_slot(u) + qrow + 256 * (ks >> 3) + ((32u * (ks & 7)) ^ x)
-                                 : rope_slot(u) + rrow + ((32u * (ks - kMainKSteps)) ^ x);
+                k < kMainPer ? main_slot(u) + qmain + qrow + 256 * (k >> 3) + ((32u * (k & 7)) ^ qx)
+                             : rope_slot(u) + rrow +
+                                   ((32u * static_cast<uint32_t>(ksplit * kRopePer + k - kMainPer)) ^ rx);
             return ds_read_b128(addr);
         };
         // V^T operand (k-step s, this wave's dim tile dt, half qq) of unit u
@@ -464,9 +500,9 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
                 f(ks);
                 const int r = ks % kRA;
                 if (ks == 0) mfma_v0(s, xa[r], qf[ks]);
-                else if (ks + 1 < kKSteps) mfma_v(s, xa[r], qf[ks]);
+                else if (ks + 1 < kKW) mfma_v(s, xa[r], qf[ks]);
                 else mfma_v_fence(s, xa[r], qf[ks]);
-                if (ks + kRA < kKSteps) xa[r] = qk_read(u, ks + kRA);
+                if (ks + kRA < kKW) xa[r] = qk_read(u, ks + kRA);
             }
         };
         auto score_prefetch = [&](int u) {
@@ -514,7 +550,7 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
                     m_run = m_new;
                     if (hk == 0) s_alpha[u & 1][head] = alpha;
                 }
-                if (lane == 0) s_flag[u & 1][wave] = moved && u > 0;  // u = 0: nothing to rescale
+                if (lane == 0) s_flag[u & 1][ht_w] = moved && u > 0;  // u = 0: nothing to rescale
             } else {
                 // pieces 4..11: probabilities 2 v, 2 v + 1 of k-step v >> 2
                 const int v = piece - 4, sv = v >> 2, e = v & 3;
@@ -522,7 +558,7 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
                 l_run = dot2_bf16(w4[e], 0x3F803F80u, l_run);  // + both rounded values (bf16 1, 1)
                 if (e == 3)
                     *(__attribute__((address_space(3))) u32x4_t *)(uintptr_t)(
-                        p_lds + (u & 1) * kPBuf + (wave * 2 + sv) * kWave * 16) =
+                        p_lds + (u & 1) * kPBuf + (ht_w * 2 + sv) * kWave * 16) =
                         u32x4_t{w4[0], w4[1], w4[2], w4[3]};
             }
         };
@@ -561,14 +597,17 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
         auto rescale = [&](int u) {
             const u32x4_t fl = *(const __attribute__((address_space(3))) u32x4_t *)(
                 uintptr_t)lds_offset(&s_flag[u & 1][0]);
-            if (__builtin_expect((fl[0] | fl[1] | fl[2] | fl[3]) != 0, 0)) {
+            int any = 0;  // (flags of head tiles past HT are never written)
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) any |= fl[ht];
+            if (__builtin_expect(any != 0, 0)) {
                 float alpha[HT];
 #pragma unroll
                 for (int ht = 0; ht < HT; ++ht)
                     alpha[ht] = fl[ht] != 0 ? s_alpha[u & 1][ht * kHeads + l31] : 1.0f;
                 acc_fence(acc);
 #pragma unroll
-                for (int t = 0; t < 16; ++t) {
+                for (int t = 0; t < NA; ++t) {
                     f32x16_t xv = acc[t];
                     asm volatile("" : "+v"(xv));
                     xv *= alpha[t % HT];
@@ -577,6 +616,34 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
                     asm volatile("" : "+a"(acc[t]));
                 }
                 asm volatile("s_nop 2" ::: "memory");
+            }
+        };
+
+        // The waves of a head tile with k-split > 0 hand their partial scores
+        // to the tile's first wave (k-split 0), which adds them in k-split
+        // order and alone runs the softmax; one barrier between the two.
+        auto exchange = [&](f32x16_t &s) {
+            if constexpr (KS > 1) {
+                if (ksplit > 0) {
+                    u32x4_t *dst = &s_spart[((ksplit - 1) * HT + ht_w) * 4 * kWave + lane];
+#pragma unroll
+                    for (int qd = 0; qd < 4; ++qd)
+                        dst[qd * kWave] = u32x4_t{as_u(s[4 * qd]), as_u(s[4 * qd + 1]),
+                                                  as_u(s[4 * qd + 2]), as_u(s[4 * qd + 3])};
+                }
+                __syncthreads();
+                if (ksplit == 0) {
+#pragma unroll
+                    for (int j = 1; j < KS; ++j) {
+                        const u32x4_t *src = &s_spart[((j - 1) * HT + ht_w) * 4 * kWave + lane];
+#pragma unroll
+                        for (int qd = 0; qd < 4; ++qd) {
+                            const u32x4_t v = src[qd * kWave];
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) s[4 * qd + i] += as_f(v[i]);
+                        }
+                    }
+                }
             }
         };
 
@@ -603,9 +670,12 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
             __syncthreads();
             f32x16_t s;
             score_prefetch(0);
-            score_steps(s, 0, 0, kKSteps, [](int) {});
+            score_steps(s, 0, 0, kKW, [](int) {});
+            exchange(s);
+            if (ksplit == 0) {
 #pragma unroll
-            for (int piece = 0; piece < 12; ++piece) softmax_piece(s, 0, piece);
+                for (int piece = 0; piece < 12; ++piece) softmax_piece(s, 0, piece);
+            }
         }
 
         for (int u = 0; u < nunits; ++u) {
@@ -624,19 +694,19 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
             // the softmax of unit u + 1 in 12 pieces beside the other kNV - kVA
             // and this wave's DMA rows of unit u + 3
             f32x16_t s;
-            score_steps(s, u1, 0, kKSteps, [&](int ks) {
+            score_steps(s, u1, 0, kKW, [&](int ks) {
 #pragma unroll
-                for (int j = (ks * kVA + kKSteps - 1) / kKSteps;
-                     j < ((ks + 1) * kVA + kKSteps - 1) / kKSteps; ++j)
+                for (int j = (ks * kVA + kKW - 1) / kKW; j < ((ks + 1) * kVA + kKW - 1) / kKW; ++j)
                     value_step(u, j);
             });
+            exchange(s);
             // (the DMA rows of unit u + 3 go beside the softmax: rows k with
             // k * 12 / kPer in [piece, piece + 1), each exactly once; beside the
             // score products they overflowed the register budget)
             constexpr int kVB = kNV - kVA;
 #pragma unroll
             for (int piece = 0; piece < 12; ++piece) {
-                softmax_piece(s, u1, piece);
+                if (ksplit == 0) softmax_piece(s, u1, piece);
 #pragma unroll
                 for (int k = (piece * kPer + 11) / 12; k < ((piece + 1) * kPer + 11) / 12; ++k)
                     issue_row(u3, d3, k);
@@ -655,12 +725,12 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
         // go out in register order, so every store writes 1 KB of consecutive
         // bytes.
         const float l_tot = l_run + __shfl_xor(l_run, 32);
-        if (hk == 0) s_l[head] = l_tot;
+        if (ksplit == 0 && hk == 0) s_l[head] = l_tot;
         __syncthreads();  // every head's sum is in s_l
         acc_fence(acc);
         {
             const int64_t slot = blockIdx.x;
-            if (hk == 0) ws_ml[slot * (HT * kHeads) + head] = make_float2(m_run, l_tot);
+            if (ksplit == 0 && hk == 0) ws_ml[slot * (HT * kHeads) + head] = make_float2(m_run, l_tot);
             u32x4_t *dst = reinterpret_cast<u32x4_t *>(ws_acc) + slot * (16 * HT * 2 * kWave) +
                            (DT * wave) * (HT * 2 * kWave) + lane;
             float inv[HT];
@@ -696,12 +766,11 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
 // 2 h + 1.  The kernel is a few memory round trips long, so every load of a
 // batch of kBatch parts is issued before any is used (parts past the last
 // re-read the last one and weigh 0), and batches merge by the running max.
-template <int NW>
-__global__ __launch_bounds__(NW *kWave) void latent_reduce_kernel(
+template <int HT>
+__global__ __launch_bounds__(HT *kWave) void latent_reduce_kernel(
     uint16_t *__restrict__ out, const float *__restrict__ ws_acc, const float2 *__restrict__ ws_ml,
     const int32_t *__restrict__ ws_prefix, const int32_t *__restrict__ context_lens,
     int num_seqs, int num_heads) {
-    constexpr int HT = NW;
     constexpr int kBatch = 8;
     const int dg = blockIdx.x;
     const int b = blockIdx.y;
@@ -772,24 +841,25 @@ __global__ __launch_bounds__(NW *kWave) void latent_reduce_kernel(
     }
 }
 
-template <int NW>
+template <int HT>
 pa_status enqueue_latent(const DecodeShape &s, const DecodeArgs &a, const DecodePlan &p,
                          float scale_log2, hipStream_t stream, std::string *why) {
     char *ws = static_cast<char *>(a.workspace);
     float *acc = reinterpret_cast<float *>(ws + p.acc_offset);
     float2 *ml = reinterpret_cast<float2 *>(ws + p.ml_offset);
     int32_t *prefix = reinterpret_cast<int32_t *>(ws + p.prefix_offset);
-    const auto kernel = latent_partition_kernel<NW>;
+    const auto kernel = latent_partition_kernel<HT>;
     // one work-group per resident slot, and at least one per sequence (each
     // work-group streams a part of one sequence)
-    const int waves = std::max(stream_waves(kernel, NW * kWave, 1, kLatentWavesMax), s.num_seqs);
-    hipLaunchKernelGGL(kernel, dim3(waves), dim3(NW * kWave), 0, stream, acc, ml, prefix,
+    const int waves =
+        std::max(stream_waves(kernel, kLatentNW * kWave, 1, kLatentWavesMax), s.num_seqs);
+    hipLaunchKernelGGL(kernel, dim3(waves), dim3(kLatentNW * kWave), 0, stream, acc, ml, prefix,
                        static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k_cache),
                        a.block_tables, a.context_lens, scale_log2, s.num_seqs, s.num_q_heads,
                        s.max_blocks_per_seq);
     pa_status st = hip_status(hipGetLastError(), why, "latent partition launch");
     if (st != PA_OK) return st;
-    hipLaunchKernelGGL(latent_reduce_kernel<NW>, dim3(kDimTiles, s.num_seqs), dim3(NW * kWave), 0,
+    hipLaunchKernelGGL(latent_reduce_kernel<HT>, dim3(kDimTiles, s.num_seqs), dim3(HT * kWave), 0,
                        stream, static_cast<uint16_t *>(a.out), acc, ml, prefix, a.context_lens,
                        s.num_seqs, s.num_q_heads);
     return hip_status(hipGetLastError(), why, "latent reduce launch");
@@ -801,7 +871,7 @@ pa_status launch_latent_decode(const DecodeShape &s, const DecodeArgs &a, const 
                                hipStream_t stream, std::string *why) {
     if (s.num_seqs == 0) return PA_OK;
     const float scale_log2 = static_cast<float>(static_cast<double>(a.scale) * 1.4426950408889634);
-    switch (latent_waves(s.num_q_heads)) {
+    switch (latent_head_tiles(s.num_q_heads)) {
         case 1: return enqueue_latent<1>(s, a, p, scale_log2, stream, why);
         case 2: return enqueue_latent<2>(s, a, p, scale_log2, stream, why);
         default: return enqueue_latent<4>(s, a, p, scale_log2, stream, why);

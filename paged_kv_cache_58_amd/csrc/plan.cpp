@@ -194,7 +194,7 @@ pa_status plan_decode(const DecodeShape &s, DecodePlan *plan, std::string *why) 
                (size_t)s.q_len;
     else
         rows = ((size_t)kLatentWavesMax + (size_t)s.num_seqs) *
-               (size_t)(latent_waves(s.num_q_heads) * kLatentHeadTile);
+               (size_t)(latent_head_tiles(s.num_q_heads) * kLatentHeadTile);
     p.acc_offset = 0;
     p.ml_offset = round_up(rows * s.head_dim_v * sizeof(float), kWorkspaceAlign);
     p.prefix_offset = round_up(p.ml_offset + rows * 2 * sizeof(float), kWorkspaceAlign);

@@ -79,9 +79,9 @@ constexpr int kStreamWavesMax = 4096;
 constexpr int kLatentWavesMax = 512;
 // Query heads one wave of the latent path covers in its scores.
 constexpr int kLatentHeadTile = 32;
-// Waves of a latent work-group: one per 32 query heads, rounded up to 1, 2
-// or 4 (the 512 output dims are split evenly over the waves).
-inline int latent_waves(int num_q_heads) {
+// Score tiles of 32 query heads in a latent work-group, rounded up to 1, 2 or
+// 4 (its four waves split each tile's score contraction 4, 2 or 1 ways).
+inline int latent_head_tiles(int num_q_heads) {
     return num_q_heads <= kLatentHeadTile ? 1 : num_q_heads <= 2 * kLatentHeadTile ? 2 : 4;
 }
 
@@ -114,10 +114,10 @@ constexpr int kMaxColTiles = 4;
 //  * latent: each sequence cut into parts of near-equal size, one
 //    work-group per part (at least one per CU, at least one per sequence);
 //    slots = kLatentWavesMax + num_seqs (more than the work-groups), each
-//    holding latent_waves(num_q_heads) * 32 heads (the query heads,
+//    holding latent_head_tiles(num_q_heads) * 32 heads (the query heads,
 //    padded); the prefix array holds the parts per sequence (num_seqs + 1).
 //    There a slot holds the part's output divided by its sum l, in bf16, in
-//    the partition kernel's register order (HT = latent_waves head tiles:
+//    the partition kernel's register order (HT = latent_head_tiles:
 //    16-byte index ((dt * HT + ht) * 2 + h) * 64 + lane holds dims 32 dt +
 //    8 qd + 4 (lane >> 5) .. + 3, qd = 2 h, 2 h + 1, of head 32 ht +
 //    (lane & 31)), half the fp32 area it is sized for, and (max, sum) in fp32.

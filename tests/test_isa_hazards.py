@@ -162,7 +162,10 @@ def latent_asm(tmp_path_factory):
 def test_latent_kernel_has_products(latent_asm):
     blocks = _instructions(latent_asm, "_ZN2pa12_GLOBAL__N_123latent_partition_kernel")
     n = sum(1 for b in blocks for mn, _ in b if mn.startswith("v_mfma"))
-    assert n >= 3 * 68  # three instantiations, 36 + 32 products per unit each
+    # three instantiations (1, 2 and 4 head tiles): per unit 36 / KS score
+    # products (the wave's share of its tile's contraction, KS = 4 / tiles)
+    # and 8 value products per head tile
+    assert n >= (9 + 8) + (18 + 16) + (36 + 32)
 
 
 def test_latent_kernel_mfma_hazards(latent_asm):
