@@ -10,13 +10,16 @@ data of the named workload, resident in HBM before timing starts.  With
 pa_cache_append_mxfp8 + pa_decode_mxfp8.  With --q-len K > 1 the decode is
 pa_decode_multi: the last K cached tokens of every sequence (the appended one
 among them) are its queries, causal among themselves, the shape of verifying
-K - 1 drafted tokens plus the new one in one pass.
+K - 1 drafted tokens plus the new one in one pass.  --q-heads H runs the
+latent workload with H query heads (its share of a 128-head model split over
+GPUs by heads); the context lengths stay those of the workload.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -245,6 +248,9 @@ def main() -> int:
     ap.add_argument("--config", default="c3", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--kv-format", default="native", choices=["native", "mxfp8"],
                     help="cache format: the workload's dtype, or MXFP8 (bf16 d=128 shapes)")
+    ap.add_argument("--q-heads", type=int, default=0,
+                    help="latent workload only: its query heads (16..128, a multiple of 16, as "
+                         "a 128-head model split over GPUs by heads); 0 keeps the workload's")
     ap.add_argument("--q-len", type=int, default=1,
                     help="query tokens per sequence (pa_decode_multi when > 1)")
     ap.add_argument("--window", type=int, default=0,
@@ -269,9 +275,16 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     spec = workloads.CONFIGS[args.config]
+    H = args.q_heads
+    if H:
+        if not spec.mla or H % 16 or not 16 <= H <= 128:
+            log(f"--q-heads takes 16..128 (a multiple of 16) on the latent workload, not {args.config}")
+            return 2
+        # same seed (the spec's index), so the same context lengths and latent
+        spec = dataclasses.replace(spec, num_q_heads=H)
 
     t0 = time.time()
-    w = workloads.make_workload(args.config)
+    w = workloads.make_workload(spec)
     log(f"[bench] generated {args.config} in {time.time() - t0:.1f}s: "
         f"{w.num_blocks} blocks, sum ctx {int(w.context_lens.sum())}")
 
@@ -428,7 +441,7 @@ def main() -> int:
     max_err = float(d.max())
 
     traffic = (load_traffic(args.config + ("_mxfp8" if mx else ""), decode_bytes)
-               if Q == 1 and not W else None)
+               if Q == 1 and not W and not H else None)
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -445,8 +458,11 @@ def main() -> int:
         "config": {"workload": WORKLOAD_TEXT[args.config] + (
                        ", KV cache in MXFP8 (E4M3 + E8M0 per 32 values)" if mx else "") + (
                        f", {Q} causal query tokens per sequence" if Q > 1 else "") + (
-                       f", sliding window of {W} tokens" if W else ""),
+                       f", sliding window of {W} tokens" if W else "") + (
+                       f", {H} query heads instead of {workloads.CONFIGS[args.config].num_q_heads}"
+                       if H else ""),
                    "name": spec.name + ("-mxfp8" if mx else "") + (f"-q{Q}" if Q > 1 else "") +
+                           (f"-h{H}" if H else "") +
                            (f"-w{W}" if W else ""),
                    "kv_format": args.kv_format,
                    "global_batch": spec.num_seqs, "seq_len": int(L1.max()),
