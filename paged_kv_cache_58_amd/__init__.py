@@ -123,6 +123,59 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _expect(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _int32(name: str, t, ndim: int, rows: Optional[int] = None) -> None:
+    import torch
+
+    _expect(t.dtype == torch.int32, f"{name} must be int32, not {t.dtype}")
+    _expect(t.dim() == ndim, f"{name} must have {ndim} dims, not {tuple(t.shape)}")
+    if rows is not None:
+        _expect(t.shape[0] == rows, f"{name} has {t.shape[0]} rows, expected {rows}")
+
+
+def _same_dtype(dtype, **tensors) -> None:
+    for name, t in tensors.items():
+        if t is not None:
+            _expect(t.dtype == dtype, f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _on_gpu(**tensors) -> None:
+    """Every array the library reads or writes must be device memory: a host
+    pointer handed to a kernel would fault the GPU, not raise."""
+    for name, t in tensors.items():
+        if t is not None:
+            _expect(t.is_cuda, f"{name} must be a GPU tensor")
+            _expect(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def _check_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, workspace,
+                       q_dims: int = 3) -> None:
+    """Shape and dtype agreement of a single- or several-query decode on
+    native caches ([num_blocks, block_size, Hkv, d])."""
+    _expect(q.dim() == q_dims, f"q must have {q_dims} dims, not {tuple(q.shape)}")
+    _expect(k_cache.dim() == 4, f"k_cache must be [num_blocks, block_size, Hkv, d], not "
+                                f"{tuple(k_cache.shape)}")
+    _same_dtype(q.dtype, k_cache=k_cache, v_cache=v_cache, out=out)
+    _expect(k_cache.shape[3] == q.shape[-1],
+            f"k_cache head dim {k_cache.shape[3]} differs from q's {q.shape[-1]}")
+    if v_cache is not None:
+        _expect(v_cache.dim() == 4 and tuple(v_cache.shape[:3]) == tuple(k_cache.shape[:3]),
+                f"v_cache {tuple(v_cache.shape)} does not match k_cache {tuple(k_cache.shape)}")
+        _expect(out.shape[-1] == v_cache.shape[3],
+                f"out head dim {out.shape[-1]} differs from v_cache's {v_cache.shape[3]}")
+    _expect(tuple(out.shape[:-1]) == tuple(q.shape[:-1]),
+            f"out {tuple(out.shape)} does not match q {tuple(q.shape)}")
+    B = q.shape[0]
+    _int32("block_tables", block_tables, 2, B)
+    _int32("context_lens", context_lens, 1, B)
+    _on_gpu(out=out, q=q, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+            context_lens=context_lens, workspace=workspace)
+
+
 def _stream(stream) -> Optional[int]:
     import torch
 
@@ -138,9 +191,26 @@ def cache_append(k_cache, v_cache, k, v, slot_mapping, stream=None) -> None:
     selects latent mode (k only).  k, v: [num_tokens, kv_heads, head_dim] with
     contiguous rows.  slot_mapping: int32 [num_tokens].
     """
+    _expect(k_cache.dim() == 4, f"k_cache must be [num_blocks, block_size, Hkv, d], not "
+                                f"{tuple(k_cache.shape)}")
     nb, bs, hkv, dk = k_cache.shape
     dv = 0 if v_cache is None else v_cache.shape[3]
+    _expect((v_cache is None) == (v is None), "v_cache and v must both be given or both None")
+    _same_dtype(k_cache.dtype, v_cache=v_cache, k=k, v=v)
+    if v_cache is not None:
+        _expect(v_cache.dim() == 4 and tuple(v_cache.shape[:3]) == (nb, bs, hkv),
+                f"v_cache {tuple(v_cache.shape)} does not match k_cache {tuple(k_cache.shape)}")
+    _int32("slot_mapping", slot_mapping, 1)
     n = slot_mapping.shape[0]
+    _expect(k.shape[0] == n and k.numel() == n * hkv * dk,
+            f"k {tuple(k.shape)} is not [{n}, {hkv}, {dk}]")
+    if v is not None:
+        _expect(v.shape[0] == n and v.numel() == n * hkv * dv,
+                f"v {tuple(v.shape)} is not [{n}, {hkv}, {dv}]")
+    _on_gpu(k_cache=k_cache, v_cache=v_cache, slot_mapping=slot_mapping)
+    for name, t in (("k", k), ("v", v)):
+        if t is not None:
+            _expect(t.is_cuda, f"{name} must be a GPU tensor")
     k2 = k.reshape(n, -1) if n else k
     v2 = None if v is None else (v.reshape(n, -1) if n else v)
     if n and k2.stride(1) != 1:
@@ -178,15 +248,10 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, workspac
     latent mode, V = first out.shape[-1] values of each K row); block_tables
     int32 [B, max_blocks]; context_lens int32 [B]; out [B, Hq, dv] in q's dtype.
     """
+    _check_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, workspace)
     B, hq, dk = q.shape
     nb, bs, hkv, _ = k_cache.shape
     dv = out.shape[2]
-    for name, t in (("q", q), ("k_cache", k_cache), ("out", out), ("block_tables", block_tables),
-                    ("context_lens", context_lens)):
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    if v_cache is not None and not v_cache.is_contiguous():
-        raise ValueError("v_cache must be contiguous")
     _check(lib().pa_decode(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         _ptr(context_lens), float(scale), B, hq, hkv, dk, dv, bs, nb, block_tables.shape[1],
@@ -215,12 +280,39 @@ def alloc_mxfp8_cache(num_blocks, block_size, num_kv_heads, head_dim=128, device
     return tuple(torch.full(sh, fill, dtype=torch.uint8, device=device) for sh in shapes)
 
 
+def _check_mx_pools(k_cache, v_cache, k_scale, v_scale) -> None:
+    """The four MXFP8 arrays: uint8, layouts of alloc_mxfp8_cache, on the GPU."""
+    import torch
+
+    _same_dtype(torch.uint8, k_cache=k_cache, v_cache=v_cache, k_scale=k_scale, v_scale=v_scale)
+    _expect(k_cache.dim() == 4, f"k_cache must be [num_blocks, Hkv, block_size, d], not "
+                                f"{tuple(k_cache.shape)}")
+    nb, hkv, bs, d = k_cache.shape
+    want = {"v_cache": (v_cache, (nb, hkv, d, bs)),
+            "k_scale": (k_scale, (nb, hkv, bs, d // MX_BLOCK)),
+            "v_scale": (v_scale, (nb, hkv, bs, d // MX_BLOCK))}
+    for name, (t, shape) in want.items():
+        _expect(tuple(t.shape) == shape, f"{name} {tuple(t.shape)} is not {shape}")
+
+
 def cache_append_mxfp8(k_cache, v_cache, k_scale, v_scale, k, v, slot_mapping,
                        stream=None) -> None:
     """Quantize k[i] and v[i] ([num_tokens, kv_heads, head_dim], fp32 or bf16)
     into slot slot_mapping[i] of the MXFP8 caches (-1 skips)."""
+    import torch
+
+    _check_mx_pools(k_cache, v_cache, k_scale, v_scale)
     nb, hkv, bs, d = k_cache.shape
+    _int32("slot_mapping", slot_mapping, 1)
     n = slot_mapping.shape[0]
+    _expect(k.dtype in (torch.float32, torch.bfloat16), f"k must be float32 or bfloat16, not {k.dtype}")
+    _same_dtype(k.dtype, v=v)
+    for name, t in (("k", k), ("v", v)):
+        _expect(t.shape[0] == n and t.numel() == n * hkv * d,
+                f"{name} {tuple(t.shape)} is not [{n}, {hkv}, {d}]")
+        _expect(t.is_cuda, f"{name} must be a GPU tensor")
+    _on_gpu(k_cache=k_cache, v_cache=v_cache, k_scale=k_scale, v_scale=v_scale,
+            slot_mapping=slot_mapping)
     k2 = k.reshape(n, -1) if n else k
     v2 = v.reshape(n, -1) if n else v
     if n and (k2.stride(1) != 1 or v2.stride(1) != 1):
@@ -244,13 +336,19 @@ def alloc_mxfp8_workspace(q, k_cache, block_tables):
 def decode_mxfp8(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, scale,
                  workspace, stream=None) -> None:
     """decode() over MXFP8 caches; q and out bf16 [B, Hq, 128]."""
+    import torch
+
+    _check_mx_pools(k_cache, v_cache, k_scale, v_scale)
+    _expect(q.dim() == 3 and q.dtype == torch.bfloat16, "q must be bf16 [B, Hq, d]")
+    _same_dtype(torch.bfloat16, out=out)
+    _expect(tuple(out.shape) == tuple(q.shape), f"out {tuple(out.shape)} is not {tuple(q.shape)}")
+    _expect(q.shape[2] == k_cache.shape[3], "q head dim differs from the cache's")
+    _int32("block_tables", block_tables, 2, q.shape[0])
+    _int32("context_lens", context_lens, 1, q.shape[0])
+    _on_gpu(out=out, q=q, k_cache=k_cache, v_cache=v_cache, k_scale=k_scale, v_scale=v_scale,
+            block_tables=block_tables, context_lens=context_lens, workspace=workspace)
     B, hq, d = q.shape
     nb, hkv, bs, _ = k_cache.shape
-    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("k_scale", k_scale),
-                    ("v_scale", v_scale), ("out", out), ("block_tables", block_tables),
-                    ("context_lens", context_lens)):
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
     _check(lib().pa_decode_mxfp8(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
         _ptr(block_tables), _ptr(context_lens), float(scale), B, hq, hkv, d, bs, nb,
@@ -283,15 +381,30 @@ def decode_multi(out, q, k_cache, v_cache, block_tables, context_lens, scale, wo
     cached tokens, query i attending to tokens 0 .. L_b - q_len + i.  out
     [B, q_len, Hq, d].  bf16 caches [num_blocks, block_size, Hkv, d], or MXFP8
     caches (layouts of cache_append_mxfp8) when k_scale and v_scale are given."""
+    import torch
+
+    _expect((k_scale is None) == (v_scale is None), "give both k_scale and v_scale, or neither")
+    if k_scale is None:
+        _check_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, workspace,
+                           q_dims=4)
+        _expect(v_cache is not None, "v_cache is required")
+    else:
+        _check_mx_pools(k_cache, v_cache, k_scale, v_scale)
+        _expect(q.dim() == 4 and q.dtype == torch.bfloat16, "q must be bf16 [B, q_len, Hq, d]")
+        _same_dtype(torch.bfloat16, out=out)
+        _expect(tuple(out.shape) == tuple(q.shape), f"out {tuple(out.shape)} is not "
+                                                    f"{tuple(q.shape)}")
+        _expect(q.shape[3] == k_cache.shape[3], "q head dim differs from the cache's")
+        _int32("block_tables", block_tables, 2, q.shape[0])
+        _int32("context_lens", context_lens, 1, q.shape[0])
+        _on_gpu(out=out, q=q, k_cache=k_cache, v_cache=v_cache, k_scale=k_scale,
+                v_scale=v_scale, block_tables=block_tables, context_lens=context_lens,
+                workspace=workspace)
     B, Q, hq, d = q.shape
     if k_scale is None:
         nb, bs, hkv, _ = k_cache.shape
     else:
         nb, hkv, bs, _ = k_cache.shape
-    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("out", out),
-                    ("block_tables", block_tables), ("context_lens", context_lens)):
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
     _check(lib().pa_decode_multi(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
         _ptr(block_tables), _ptr(context_lens), float(scale), B, Q, hq, hkv, d, bs, nb,
@@ -377,6 +490,9 @@ class BlockManager:
 def copy_blocks(pool, src, dst, stream=None) -> None:
     """Block dst[i] of pool (first axis = blocks) becomes a copy of block
     src[i]; src and dst int32 device tensors."""
+    _int32("src", src, 1)
+    _int32("dst", dst, 1, src.shape[0])
+    _on_gpu(pool=pool, src=src, dst=dst)
     n = int(src.numel())
     block_bytes = pool[0].numel() * pool.element_size() if pool.shape[0] else 0
     _check(lib().pa_copy_blocks(_ptr(pool), block_bytes, _ptr(src), _ptr(dst), n,
@@ -392,12 +508,16 @@ def decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, scale, works
     """decode() attending only to the last ``window`` tokens of each sequence
     (0: all), optionally writing the log-sum-exp of the scores into ``lse``
     (fp32 [B, Hq])."""
+    import torch
+
+    _expect(v_cache is not None, "v_cache is required (no latent mode)")
+    if lse is not None:
+        _expect(lse.dtype == torch.float32 and tuple(lse.shape) == tuple(q.shape[:2]),
+                f"lse must be float32 [{q.shape[0]}, {q.shape[1]}]")
+        _on_gpu(lse=lse)
+    _check_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, workspace)
     B, hq, d = q.shape
     nb, bs, hkv, _ = k_cache.shape
-    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("out", out),
-                    ("block_tables", block_tables), ("context_lens", context_lens)):
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
     _check(lib().pa_decode_ex(
         _ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         _ptr(context_lens), float(scale), int(window), B, hq, hkv, d, bs, nb,
@@ -409,8 +529,21 @@ def attention_scores(scores, q, k_cache, block_tables, context_lens, lse, scale,
                      stream=None) -> None:
     """scores fp32 [B, Hkv, max_context]: each token's attention mass from the
     query heads of its KV head, exp(scale q.k - lse) summed over the group."""
+    import torch
+
+    _expect(q.dim() == 3 and k_cache.dim() == 4, "q must be [B, Hq, d], k_cache [nb, bs, Hkv, d]")
+    _same_dtype(q.dtype, k_cache=k_cache)
+    _expect(k_cache.shape[3] == q.shape[2], "k_cache head dim differs from q's")
     B, hq, d = q.shape
     nb, bs, hkv, _ = k_cache.shape
+    _expect(scores.dtype == torch.float32 and scores.dim() == 3 and
+            tuple(scores.shape[:2]) == (B, hkv), f"scores must be float32 [{B}, {hkv}, max_context]")
+    _expect(lse.dtype == torch.float32 and tuple(lse.shape) == (B, hq),
+            f"lse must be float32 [{B}, {hq}]")
+    _int32("block_tables", block_tables, 2, B)
+    _int32("context_lens", context_lens, 1, B)
+    _on_gpu(scores=scores, q=q, k_cache=k_cache, block_tables=block_tables,
+            context_lens=context_lens, lse=lse)
     _check(lib().pa_attention_scores(
         _ptr(scores), _ptr(q), _ptr(k_cache), _ptr(block_tables), _ptr(context_lens), _ptr(lse),
         float(scale), int(window), B, hq, hkv, d, bs, block_tables.shape[1], scores.shape[2],

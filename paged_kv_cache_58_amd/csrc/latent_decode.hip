@@ -714,25 +714,25 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
                 for (int j = (piece * kVB + 11) / 12; j < ((piece + 1) * kVB + 11) / 12; ++j)
                     value_step(u, kVA + j);
             }
+            // This unit's value products drain before the step ends: the
+            // compiler may move the accumulators between registers on the
+            // loop's edges (its exit, say), ahead of any statement after them.
+            acc_fence(acc);
         }
 
         // ---- this part's partial ---------------------------------------------
         // Slot blockIdx.x: (max, sum) per head in fp32 from the score waves,
-        // and the part's output normalised by its own sum, acc / l, rounded to
-        // bf16 (as split-KV kernels commonly hand their partial outputs over in
-        // the output type): half the bytes of fp32 accumulators, for one more
-        // rounding of the order of the output's own.  The tiles of this wave
-        // go out in register order, so every store writes 1 KB of consecutive
-        // bytes.
+        // and the part's output normalised by its own sum, acc / l, in fp32.
+        // The tiles of this wave go out in register order, so every store
+        // writes 1 KB of consecutive bytes.
         const float l_tot = l_run + __shfl_xor(l_run, 32);
         if (ksplit == 0 && hk == 0) s_l[head] = l_tot;
         __syncthreads();  // every head's sum is in s_l
-        acc_fence(acc);
         {
             const int64_t slot = blockIdx.x;
             if (ksplit == 0 && hk == 0) ws_ml[slot * (HT * kHeads) + head] = make_float2(m_run, l_tot);
-            u32x4_t *dst = reinterpret_cast<u32x4_t *>(ws_acc) + slot * (16 * HT * 2 * kWave) +
-                           (DT * wave) * (HT * 2 * kWave) + lane;
+            f32x4_t *dst = reinterpret_cast<f32x4_t *>(ws_acc) + slot * (kDimTiles * HT * 4 * kWave) +
+                           (DT * wave) * (HT * 4 * kWave) + lane;
             float inv[HT];
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) {
@@ -744,14 +744,12 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
 #pragma unroll
                 for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
+                    for (int qd = 0; qd < 4; ++qd) {
                         const f32x16_t &t = acc[dt * HT + ht];
                         const float r = inv[ht];
-                        dst[((dt * HT + ht) * 2 + h) * kWave] = u32x4_t{
-                            pack_bf16(t[8 * h] * r, t[8 * h + 1] * r),
-                            pack_bf16(t[8 * h + 2] * r, t[8 * h + 3] * r),
-                            pack_bf16(t[8 * h + 4] * r, t[8 * h + 5] * r),
-                            pack_bf16(t[8 * h + 6] * r, t[8 * h + 7] * r)};
+                        dst[((dt * HT + ht) * 4 + qd) * kWave] =
+                            f32x4_t{t[4 * qd] * r, t[4 * qd + 1] * r, t[4 * qd + 2] * r,
+                                    t[4 * qd + 3] * r};
                     }
         }
     }
@@ -759,13 +757,13 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
 
 // Log-sum-exp merge of a sequence's parts, O = sum_p 2^(m_p - M) l_p O_p /
 // sum_p 2^(m_p - M) l_p (the merge rule of the grouped path, with each part's
-// output already divided by its l_p), reading the register-ordered bf16 tiles:
-// work-group (dim tile dg, b) writes dims 32 dg .. + 31 of every head; thread
-// t = 64 ht + lane always sees head 32 ht + (lane & 31), and 16-byte half h
-// of its tile holds dims 32 dg + 8 qd + 4 (lane >> 5) .. + 3 for qd = 2 h,
-// 2 h + 1.  The kernel is a few memory round trips long, so every load of a
-// batch of kBatch parts is issued before any is used (parts past the last
-// re-read the last one and weigh 0), and batches merge by the running max.
+// output already divided by its l_p), reading the register-ordered fp32
+// tiles: work-group (dim tile dg, b) writes dims 32 dg .. + 31 of every head;
+// thread t = 64 ht + lane always sees head 32 ht + (lane & 31), and 16-byte
+// piece qd of its tile holds dims 32 dg + 8 qd + 4 (lane >> 5) .. + 3.  The
+// kernel is a few memory round trips long, so every load of a batch of
+// kBatch parts is issued before any is used (parts past the last re-read the
+// last one and weigh 0), and batches merge by the running max.
 template <int HT>
 __global__ __launch_bounds__(HT *kWave) void latent_reduce_kernel(
     uint16_t *__restrict__ out, const float *__restrict__ ws_acc, const float2 *__restrict__ ws_ml,
@@ -793,21 +791,22 @@ __global__ __launch_bounds__(HT *kWave) void latent_reduce_kernel(
         return;
     }
 
-    // part p holds its normalised output O_p (bf16) and (m_p, l_p): the merge
+    // part p holds its normalised output O_p (fp32) and (m_p, l_p): the merge
     // weight is 2^(m_p - M) l_p
     float M = kNegInf, den = 0.f;
     f32x4_t num[4] = {};
     for (int p0 = 0; p0 < n; p0 += kBatch) {
         float2 mp[kBatch];
-        u32x4_t v[kBatch][2];
+        f32x4_t v[kBatch][4];
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             const int64_t slot = first + min(p0 + j, n - 1);
             mp[j] = ws_ml[slot * (HT * kHeads) + head];
-            const u32x4_t *a = reinterpret_cast<const u32x4_t *>(ws_acc) +
-                               slot * (16 * HT * 2 * kWave) + ((dg * HT + ht) * 2) * kWave + lane;
-            v[j][0] = a[0];  // dims 8 (2 h + i / 2) + 4 (lane >> 5) .. of this tile, h = 0, 1
-            v[j][1] = a[kWave];
+            const f32x4_t *a = reinterpret_cast<const f32x4_t *>(ws_acc) +
+                               slot * (kDimTiles * HT * 4 * kWave) + ((dg * HT + ht) * 4) * kWave +
+                               lane;
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) v[j][qd] = a[qd * kWave];
         }
         float bm = kNegInf;
 #pragma unroll
@@ -825,12 +824,9 @@ __global__ __launch_bounds__(HT *kWave) void latent_reduce_kernel(
             const float wgt = p0 + j < n && mp[j].y > 0.f ? exp2_fast(mp[j].x - M) * mp[j].y : 0.f;
             den += wgt;
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+            for (int qd = 0; qd < 4; ++qd)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    num[2 * h + (i >> 1)][2 * (i & 1)] += wgt * bf16_lo(v[j][h][i]);
-                    num[2 * h + (i >> 1)][2 * (i & 1) + 1] += wgt * bf16_hi(v[j][h][i]);
-                }
+                for (int i = 0; i < 4; ++i) num[qd][i] = fmaf(wgt, v[j][qd][i], num[qd][i]);
         }
     }
 #pragma unroll

@@ -22,19 +22,16 @@ pa_status fail(pa_status st, std::string *why, const std::string &msg) {
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Whether a grouped-shape bf16 decode with head dim 128 runs its per-block
-// products on the matrix cores.  They are the default when a KV head serves
-// several query heads: two small products per block in place of about 400
-// VALU instructions per block and wave measure 2.5% faster on a 64/8-head
-// layer with 1K-8K contexts and 6% faster at 128K.  With one query head per
-// KV head both kernels take the same time and the lane-wise dot products,
-// which waste no matrix columns, stay.  PA_GQA_MFMA (0 or 1) overrides the
-// default.
+// Whether a single-query grouped-shape bf16 decode with head dim 128 runs its
+// per-block products on the matrix cores.  The lane-wise dot-product kernel is
+// the default: decode attention with one query row per head is a matrix-vector
+// product per KV head, which the vector units cover within the memory time.
+// PA_GQA_MFMA=1 selects the matrix-core variant (the same split, partials and
+// reduce), which carries the several-query and MXFP8 paths in any case.
 bool grouped_mfma_default(const DecodeShape &s) {
     if (s.dtype != PA_BF16 || s.head_dim_k != 128) return false;
     const char *env = std::getenv("PA_GQA_MFMA");
-    if (env && *env) return std::atoi(env) != 0;
-    return s.num_q_heads / s.num_kv_heads >= 2;
+    return env && *env && std::atoi(env) != 0;
 }
 
 // Cache blocks each wave of the grouped paths streams into LDS (ring depth):

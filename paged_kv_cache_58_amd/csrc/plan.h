@@ -116,11 +116,11 @@ constexpr int kMaxColTiles = 4;
 //    slots = kLatentWavesMax + num_seqs (more than the work-groups), each
 //    holding latent_head_tiles(num_q_heads) * 32 heads (the query heads,
 //    padded); the prefix array holds the parts per sequence (num_seqs + 1).
-//    There a slot holds the part's output divided by its sum l, in bf16, in
+//    There a slot holds the part's output divided by its sum l, in fp32, in
 //    the partition kernel's register order (HT = latent_head_tiles:
-//    16-byte index ((dt * HT + ht) * 2 + h) * 64 + lane holds dims 32 dt +
-//    8 qd + 4 (lane >> 5) .. + 3, qd = 2 h, 2 h + 1, of head 32 ht +
-//    (lane & 31)), half the fp32 area it is sized for, and (max, sum) in fp32.
+//    16-byte index ((dt * HT + ht) * 4 + qd) * 64 + lane holds dims 32 dt +
+//    8 qd + 4 (lane >> 5) .. + 3 of head 32 ht + (lane & 31)), and (max,
+//    sum) in fp32.
 struct DecodePlan {
     DecodePath path;
     int group;             // query heads per KV head

@@ -16,8 +16,10 @@ code, the two hazards the source relies on avoiding:
   write-back latency of the 32x32x16 bf16 product.
 
 Wait states are counted as one per instruction, s_nop N as N + 1.  The scan
-stops at labels and branches, so it covers each basic block on its own; the
-kernel keeps every product chain and its fence inside one block.
+follows the control flow: from each product forward along every fall-through
+and branch edge (s_branch has no fall-through; s_endpgm ends a path), and
+backward along every edge into the product, so a hazard that spans a branch
+(a result read on one side of a uniform if, say) is seen.
 
 2. The LDS-DMA loads of every kernel (global_load_lds, issued from inline
 assembly with an SGPR base): a vector memory instruction may read an SGPR
@@ -57,38 +59,55 @@ def _regs(text: str) -> set[tuple[str, int]]:
     return out
 
 
-def _instructions(asm: str, kernel_prefix: str) -> list[list[tuple[str, str]]]:
-    """Basic blocks of every function whose name starts with kernel_prefix,
-    as lists of (mnemonic, operand text)."""
-    blocks: list[list[tuple[str, str]]] = []
-    inside = False
-    cur: list[tuple[str, str]] = []
-    for line in asm.splitlines():
-        if re.match(r"^_Z\w+:", line):
-            inside = line.startswith(kernel_prefix)
-            cur = []
-            continue
-        if not inside:
-            continue
+def _is_branch(mn: str) -> bool:
+    return mn.startswith("s_cbranch") or mn == "s_branch"
+
+
+def parse(lines) -> tuple[list[tuple[str, str]], list[list[int]]]:
+    """Instructions of one function body (a list of assembly lines) and the
+    successors of each: the next instruction unless it is an unconditional
+    branch or ends the program, plus the target of a branch."""
+    instrs: list[tuple[str, str]] = []
+    labels: dict[str, int] = {}
+    for line in lines:
         s = line.split(";", 1)[0].strip()
         if not s:
             continue
-        if s.endswith(":") or s.startswith("."):
-            if cur:
-                blocks.append(cur)
-            cur = []
-            if s.startswith(".Lfunc_end"):
-                inside = False
+        if s.endswith(":"):
+            labels[s[:-1]] = len(instrs)
+            continue
+        if s.startswith("."):
             continue
         parts = s.split(None, 1)
-        mn, ops = parts[0], parts[1] if len(parts) > 1 else ""
-        cur.append((mn, ops))
-        if mn.startswith("s_cbranch") or mn in ("s_branch", "s_endpgm", "s_setpc_b64"):
-            blocks.append(cur)
-            cur = []
-    if cur:
-        blocks.append(cur)
-    return blocks
+        instrs.append((parts[0], parts[1] if len(parts) > 1 else ""))
+    succ: list[list[int]] = []
+    for i, (mn, ops) in enumerate(instrs):
+        nxt = []
+        if mn not in ("s_branch", "s_endpgm", "s_setpc_b64") and i + 1 < len(instrs):
+            nxt.append(i + 1)
+        if _is_branch(mn):
+            target = ops.split(",")[0].strip()
+            if target in labels and labels[target] < len(instrs):
+                nxt.append(labels[target])
+        succ.append(nxt)
+    return instrs, succ
+
+
+def _preds(succ: list[list[int]]) -> list[list[int]]:
+    pred: list[list[int]] = [[] for _ in succ]
+    for i, nx in enumerate(succ):
+        for j in nx:
+            pred[j].append(i)
+    return pred
+
+
+def _functions(asm: str, kernel_prefix: str) -> list[list[str]]:
+    """Body lines of every function whose name starts with kernel_prefix."""
+    out = []
+    for m in re.finditer(r"^(_Z\w+):", asm, re.M):
+        if m.group(1).startswith(kernel_prefix):
+            out.append(asm[m.end():asm.find(".Lfunc_end", m.end())].splitlines())
+    return out
 
 
 def _wait_states(mn: str, ops: str) -> int:
@@ -106,42 +125,60 @@ def _dst(ops: str) -> set[tuple[str, int]]:
     return _regs(first)
 
 
-def check(blocks) -> list[str]:
+def _walk(start: list[int], edges: list[list[int]], budget: int, visit) -> None:
+    """Every instruction reachable from `start` along `edges` with fewer than
+    `budget` wait states between it and the origin; visit(j, ws) returns
+    False to stop the path there.  Each instruction is entered again only by
+    a path with fewer wait states than before."""
+    best: dict[int, int] = {}
+    stack = [(j, 0) for j in start]
+    while stack:
+        j, ws = stack.pop()
+        if ws >= budget or best.get(j, budget) <= ws:
+            continue
+        best[j] = ws
+        if visit(j, ws):
+            stack.extend((k, ws + visit.cost(j)) for k in edges[j])
+
+
+def check(lines) -> list[str]:
+    """Matrix-core hazards in one function body (assembly lines)."""
+    instrs, succ = parse(lines)
+    pred = _preds(succ)
     problems = []
-    for blk in blocks:
-        for i, (mn, ops) in enumerate(blk):
-            if not mn.startswith("v_mfma"):
-                continue
-            fields = [f.strip() for f in ops.split(",")]
-            dst, srcs = _regs(fields[0]), set()
-            for f in fields[1:4]:
-                srcs |= _regs(f)
-            # VALU writes shortly before the product
-            ws = 0
-            for j in range(i - 1, -1, -1):
-                pm, pops = blk[j]
-                if ws >= VALU_TO_MFMA:
-                    break
-                if _is_valu(pm) and _dst(pops) & srcs:
-                    problems.append(f"{pm} {pops} -> {mn} {ops} after {ws} wait states")
-                ws += _wait_states(pm, pops)
-            # uses of the result before it has drained
-            ws = 0
-            for j in range(i + 1, len(blk)):
-                nm, nops = blk[j]
-                if ws >= MFMA_DRAIN:
-                    break
-                if nm.startswith("v_mfma"):
-                    nf = [f.strip() for f in nops.split(",")]
-                    same_chain = _regs(nf[0]) == dst and _regs(nf[3]) == dst
-                    touches = (_regs(nf[0]) | _regs(nf[1]) | _regs(nf[2]) | _regs(nf[3])) & dst
-                    if touches and not same_chain:
-                        problems.append(f"{mn} {ops} -> {nm} {nops} after {ws} wait states")
-                    if same_chain:
-                        break  # the chain's next link takes over the result
-                elif _regs(nops) & dst:
+    for i, (mn, ops) in enumerate(instrs):
+        if not mn.startswith("v_mfma"):
+            continue
+        fields = [f.strip() for f in ops.split(",")]
+        dst, srcs = _regs(fields[0]), set()
+        for f in fields[1:4]:
+            srcs |= _regs(f)
+
+        # VALU writes shortly before the product, along every path into it
+        def back(j, ws):
+            pm, pops = instrs[j]
+            if _is_valu(pm) and _dst(pops) & srcs:
+                problems.append(f"{pm} {pops} -> {mn} {ops} after {ws} wait states")
+            return True
+        back.cost = lambda j: _wait_states(*instrs[j])
+        _walk(pred[i], pred, VALU_TO_MFMA, back)
+
+        # uses of the result before it has drained, along every path out of it
+        def fwd(j, ws):
+            nm, nops = instrs[j]
+            if nm.startswith("v_mfma"):
+                nf = [f.strip() for f in nops.split(",")]
+                same_chain = _regs(nf[0]) == dst and _regs(nf[3]) == dst
+                touches = (_regs(nf[0]) | _regs(nf[1]) | _regs(nf[2]) | _regs(nf[3])) & dst
+                if touches and not same_chain:
                     problems.append(f"{mn} {ops} -> {nm} {nops} after {ws} wait states")
-                ws += _wait_states(nm, nops)
+                if same_chain:
+                    return False  # the chain's next link takes over the result
+            elif _regs(nops) & dst:
+                problems.append(f"{mn} {ops} -> {nm} {nops} after {ws} wait states")
+            return True
+        fwd.cost = lambda j: _wait_states(*instrs[j])
+        _walk(succ[i], succ, MFMA_DRAIN, fwd)
     return problems
 
 
@@ -159,9 +196,13 @@ def latent_asm(tmp_path_factory):
     return out.read_text()
 
 
+LATENT = "_ZN2pa12_GLOBAL__N_123latent_partition_kernel"
+
+
 def test_latent_kernel_has_products(latent_asm):
-    blocks = _instructions(latent_asm, "_ZN2pa12_GLOBAL__N_123latent_partition_kernel")
-    n = sum(1 for b in blocks for mn, _ in b if mn.startswith("v_mfma"))
+    fns = _functions(latent_asm, LATENT)
+    assert len(fns) == 3
+    n = sum(1 for f in fns for mn, _ in parse(f)[0] if mn.startswith("v_mfma"))
     # three instantiations (1, 2 and 4 head tiles): per unit 36 / KS score
     # products (the wave's share of its tile's contraction, KS = 4 / tiles)
     # and 8 value products per head tile
@@ -169,26 +210,45 @@ def test_latent_kernel_has_products(latent_asm):
 
 
 def test_latent_kernel_mfma_hazards(latent_asm):
-    blocks = _instructions(latent_asm, "_ZN2pa12_GLOBAL__N_123latent_partition_kernel")
-    problems = check(blocks)
+    problems = []
+    for body in _functions(latent_asm, LATENT):
+        problems += check(body)
     assert not problems, "\n".join(problems[:20])
 
 
 def test_checker_catches_planted_hazards():
     """The checker itself flags a VALU write right before a product and a
-    read of a product's result before it drains, and passes a fenced chain."""
-    bad = [[("v_mov_b32", "v4, 0"),
-            ("v_mfma_f32_32x32x16_bf16", "v[10:25], v[2:5], v[6:9], 0")]]
-    assert check(bad)
-    bad2 = [[("v_mfma_f32_32x32x16_bf16", "v[10:25], v[2:5], v[6:9], 0"),
-             ("v_add_f32_e32", "v30, v10, v11")]]
-    assert check(bad2)
-    ok = [[("v_mfma_f32_32x32x16_bf16", "v[10:25], v[2:5], v[6:9], 0"),
-           ("ds_read_b128", "v[2:5], v40"),
-           ("v_mfma_f32_32x32x16_bf16", "v[10:25], v[26:29], v[6:9], v[10:25]"),
-           ("s_nop", "7"), ("s_nop", "7"), ("s_nop", "7"), ("s_nop", "7"),
-           ("v_add_f32_e32", "v30, v10, v11")]]
+    read of a product's result before it drains, also across a branch, and
+    passes a fenced chain."""
+    assert check(["v_mov_b32 v4, 0", "v_mfma_f32_32x32x16_bf16 v[10:25], v[2:5], v[6:9], 0"])
+    assert check(["v_mfma_f32_32x32x16_bf16 v[10:25], v[2:5], v[6:9], 0",
+                  "v_add_f32_e32 v30, v10, v11"])
+    ok = ["v_mfma_f32_32x32x16_bf16 v[10:25], v[2:5], v[6:9], 0",
+          "ds_read_b128 v[2:5], v40",
+          "v_mfma_f32_32x32x16_bf16 v[10:25], v[26:29], v[6:9], v[10:25]",
+          "s_nop 7", "s_nop 7", "s_nop 7", "s_nop 7",
+          "v_add_f32_e32 v30, v10, v11"]
     assert not check(ok)
+    # the read sits behind a taken branch: a block-local scan would miss it
+    cross = ["v_mfma_f32_32x32x16_bf16 a[0:15], v[2:5], v[6:9], a[0:15]",
+             "s_cbranch_scc1 .LBB0_2",
+             "s_nop 7", "s_nop 7", "s_nop 7", "s_nop 7",
+             ".LBB0_2:",
+             "v_accvgpr_read_b32 v30, a3"]
+    assert check(cross)
+    # ... and one on the fall-through side of an unconditional branch is not
+    # reachable from the product
+    dead = ["v_mfma_f32_32x32x16_bf16 a[0:15], v[2:5], v[6:9], a[0:15]",
+            "s_branch .LBB0_3",
+            "v_accvgpr_read_b32 v30, a3",
+            ".LBB0_3:",
+            "s_nop 7", "s_nop 7", "s_nop 7", "s_nop 7",
+            "v_accvgpr_read_b32 v31, a4"]
+    assert not check(dead)
+    # a VALU write reaching the product through a branch edge
+    into = ["v_mov_b32 v4, 0", "s_cbranch_vccz .LBB0_5", "s_nop 7", ".LBB0_5:",
+            "v_mfma_f32_32x32x16_bf16 v[10:25], v[2:5], v[6:9], 0"]
+    assert check(into)
 
 
 # ---- 2. VALU-written SGPR read by an LDS-DMA load ---------------------------
@@ -209,27 +269,22 @@ def _sregs(text: str) -> set[int]:
 
 def sgpr_dma_hazards(lines: list[str]) -> list[str]:
     """Each global_load_lds whose SGPR operands a VALU instruction wrote fewer
-    than VALU_SGPR_TO_VMEM wait states before (within its basic block)."""
+    than VALU_SGPR_TO_VMEM wait states before, along any path into it."""
+    instrs, succ = parse(lines)
+    pred = _preds(succ)
     problems = []
-    text = [l.split(";", 1)[0].strip() for l in lines]
-    for i, l in enumerate(text):
-        if not l.startswith("global_load_lds"):
+    for i, (mn, ops) in enumerate(instrs):
+        if not mn.startswith("global_load_lds"):
             continue
-        ops = l.split(None, 1)[1] if " " in l else ""
         need = _sregs(ops.split(",", 1)[1] if "," in ops else "")
-        ws = 0
-        for j in range(i - 1, -1, -1):
-            p = text[j]
-            if not p:
-                continue
-            if p.endswith(":") or p.startswith(".") or p.startswith("s_cbranch") or p == "s_branch":
-                break
-            if ws >= VALU_SGPR_TO_VMEM:
-                break
-            mn = p.split()[0]
-            if _is_valu(mn) and " " in p and _sregs(p.split(None, 1)[1].split(",", 1)[0]) & need:
-                problems.append(f"{p} -> {l} after {ws} wait states")
-            ws += _wait_states(mn, p.split(None, 1)[1] if " " in p else "")
+
+        def back(j, ws):
+            pm, pops = instrs[j]
+            if _is_valu(pm) and _sregs(pops.split(",", 1)[0]) & need:
+                problems.append(f"{pm} {pops} -> {mn} {ops} after {ws} wait states")
+            return True
+        back.cost = lambda j: _wait_states(*instrs[j])
+        _walk(pred[i], pred, VALU_SGPR_TO_VMEM, back)
     return problems
 
 
@@ -260,7 +315,8 @@ def test_lds_dma_sgpr_operands_settled(all_kernel_asm):
     assert any("global_load_lds_dwordx4" in a for a in all_kernel_asm.values())
     problems = []
     for src, text in all_kernel_asm.items():
-        problems += [f"{src}: {p}" for p in sgpr_dma_hazards(text.splitlines())]
+        for body in _functions(text, "_Z"):
+            problems += [f"{src}: {p}" for p in sgpr_dma_hazards(body)]
     assert not problems, "\n".join(problems[:20])
 
 
@@ -272,6 +328,9 @@ def test_sgpr_checker_catches_planted_hazard():
     assert not sgpr_dma_hazards(ok)
     salu = ["s_add_u32 s6, s6, s8", "global_load_lds_dwordx4 v1, s[6:7] nt"]
     assert not sgpr_dma_hazards(salu)
+    across = ["v_readlane_b32 s7, v248, 26", "s_cbranch_scc1 .LBB1_4", "s_nop 7", ".LBB1_4:",
+              "global_load_lds_dword v0, s[6:7]"]
+    assert sgpr_dma_hazards(across)
 
 
 # 3. Serialized loads.  An empty asm that takes a just-loaded value as an

@@ -207,20 +207,36 @@ def test_p6_scores_beyond_exp_range_stay_finite():
     assert np.array_equal(got, V[0, 0].astype(np.float64))
 
 
+def _tile_stats(q, K, V, scale):
+    """One tile on its own: its largest score m, l = sum of exp(s - m) over
+    the tile, and the tile's own normalised output."""
+    sc = (K @ q) * scale
+    m = float(sc.max())
+    e = np.exp(sc - m)
+    l = float(e.sum())
+    return (e @ V) / l, m, l
+
+
+def _fold(a, b):
+    """Combine two (normalised output, max, sum) triples over disjoint token
+    sets into the triple of their union: the running max is the larger max,
+    each side's sum is re-referenced to it, and the outputs mix in proportion
+    to the re-referenced sums ('Étape 2: softmax en carreaux' keeps exactly
+    this pair of running statistics while it walks the tiles)."""
+    (oa, ma, la), (ob, mb, lb) = a, b
+    m = max(ma, mb)
+    wa, wb = la * math.exp(ma - m), lb * math.exp(mb - m)
+    return (wa * oa + wb * ob) / (wa + wb), m, wa + wb
+
+
 def _tiled_attention(q, K, V, scale, tile):
-    """Running-max / running-sum softmax over tiles of K, V (the tiled softmax
-    of 'Étape 2: softmax en carreaux'), one query vector, float64."""
-    m, s = -math.inf, 0.0
-    out = np.zeros(V.shape[1])
+    """One query vector over K, V cut into tiles of `tile` tokens: every
+    tile's statistics formed alone, then folded left to right, float64."""
+    acc = None
     for start in range(0, K.shape[0], tile):
-        sc = (K[start:start + tile] @ q) * scale
-        new_m = max(m, sc.max())
-        old = math.exp(m - new_m) if m != -math.inf else 0.0
-        e = np.exp(sc - new_m)
-        s = s * old + e.sum()
-        out = out * old + e @ V[start:start + tile]
-        m = new_m
-    return out / s, m, s
+        t = _tile_stats(q, K[start:start + tile], V[start:start + tile], scale)
+        acc = t if acc is None else _fold(acc, t)
+    return acc
 
 
 def _merge_partitions(parts):
