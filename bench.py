@@ -46,6 +46,36 @@ KERNEL_SOURCES = ["grouped_decode.hip", "gqa_mfma_decode.hip", "latent_decode.hi
                   "mxfp8_append.hip", "device_common.h", "plan.cpp", "plan.h"]
 
 
+FLUSH_BYTES = 512 << 20
+GROUPED = "grouped_partition_kernel + stream_reduce_kernel"
+GROUPED_MFMA = "gqa_mfma_partition_kernel + stream_reduce_kernel"
+
+
+def kernel_name(spec, mx: bool, q_len: int, window: int) -> str:
+    """The kernels one decode call of this run launches (the partition kernel
+    dominates; the reduce is 2-10% of the time)."""
+    if spec.mla:
+        return "latent_partition_kernel + latent_reduce_kernel"
+    if mx:
+        return "gqa_mfma_partition_kernel (MXFP8 operands) + stream_reduce_kernel"
+    if q_len > 1:
+        return GROUPED_MFMA
+    if spec.dtype == "bf16" and spec.head_dim_k == 128 and os.environ.get("PA_GQA_MFMA", "0") not in ("", "0"):
+        return GROUPED_MFMA
+    return GROUPED
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
@@ -137,7 +167,7 @@ def multi_oracle_check(w, L1, got, q_host, decode_bytes, args, oracle, mx):
     cpu = None
     if not args.no_cpu_baseline:
         cpu = {"value": round(decode_bytes * frac / cpu_s / 1e9, 3), "unit": "GB/s",
-               "cores": oracle.default_threads(), "kind": "oracle",
+               "cores": oracle.default_threads(), "cpu_model": cpu_model(), "kind": "oracle",
                "sample": f"oracle decode of {len(seqs)} of the {spec.num_seqs} sequences x {Q} "
                          f"queries x all heads ({frac:.1%} of the attended tokens), fp64, "
                          f"{cpu_s:.2f} s wall; GB/s over that sample's share of the bytes",
@@ -165,7 +195,7 @@ def window_oracle_check(w, L1, got, window, decode_bytes, args, oracle):
     cpu = None
     if not args.no_cpu_baseline:
         cpu = {"value": round(decode_bytes * frac / cpu_s / 1e9, 3), "unit": "GB/s", "cores": 1,
-               "kind": "oracle",
+               "cpu_model": cpu_model(), "kind": "oracle",
                "sample": f"numpy oracle windowed decode of {len(seqs)} of the {spec.num_seqs} "
                          f"sequences ({frac:.1%} of the attended tokens), fp64, {cpu_s:.2f} s "
                          f"wall; GB/s over that sample's share of the bytes",
@@ -195,7 +225,7 @@ def mx_oracle_check(w, L1, got, decode_bytes, args, oracle):
     cpu = None
     if not args.no_cpu_baseline:
         cpu = {"value": round(decode_bytes * frac / cpu_s / 1e9, 3), "unit": "GB/s",
-               "cores": threads, "kind": "oracle",
+               "cores": threads, "cpu_model": cpu_model(), "kind": "oracle",
                "sample": f"oracle MXFP8 decode of {len(seqs)} of the {spec.num_seqs} sequences "
                          f"({frac:.1%} of the attended tokens, all {spec.num_q_heads} heads), "
                          f"fp64, {cpu_s:.2f} s wall; GB/s over that sample's share of the bytes",
@@ -231,7 +261,7 @@ def native_oracle_check(w, L1, got, decode_bytes, args, oracle):
         times.append(time.perf_counter() - t_c)
     cpu_s = float(np.median(times))
     cpu = {"value": round(decode_bytes / cpu_s / 1e9, 3), "unit": "GB/s",
-           "cores": threads, "kind": "oracle",
+           "cores": threads, "cpu_model": cpu_model(), "kind": "oracle",
            "sample": f"the full decode of the {args.config} batch "
                      f"({spec.num_seqs} seqs x {spec.num_q_heads} heads), fp64, "
                      f"median of 3 runs, {cpu_s:.2f} s wall each",
@@ -367,12 +397,27 @@ def main() -> int:
         append()
         decode()
 
+    # L2 (4 MB per XCD) and MALL (256 MB) flush: a plain kernel write of
+    # 512 MiB between the cold repetitions below, outside their event pairs.
+    flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+
+    def flush():
+        flush_buf.fill_(7)
+
+    # Clock ramp: the GPU runs its first few hundred ms of work at lower
+    # clocks, so flush writes (not steps of the hot path) run for ~0.5 s first.
+    t_ramp = time.perf_counter()
+    while time.perf_counter() - t_ramp < 0.5:
+        for _ in range(20):
+            flush()
+        torch.cuda.synchronize()
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # Timed region: K steps; events on torch's current stream, which is the
-    # stream the binding hands to the library.
+    # Timed region: K steps back to back; events on torch's current stream,
+    # which is the stream the binding hands to the library.
     K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     start = torch.cuda.Event(enable_timing=True)
@@ -390,9 +435,47 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     total_ms = start.elapsed_time(end)
-    t_append = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    t_decode = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    t_append_warm = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    t_decode_warm = np.array([e[1].elapsed_time(e[2]) for e in ev])
     ms_per_step = total_ms / K
+
+    def cold_times(fn_append, fn_decode, reps):
+        """Per-call event times with L2 and MALL flushed before every call."""
+        ta, td = [], []
+        for _ in range(reps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            flush()
+            e[0].record()
+            fn_append()
+            e[1].record()
+            flush()
+            e[2].record()
+            fn_decode()
+            e[3].record()
+            torch.cuda.synchronize()
+            ta.append(e[0].elapsed_time(e[1]))
+            td.append(e[2].elapsed_time(e[3]))
+        return np.array(ta), np.array(td)
+
+    # The same K steps again, each call on cold caches: the per-kernel times
+    # the roofline is quoted on.
+    t_append, t_decode = cold_times(append, decode, K)
+
+    # The other grouped kernel on the same inputs, for comparison (the
+    # matrix-core variant of the single-query GQA decode).
+    alt = None
+    if kernel_name(spec, mx, Q, W) == GROUPED:
+        os.environ["PA_GQA_MFMA"] = "1"
+        try:
+            for _ in range(max(args.warmup, 3)):
+                decode()
+            _, t_alt = cold_times(lambda: None, decode, K)
+        finally:
+            del os.environ["PA_GQA_MFMA"]
+        alt = {"kernel": GROUPED_MFMA, "us_decode": round(float(np.mean(t_alt)) * 1e3, 2)}
+        decode()  # the default kernel's output for the oracle check below
+        torch.cuda.synchronize()
+    del flush_buf
 
     # accounting over the context actually attended (ctx + 1)
     # accounting over the tokens attended (the window's, with --window)
@@ -412,9 +495,13 @@ def main() -> int:
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     dec_ms = float(np.mean(t_decode))
     achieved = decode_bytes / (dec_ms * 1e-3) / 1e9
-    log(f"[bench] {K} steps: {ms_per_step * 1e3:.1f} us/step (append {np.mean(t_append) * 1e3:.1f}"
-        f" us, decode {dec_ms * 1e3:.1f} us); decode {achieved:.0f} GB/s = "
+    log(f"[bench] {K} steps: {ms_per_step * 1e3:.1f} us/step back to back (decode "
+        f"{np.mean(t_decode_warm) * 1e3:.1f} us); cold caches: append "
+        f"{np.mean(t_append) * 1e3:.1f} us, decode {dec_ms * 1e3:.1f} us = {achieved:.0f} GB/s = "
         f"{achieved / HBM_PEAK_GBS:.1%} of HBM peak")
+    if alt is not None:
+        alt["frac"] = round(decode_bytes / (alt["us_decode"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        log(f"[bench] {alt['kernel']}: decode {alt['us_decode']:.1f} us = {alt['frac']:.1%}")
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 4
@@ -472,14 +559,19 @@ def main() -> int:
         "q_len": Q,
         "us_append": round(float(np.mean(t_append)) * 1e3, 2),
         "us_decode": round(dec_ms * 1e3, 2),
+        "us_decode_median": round(float(np.median(t_decode)) * 1e3, 2),
         "us_decode_p10_p90": [round(float(np.percentile(t_decode, 10)) * 1e3, 2),
                               round(float(np.percentile(t_decode, 90)) * 1e3, 2)],
+        "us_decode_warm": round(float(np.mean(t_decode_warm)) * 1e3, 2),
+        "timing": "us_append / us_decode: per-call HIP events with L2 and MALL flushed "
+                  "(512 MiB written) before every call; us_decode_warm and ms_per_step: "
+                  "the K steps back to back",
         "decode_tflops": round(flops / (dec_ms * 1e-3) / 1e12, 3),
-        "roofline": {"bound": "hbm", "kernel": ("pa_decode_mxfp8" if mx else "pa_decode") +
-                     " (partition + log-sum-exp reduce)",
+        "roofline": {"bound": "hbm", "kernel": kernel_name(spec, mx, Q, W),
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": decode_bytes},
+        "other_kernel": alt,
         "cpu_baseline": cpu,
         "max_abs_err_vs_oracle": max_err,
         "wall_s_timed": round(wall, 4),

@@ -38,6 +38,14 @@
  *  - Undefined (not checked, the contract is the caller's): a slot or block id
  *    outside the pool, a context longer than max_blocks_per_seq * block_size,
  *    duplicate non-negative slots in one append, negative context lengths.
+ *  - Debug builds (libpa_debug.so, compiled with PA_DEBUG): every call first
+ *    runs a device pass over the index arrays it will use (slot_mapping;
+ *    context_lens and the block-table entries of the blocks it reads;
+ *    copy pairs), waits for the stream, and returns PA_ERR_INDEX, naming the
+ *    rule and the element, without enqueuing its own kernels when one is
+ *    broken (duplicates are looked for among the first 4096 slots or pairs).
+ *    Debug calls therefore synchronise and cannot be captured into a graph;
+ *    their results are bitwise those of the release build.
  *  - Results are deterministic: no atomics, bitwise identical run to run and
  *    independent of where the physical blocks sit in the pool.
  */
@@ -59,7 +67,8 @@ typedef enum pa_status {
     PA_ERR_UNSUPPORTED = 4, /* valid but outside the shapes the library runs */
     PA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
     PA_ERR_HIP = 6,         /* the HIP runtime reported an error */
-    PA_ERR_ALIGN = 7        /* a pointer or stride breaks the 16-byte alignment rule */
+    PA_ERR_ALIGN = 7,       /* a pointer or stride breaks the 16-byte alignment rule */
+    PA_ERR_INDEX = 8        /* PA_DEBUG builds only: an index array broke the contract */
 } pa_status;
 
 typedef enum pa_dtype {
@@ -396,6 +405,9 @@ int32_t pa_bm_take_copies(pa_block_manager *m, int32_t *src, int32_t *dst,
  */
 pa_status pa_copy_blocks(void *pool, int64_t block_bytes, const int32_t *src,
                          const int32_t *dst, int32_t num_pairs, void *stream);
+
+/* Build flags of the loaded library: bit 0 set in a PA_DEBUG build. */
+int32_t pa_build_flags(void);
 
 /* Static text for a status code ("PA_OK", ...); never NULL. */
 const char *pa_status_string(pa_status status);

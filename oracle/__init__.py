@@ -66,6 +66,10 @@ def _load(lib=None):
     if lib is not None:
         return lib
     if _lib is None:
+        override = os.environ.get("ORACLE_LIB")  # a rebuilt copy (sanitizer runs)
+        if override:
+            _lib = load_library(override)
+            return _lib
         if not os.path.exists(_LIB_PATH) or (
                 os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
             build(force=True)

@@ -16,20 +16,24 @@ from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa.so")
+# PA_DEBUG builds check every call's index arrays on the device first (and
+# synchronise); PA_DEBUG=1 in the environment selects it.
+DEBUG_LIB_PATH = os.path.join(_HERE, "libpa_debug.so")
 
 PA_F32, PA_BF16 = 0, 1
 STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_DTYPE",
-          4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP", 7: "PA_ERR_ALIGN"}
+          4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP", 7: "PA_ERR_ALIGN",
+          8: "PA_ERR_INDEX"}
 
 EXPORTS = ("pa_cache_append", "pa_decode_workspace_size", "pa_decode", "pa_cache_append_mxfp8",
            "pa_decode_mxfp8", "pa_decode_multi_workspace_size", "pa_decode_multi",
            "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free", "pa_bm_ref_count",
            "pa_bm_add_sequence", "pa_bm_append_token", "pa_bm_fork", "pa_bm_free_sequence",
            "pa_bm_num_tokens", "pa_bm_block_table", "pa_bm_take_copies", "pa_copy_blocks",
-           "pa_decode_ex", "pa_attention_scores",
+           "pa_decode_ex", "pa_attention_scores", "pa_build_flags",
            "pa_status_string", "pa_last_error")
 
-_lib = None
+_libs: dict = {}
 
 
 class PAError(RuntimeError):
@@ -39,13 +43,24 @@ class PAError(RuntimeError):
         self.detail = detail
 
 
+def library_path() -> str:
+    """The library calls go to: libpa.so, libpa_debug.so when PA_DEBUG is set
+    (to anything but 0), or the file PA_LIB names."""
+    if os.environ.get("PA_LIB"):
+        return os.environ["PA_LIB"]
+    if os.environ.get("PA_DEBUG", "0") not in ("", "0"):
+        return DEBUG_LIB_PATH
+    return LIB_PATH
+
+
 def lib():
     """The loaded ctypes library (built in-tree); raises if it is missing."""
-    global _lib
-    if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is not built; run python -m paged_kv_cache_58_amd.build")
-        L = ctypes.CDLL(LIB_PATH)
+    path = library_path()
+    L = _libs.get(path)
+    if L is None:
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is not built; run python -m paged_kv_cache_58_amd.build")
+        L = ctypes.CDLL(path)
         P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
         L.pa_cache_append.restype = ctypes.c_int
         L.pa_cache_append.argtypes = [P, P, P, I64, P, I64, P, I32, I32, I32, I32, I32, I32,
@@ -100,8 +115,14 @@ def lib():
         L.pa_status_string.argtypes = [ctypes.c_int]
         L.pa_last_error.restype = ctypes.c_char_p
         L.pa_last_error.argtypes = []
-        _lib = L
-    return _lib
+        L.pa_build_flags.restype = I32
+        L.pa_build_flags.argtypes = []
+        _libs[path] = L
+    return L
+
+
+def is_debug_build() -> bool:
+    return bool(lib().pa_build_flags() & 1)
 
 
 def _check(status: int) -> None:

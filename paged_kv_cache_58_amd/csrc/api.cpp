@@ -1,7 +1,6 @@
 // C ABI of libpa.so (declared in include/pa.h): argument checks, planning and
 // kernel launches on the caller's stream.  Only the pa_* symbols are exported.
-#include <hip/hip_runtime.h>
-
+#include <climits>
 #include <string>
 
 #include "launch.h"
@@ -9,6 +8,21 @@
 #include "plan.h"
 
 #define PA_EXPORT extern "C" __attribute__((visibility("default")))
+
+// PA_DEBUG builds check the call's index arrays on the device first (and
+// return PA_ERR_INDEX on a violation); release builds compile this to nothing.
+#ifdef PA_DEBUG
+#define PA_DEBUG_CHECK(call)                                  \
+    do {                                                      \
+        std::string dbg_why;                                  \
+        const pa_status dbg_st = (call);                      \
+        if (dbg_st != PA_OK) return finish(dbg_st, dbg_why);  \
+    } while (0)
+#else
+#define PA_DEBUG_CHECK(call) \
+    do {                     \
+    } while (0)
+#endif
 
 namespace {
 
@@ -21,7 +35,7 @@ pa_status finish(pa_status st, const std::string &why) {
 
 pa::DecodeShape make_shape(bool latent, int32_t num_seqs, int32_t num_q_heads,
                            int32_t num_kv_heads, int32_t head_dim_k, int32_t head_dim_v,
-                           int32_t block_size, int32_t max_blocks_per_seq, pa_dtype dtype) {
+                           int32_t block_size, int32_t max_blocks_per_seq, int32_t dtype) {
     pa::DecodeShape s{};
     s.num_seqs = num_seqs;
     s.num_q_heads = num_q_heads;
@@ -49,8 +63,11 @@ PA_EXPORT pa_status pa_cache_append(void *k_cache, void *v_cache, const void *k,
     std::string why;
     pa::AppendPlan plan{};
     pa_status st = pa::check_append(a, &plan, &why);
-    if (st != PA_OK) return finish(st, why);
-    st = pa::launch_append(a, plan, static_cast<hipStream_t>(stream), &why);
+    if (st != PA_OK || num_tokens == 0) return finish(st, why);
+    PA_DEBUG_CHECK(pa::debug_check_slots(slot_mapping, num_tokens,
+                                         static_cast<int64_t>(num_blocks) * block_size, stream,
+                                         &dbg_why));
+    st = pa::launch_append(a, plan, stream, &why);
     return finish(st, why);
 }
 
@@ -86,13 +103,16 @@ PA_EXPORT pa_status pa_decode(void *out, const void *q, const void *k_cache,
                            nullptr, scale, num_blocks, workspace, workspace_bytes};
     st = pa::check_decode(s, a, plan, &why);
     if (st != PA_OK || num_seqs == 0) return finish(st, why);
-    hipStream_t hs = static_cast<hipStream_t>(stream);
+    PA_DEBUG_CHECK(pa::debug_check_tables(block_tables, context_lens, num_seqs,
+                                          max_blocks_per_seq, block_size, 0, num_blocks,
+                                          static_cast<int64_t>(max_blocks_per_seq) * block_size,
+                                          stream, &dbg_why));
     if (plan.path == pa::DecodePath::kLatent)
-        st = pa::launch_latent_decode(s, a, plan, hs, &why);
+        st = pa::launch_latent_decode(s, a, plan, stream, &why);
     else if (plan.path == pa::DecodePath::kGroupedMfma)
-        st = pa::launch_gqa_mfma_decode(s, a, plan, hs, &why);
+        st = pa::launch_gqa_mfma_decode(s, a, plan, stream, &why);
     else
-        st = pa::launch_grouped_decode(s, a, plan, hs, &why);
+        st = pa::launch_grouped_decode(s, a, plan, stream, &why);
     return finish(st, why);
 }
 
@@ -109,7 +129,10 @@ PA_EXPORT pa_status pa_cache_append_mxfp8(void *k_cache, void *v_cache, void *k_
     std::string why;
     pa_status st = pa::check_append_mxfp8(a, &why);
     if (st != PA_OK || num_tokens == 0) return finish(st, why);
-    st = pa::launch_append_mxfp8(a, static_cast<hipStream_t>(stream), &why);
+    PA_DEBUG_CHECK(pa::debug_check_slots(slot_mapping, num_tokens,
+                                         static_cast<int64_t>(num_blocks) * block_size, stream,
+                                         &dbg_why));
+    st = pa::launch_append_mxfp8(a, stream, &why);
     return finish(st, why);
 }
 
@@ -132,7 +155,11 @@ PA_EXPORT pa_status pa_decode_mxfp8(void *out, const void *q, const void *k_cach
                            v_scale, scale, num_blocks, workspace, workspace_bytes};
     st = pa::check_decode(s, a, plan, &why);
     if (st != PA_OK || num_seqs == 0) return finish(st, why);
-    st = pa::launch_mxfp8_decode(s, a, plan, static_cast<hipStream_t>(stream), &why);
+    PA_DEBUG_CHECK(pa::debug_check_tables(block_tables, context_lens, num_seqs,
+                                          max_blocks_per_seq, block_size, 0, num_blocks,
+                                          static_cast<int64_t>(max_blocks_per_seq) * block_size,
+                                          stream, &dbg_why));
+    st = pa::launch_mxfp8_decode(s, a, plan, stream, &why);
     return finish(st, why);
 }
 
@@ -173,9 +200,12 @@ PA_EXPORT pa_status pa_decode_multi(void *out, const void *q, const void *k_cach
                            v_scale, scale, num_blocks, workspace, workspace_bytes};
     st = pa::check_decode(s, a, plan, &why);
     if (st != PA_OK || num_seqs == 0) return finish(st, why);
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    st = s.mxfp8 ? pa::launch_mxfp8_decode(s, a, plan, hs, &why)
-                 : pa::launch_gqa_mfma_decode(s, a, plan, hs, &why);
+    PA_DEBUG_CHECK(pa::debug_check_tables(block_tables, context_lens, num_seqs,
+                                          max_blocks_per_seq, block_size, 0, num_blocks,
+                                          static_cast<int64_t>(max_blocks_per_seq) * block_size,
+                                          stream, &dbg_why));
+    st = s.mxfp8 ? pa::launch_mxfp8_decode(s, a, plan, stream, &why)
+                 : pa::launch_gqa_mfma_decode(s, a, plan, stream, &why);
     return finish(st, why);
 }
 
@@ -202,9 +232,12 @@ PA_EXPORT pa_status pa_decode_ex(void *out, float *lse, const void *q, const voi
     a.lse = lse;
     st = pa::check_decode(s, a, plan, &why);
     if (st != PA_OK || num_seqs == 0) return finish(st, why);
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    st = plan.path == pa::DecodePath::kGroupedMfma ? pa::launch_gqa_mfma_decode(s, a, plan, hs, &why)
-                                                   : pa::launch_grouped_decode(s, a, plan, hs, &why);
+    PA_DEBUG_CHECK(pa::debug_check_tables(block_tables, context_lens, num_seqs,
+                                          max_blocks_per_seq, block_size, window, num_blocks,
+                                          static_cast<int64_t>(max_blocks_per_seq) * block_size,
+                                          stream, &dbg_why));
+    st = plan.path == pa::DecodePath::kGroupedMfma ? pa::launch_gqa_mfma_decode(s, a, plan, stream, &why)
+                                                   : pa::launch_grouped_decode(s, a, plan, stream, &why);
     return finish(st, why);
 }
 
@@ -235,10 +268,13 @@ PA_EXPORT pa_status pa_attention_scores(float *scores, const void *q, const void
         reinterpret_cast<uintptr_t>(scores) % 4 != 0 || reinterpret_cast<uintptr_t>(lse) % 4 != 0)
         return finish(PA_ERR_ALIGN, "scores: q and k_cache must be 16-byte aligned");
     std::string why;
+    PA_DEBUG_CHECK(pa::debug_check_tables(block_tables, context_lens, num_seqs,
+                                          max_blocks_per_seq, block_size, window, INT32_MAX,
+                                          max_context, stream, &dbg_why));
     const pa_status st = pa::launch_attention_scores(
         scores, q, k_cache, block_tables, context_lens, lse, scale, window, num_seqs, num_q_heads,
         num_kv_heads, head_dim, max_blocks_per_seq, max_context, dtype,
-        static_cast<hipStream_t>(stream), &why);
+        stream, &why);
     return finish(st, why);
 }
 
@@ -253,8 +289,9 @@ PA_EXPORT pa_status pa_copy_blocks(void *pool, int64_t block_bytes, const int32_
         reinterpret_cast<uintptr_t>(src) % 4 != 0 || reinterpret_cast<uintptr_t>(dst) % 4 != 0)
         return finish(PA_ERR_ALIGN, "copy_blocks: pool and block_bytes must be multiples of 16 bytes");
     std::string why;
+    PA_DEBUG_CHECK(pa::debug_check_copies(src, dst, num_pairs, stream, &dbg_why));
     const pa_status st = pa::launch_copy_blocks(pool, block_bytes, src, dst, num_pairs,
-                                                static_cast<hipStream_t>(stream), &why);
+                                                stream, &why);
     return finish(st, why);
 }
 
@@ -268,8 +305,17 @@ PA_EXPORT const char *pa_status_string(pa_status status) {
         case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
         case PA_ERR_HIP: return "PA_ERR_HIP";
         case PA_ERR_ALIGN: return "PA_ERR_ALIGN";
+        case PA_ERR_INDEX: return "PA_ERR_INDEX";
     }
     return "PA_ERR_UNKNOWN";
 }
 
 PA_EXPORT const char *pa_last_error(void) { return g_last_error.c_str(); }
+
+PA_EXPORT int32_t pa_build_flags(void) {
+#ifdef PA_DEBUG
+    return 1;
+#else
+    return 0;
+#endif
+}

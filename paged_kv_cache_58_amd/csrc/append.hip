@@ -10,6 +10,7 @@
 
 #include <cstdint>
 
+#include "hip_util.h"
 #include "launch.h"
 
 namespace pa {
@@ -65,8 +66,9 @@ void enqueue(const AppendArgs &a, const AppendPlan &p, hipStream_t stream) {
 
 }  // namespace
 
-pa_status launch_append(const AppendArgs &a, const AppendPlan &plan, hipStream_t stream,
+pa_status launch_append(const AppendArgs &a, const AppendPlan &plan, void *stream_arg,
                         std::string *why) {
+    const hipStream_t stream = static_cast<hipStream_t>(stream_arg);
     if (a.num_tokens == 0) return PA_OK;
     switch (plan.vec_bytes) {
         case 16: enqueue<16>(a, plan, stream); break;

@@ -25,6 +25,7 @@
 #include <cstdint>
 
 #include "device_common.h"
+#include "hip_util.h"
 #include "launch.h"
 
 namespace pa {
@@ -101,8 +102,9 @@ pa_status launch_attention_scores(float *scores, const void *q, const void *k_ca
                                   const int32_t *block_tables, const int32_t *context_lens,
                                   const float *lse, float scale, int32_t window, int32_t num_seqs,
                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                  int32_t max_blocks_per_seq, int32_t max_context, pa_dtype dtype,
-                                  hipStream_t stream, std::string *why) {
+                                  int32_t max_blocks_per_seq, int32_t max_context, int32_t dtype,
+                                  void *stream_arg, std::string *why) {
+    const hipStream_t stream = static_cast<hipStream_t>(stream_arg);
     const int group = num_q_heads / num_kv_heads;
     if (dtype == PA_BF16) {
         if (head_dim == 64)

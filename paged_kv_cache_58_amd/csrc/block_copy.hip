@@ -8,6 +8,7 @@
 
 #include <cstdint>
 
+#include "hip_util.h"
 #include "launch.h"
 
 namespace pa {
@@ -29,8 +30,9 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(char *__restrict__ poo
 }  // namespace
 
 pa_status launch_copy_blocks(void *pool, int64_t block_bytes, const int32_t *src,
-                             const int32_t *dst, int32_t num_pairs, hipStream_t stream,
+                             const int32_t *dst, int32_t num_pairs, void *stream_arg,
                              std::string *why) {
+    const hipStream_t stream = static_cast<hipStream_t>(stream_arg);
     if (num_pairs == 0) return PA_OK;
     const int64_t vecs = block_bytes / 16;
     const int64_t per = (vecs + 255) / 256;

@@ -58,6 +58,7 @@
 #include <cstdint>
 
 #include "device_common.h"
+#include "hip_util.h"
 #include "launch.h"
 
 namespace pa {
@@ -559,12 +560,14 @@ pa_status launch_mfma(const DecodeShape &s, const DecodeArgs &a, const DecodePla
 }  // namespace
 
 pa_status launch_gqa_mfma_decode(const DecodeShape &s, const DecodeArgs &a, const DecodePlan &p,
-                                 hipStream_t stream, std::string *why) {
+                                 void *stream_arg, std::string *why) {
+    const hipStream_t stream = static_cast<hipStream_t>(stream_arg);
     return launch_mfma<false>(s, a, p, stream, why);
 }
 
 pa_status launch_mxfp8_decode(const DecodeShape &s, const DecodeArgs &a, const DecodePlan &p,
-                              hipStream_t stream, std::string *why) {
+                              void *stream_arg, std::string *why) {
+    const hipStream_t stream = static_cast<hipStream_t>(stream_arg);
     return launch_mfma<true>(s, a, p, stream, why);
 }
 

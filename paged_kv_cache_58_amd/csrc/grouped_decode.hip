@@ -45,6 +45,7 @@
 #include <cstdint>
 
 #include "device_common.h"
+#include "hip_util.h"
 #include "launch.h"
 
 namespace pa {
@@ -533,7 +534,8 @@ pa_status enqueue_grouped_g(const DecodeShape &s, const DecodeArgs &a, const Dec
 }  // namespace
 
 pa_status launch_grouped_decode(const DecodeShape &s, const DecodeArgs &a, const DecodePlan &p,
-                                hipStream_t stream, std::string *why) {
+                                void *stream_arg, std::string *why) {
+    const hipStream_t stream = static_cast<hipStream_t>(stream_arg);
     if (s.num_seqs == 0) return PA_OK;
     const float scale_log2 = static_cast<float>(static_cast<double>(a.scale) * 1.4426950408889634);
     if (s.dtype == PA_BF16) {

@@ -55,6 +55,7 @@
 #include <cstdint>
 
 #include "device_common.h"
+#include "hip_util.h"
 #include "launch.h"
 
 namespace pa {
@@ -864,7 +865,8 @@ pa_status enqueue_latent(const DecodeShape &s, const DecodeArgs &a, const Decode
 }  // namespace
 
 pa_status launch_latent_decode(const DecodeShape &s, const DecodeArgs &a, const DecodePlan &p,
-                               hipStream_t stream, std::string *why) {
+                               void *stream_arg, std::string *why) {
+    const hipStream_t stream = static_cast<hipStream_t>(stream_arg);
     if (s.num_seqs == 0) return PA_OK;
     const float scale_log2 = static_cast<float>(static_cast<double>(a.scale) * 1.4426950408889634);
     switch (latent_head_tiles(s.num_q_heads)) {

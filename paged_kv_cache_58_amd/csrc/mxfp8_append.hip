@@ -23,6 +23,7 @@
 #include <cstdint>
 
 #include "device_common.h"
+#include "hip_util.h"
 #include "launch.h"
 
 namespace pa {
@@ -117,7 +118,8 @@ __global__ __launch_bounds__(kWave) void mx_append_kernel(
 
 }  // namespace
 
-pa_status launch_append_mxfp8(const MxAppendArgs &a, hipStream_t stream, std::string *why) {
+pa_status launch_append_mxfp8(const MxAppendArgs &a, void *stream_arg, std::string *why) {
+    const hipStream_t stream = static_cast<hipStream_t>(stream_arg);
     if (a.num_tokens == 0) return PA_OK;
     const dim3 grid(a.num_tokens, a.num_kv_heads);
     uint8_t *k8 = static_cast<uint8_t *>(a.k_cache);

@@ -11,9 +11,11 @@ constexpr size_t kWorkspaceAlign = 256;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-int elt_bytes(pa_dtype d) { return d == PA_F32 ? 4 : 2; }
+int elt_bytes(int32_t d) { return d == PA_F32 ? 4 : 2; }
 
-bool valid_dtype(pa_dtype d) { return d == PA_F32 || d == PA_BF16; }
+// A caller passing an int that is no pa_dtype value must get PA_ERR_DTYPE,
+// so the value is compared as an integer, never loaded as the enum.
+bool valid_dtype(int32_t d) { return d == PA_F32 || d == PA_BF16; }
 
 pa_status fail(pa_status st, std::string *why, const std::string &msg) {
     if (why) *why = msg;

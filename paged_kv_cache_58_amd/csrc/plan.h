@@ -26,7 +26,7 @@ struct AppendArgs {
     int32_t num_kv_heads;
     int32_t head_dim_k;
     int32_t head_dim_v;
-    pa_dtype dtype;
+    int32_t dtype;  // a pa_dtype value, kept as an integer until validated
 };
 
 // Launch shape of the append copy: the widest vector (bytes) that divides both
@@ -59,7 +59,7 @@ struct MxAppendArgs {
     int32_t block_size;
     int32_t num_kv_heads;
     int32_t head_dim;
-    pa_dtype dtype;  // of k and v
+    int32_t dtype;  // of k and v (a pa_dtype value, kept as an integer until validated)
 };
 
 pa_status check_append_mxfp8(const MxAppendArgs &a, std::string *why);
@@ -95,7 +95,7 @@ struct DecodeShape {
     int32_t max_blocks_per_seq;
     bool latent;  // v_cache == NULL
     bool mxfp8;   // MXFP8 caches (dtype is then that of q and out)
-    pa_dtype dtype;
+    int32_t dtype;  // a pa_dtype value, kept as an integer until validated
     int32_t q_len = 1;  // new query tokens per sequence, causal among themselves
     int32_t window = 0; // > 0: attend only to the last `window` tokens (sliding window)
 };

@@ -99,6 +99,21 @@ def test_workspace_size():
     assert pa.decode_workspace_size(64, 128, 1, 576, 512, 64, 129) > 0
 
 
+@pytest.mark.parametrize("hkv,dk,dv,bs,hq", [
+    (8, 256, 128, 16, 64),   # d_k != d_v outside the latent shape
+    (1, 576, 256, 64, 128),  # not V = the first 512 latent dims
+    (2, 576, 512, 64, 128),  # the latent shape needs one shared KV head
+    (1, 576, 512, 16, 128),  # and 64-token blocks
+    (1, 576, 512, 64, 136),  # and at most 128 query heads
+    (8, 128, 64, 16, 64),
+])
+def test_workspace_size_latent_only_for_the_latent_shape(hkv, dk, dv, bs, hq):
+    """pa_decode_workspace_size takes d_k != d_v to mean latent mode, the one
+    shape with unequal head dims; every other unequal pair is unsupported and
+    sizes to 0 rather than being planned as something else."""
+    assert pa.decode_workspace_size(64, hq, hkv, dk, dv, bs, 129) == 0
+
+
 def _append(**kw):
     a = dict(kc=FAKE, vc=FAKE, k=FAKE, ks=1024, v=FAKE, vs=1024, sm=FAKE, n=4, nb=10, bs=16,
              hkv=8, dk=128, dv=128, dtype=pa.PA_BF16)

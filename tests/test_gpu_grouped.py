@@ -228,13 +228,10 @@ def test_full_config_parity(dev, name):
     stats = compare(d.decode(), oracle.decode_workload(w), "bf16")
     say(f"  {name}: {stats}")
     hk, hv = _append_bitwise(d)
-    say(f"  {name}: append bit-exact; decode(ctx+1) on sampled rows")
+    say(f"  {name}: append bit-exact; decode(ctx+1) vs oracle on every row")
     L1 = w.context_lens + 1
     out = d.decode(context_lens=torch.from_numpy(L1).to(dev))
-    rng = np.random.default_rng(0)
-    rows = [(int(b), int(h)) for b, h in zip(rng.integers(0, w.spec.num_seqs, 64),
-                                             rng.integers(0, w.spec.num_q_heads, 64))]
-    ref = oracle.decode(w.q, hk, hv, w.block_tables, L1, w.scale, pairs=rows)
-    say(f"  {name}: {compare(out, ref, 'bf16', rows=rows)}")
+    ref = oracle.decode(w.q, hk, hv, w.block_tables, L1, w.scale)
+    say(f"  {name}: {compare(out, ref, 'bf16')}")
     del d
     torch.cuda.empty_cache()

@@ -44,7 +44,7 @@ def test_latent_parity_small(dev, hq, ctx):
 
 
 def test_latent_rescale_heavy(dev):
-    say("case: latent, scale 1 (wide score range)")
+    say("case: latent, scale 0.5 (wide score range)")
     w = make_workload(_spec(64, [900, 333], scale=0.5), seed=3)
     d = to_device(w, dev)
     say(f"  {compare(d.decode(), oracle.decode_workload(w), 'bf16')}")
@@ -106,12 +106,23 @@ def test_latent_append_then_decode(dev):
 
 
 def test_config5_full(dev):
-    say("case: full config c5 (MLA latent decode)")
+    """The latent workload at full size: decode(ctx) on every (sequence, head)
+    row, the append of each sequence's new latent row bit-exact over the
+    whole pool, then decode(ctx + 1) on every row."""
+    say("case: full config c5 (MLA latent decode): decode(ctx) vs oracle on every row")
     w = make_workload("c5")
     d = to_device(w, dev)
-    rng = np.random.default_rng(0)
-    rows = [(int(b), int(h)) for b, h in zip(rng.integers(0, 64, 256), rng.integers(0, 128, 256))]
-    ref = oracle.decode_workload(w, pairs=rows)
-    say(f"  c5 sampled rows: {compare(d.decode(), ref, 'bf16', rows=rows)}")
+    say(f"  c5: {compare(d.decode(), oracle.decode_workload(w), 'bf16')}")
+    hk = w.k_cache.copy()
+    oracle.append(hk, None, w.k_new, None, w.slot_mapping)
+    d.append()
+    torch.cuda.synchronize()
+    assert np.array_equal(host_array(d.k_cache).view(np.uint8), hk.view(np.uint8)), \
+        "latent pool differs after append"
+    say("  c5: append bit-exact; decode(ctx+1) vs oracle on every row")
+    L1 = w.context_lens + 1
+    out = d.decode(context_lens=torch.from_numpy(L1).to(dev))
+    ref = oracle.decode(w.q, hk, None, w.block_tables, L1, w.scale, head_dim_v=512)
+    say(f"  c5: {compare(out, ref, 'bf16')}")
     del d
     torch.cuda.empty_cache()
