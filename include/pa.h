@@ -160,6 +160,30 @@ pa_status pa_decode(void *out, const void *q, const void *k_cache,
                     void *stream);
 
 /*
+ * pa_decode_noalloc — pa_decode without a workspace argument, for callers
+ * that cannot allocate device memory (code under graph capture, tight
+ * serving loops, harnesses that forbid allocation).  The same kernels and
+ * results as pa_decode (bitwise); the split-context partials go to a scratch
+ * array of 32 MiB that the library holds on each GPU it runs on until the
+ * process ends (the first call on a device looks its address up; no call
+ * allocates or frees anything).  Sizes whose pa_decode_workspace_size
+ * exceeds 32 MiB return PA_ERR_WORKSPACE without enqueuing anything: the
+ * grouped shapes fit up to 496 sequences of 64/8 heads (any context
+ * length), the latent shape, whose workspace holds 512 partial slots of
+ * every head, does not fit.  Every call on one GPU uses
+ * that GPU's one array: calls that overlap on a device (two streams, two
+ * threads) race and must be ordered by the caller.  Arguments and errors
+ * otherwise as for pa_decode.
+ */
+pa_status pa_decode_noalloc(void *out, const void *q, const void *k_cache,
+                            const void *v_cache, const int32_t *block_tables,
+                            const int32_t *context_lens, float scale, int32_t num_seqs,
+                            int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim_k, int32_t head_dim_v, int32_t block_size,
+                            int32_t num_blocks, int32_t max_blocks_per_seq,
+                            pa_dtype dtype, void *stream);
+
+/*
  * MXFP8 KV cache.  Fewer bytes per cached value make memory-bound decode
  * faster, fp8 being one of the formats (CS336 lecture 10 notes, "第 10 讲：
  * 推理", "核心概念与定义", quantization bullet), and the scales should be

@@ -30,7 +30,7 @@ EXPORTS = ("pa_cache_append", "pa_decode_workspace_size", "pa_decode", "pa_cache
            "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free", "pa_bm_ref_count",
            "pa_bm_add_sequence", "pa_bm_append_token", "pa_bm_fork", "pa_bm_free_sequence",
            "pa_bm_num_tokens", "pa_bm_block_table", "pa_bm_take_copies", "pa_copy_blocks",
-           "pa_decode_ex", "pa_attention_scores", "pa_build_flags",
+           "pa_decode_ex", "pa_attention_scores", "pa_build_flags", "pa_decode_noalloc",
            "pa_status_string", "pa_last_error")
 
 _libs: dict = {}
@@ -115,6 +115,9 @@ def lib():
         L.pa_status_string.argtypes = [ctypes.c_int]
         L.pa_last_error.restype = ctypes.c_char_p
         L.pa_last_error.argtypes = []
+        L.pa_decode_noalloc.restype = ctypes.c_int
+        L.pa_decode_noalloc.argtypes = [P, P, P, P, P, P, ctypes.c_float, I32, I32, I32, I32,
+                                        I32, I32, I32, I32, ctypes.c_int, P]
         L.pa_build_flags.restype = I32
         L.pa_build_flags.argtypes = []
         _libs[path] = L
@@ -278,6 +281,21 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, workspac
         _ptr(context_lens), float(scale), B, hq, hkv, dk, dv, bs, nb, block_tables.shape[1],
         _dtype_code(q), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+
+
+def decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                   stream=None) -> None:
+    """decode() with the partials in the library's per-GPU scratch array
+    instead of a workspace (for callers that cannot allocate; calls that
+    overlap on one GPU race)."""
+    _check_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, None)
+    B, hq, dk = q.shape
+    nb, bs, hkv, _ = k_cache.shape
+    dv = out.shape[2]
+    _check(lib().pa_decode_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        _ptr(context_lens), float(scale), B, hq, hkv, dk, dv, bs, nb, block_tables.shape[1],
+        _dtype_code(q), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

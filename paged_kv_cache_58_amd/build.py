@@ -21,7 +21,7 @@ ARCH = "gfx950"
 
 SOURCES = ["plan.cpp", "block_manager.cpp", "api.cpp", "append.hip", "grouped_decode.hip",
            "gqa_mfma_decode.hip", "latent_decode.hip", "mxfp8_append.hip", "block_copy.hip",
-           "attention_scores.hip"]
+           "attention_scores.hip", "noalloc.hip"]
 HOST_ONLY = {"plan.cpp", "block_manager.cpp", "api.cpp"}  # pure C++: no HIP headers
 # The debug library links the release objects except api.cpp, which it
 # compiles again with PA_DEBUG, plus the check kernels.

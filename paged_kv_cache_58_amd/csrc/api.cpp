@@ -116,6 +116,47 @@ PA_EXPORT pa_status pa_decode(void *out, const void *q, const void *k_cache,
     return finish(st, why);
 }
 
+PA_EXPORT pa_status pa_decode_noalloc(void *out, const void *q, const void *k_cache,
+                                      const void *v_cache, const int32_t *block_tables,
+                                      const int32_t *context_lens, float scale, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim_k, int32_t head_dim_v, int32_t block_size,
+                                      int32_t num_blocks, int32_t max_blocks_per_seq,
+                                      pa_dtype dtype, void *stream) {
+    const pa::DecodeShape s =
+        make_shape(v_cache == nullptr, num_seqs, num_q_heads, num_kv_heads, head_dim_k,
+                   head_dim_v, block_size, max_blocks_per_seq, dtype);
+    std::string why;
+    pa::DecodePlan plan{};
+    pa_status st = pa::plan_decode(s, &plan, &why);
+    if (st != PA_OK) return finish(st, why);
+    if (plan.bytes > pa::kNoAllocScratchBytes)
+        return finish(PA_ERR_WORKSPACE,
+                      "decode_noalloc: these sizes need " + std::to_string(plan.bytes) +
+                          " bytes of scratch, more than the " +
+                          std::to_string(pa::kNoAllocScratchBytes) +
+                          " the library holds per GPU; call pa_decode with a workspace");
+    if (num_seqs == 0) return finish(PA_OK, why);
+    void *scratch = nullptr;
+    st = pa::noalloc_scratch(&scratch, &why);
+    if (st != PA_OK) return finish(st, why);
+    const pa::DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens, nullptr,
+                           nullptr, scale, num_blocks, scratch, pa::kNoAllocScratchBytes};
+    st = pa::check_decode(s, a, plan, &why);
+    if (st != PA_OK) return finish(st, why);
+    PA_DEBUG_CHECK(pa::debug_check_tables(block_tables, context_lens, num_seqs,
+                                          max_blocks_per_seq, block_size, 0, num_blocks,
+                                          static_cast<int64_t>(max_blocks_per_seq) * block_size,
+                                          stream, &dbg_why));
+    if (plan.path == pa::DecodePath::kLatent)
+        st = pa::launch_latent_decode(s, a, plan, stream, &why);
+    else if (plan.path == pa::DecodePath::kGroupedMfma)
+        st = pa::launch_gqa_mfma_decode(s, a, plan, stream, &why);
+    else
+        st = pa::launch_grouped_decode(s, a, plan, stream, &why);
+    return finish(st, why);
+}
+
 PA_EXPORT pa_status pa_cache_append_mxfp8(void *k_cache, void *v_cache, void *k_scale,
                                           void *v_scale, const void *k, int64_t k_token_stride,
                                           const void *v, int64_t v_token_stride,

@@ -49,6 +49,11 @@ pa_status launch_latent_decode(const DecodeShape &s, const DecodeArgs &a,
                                const DecodePlan &plan, void *stream, std::string *why);
 
 
+// Scratch of pa_decode_noalloc (noalloc.hip): the current device's copy of a
+// file-scope device array of kNoAllocScratchBytes, looked up once per device.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+pa_status noalloc_scratch(void **out, std::string *why);
+
 // PA_DEBUG builds only (debug_checks.hip): the device pass over a call's
 // index arrays.  Each waits for the stream and returns PA_ERR_INDEX, naming
 // the violation, when an index breaks the contract (validate.h).

@@ -42,4 +42,5 @@ pa_status launch_latent_decode(const DecodeShape &, const DecodeArgs &, const De
                                std::string *why) {
     return none(why);
 }
+pa_status noalloc_scratch(void **, std::string *why) { return none(why); }
 }  // namespace pa
