@@ -135,6 +135,9 @@ struct Cfg {
     static constexpr int kCPL = kChunks / 8;        // chunks per lane per token
     static constexpr int kDPL = D / kWave;          // output dims per lane
     static constexpr int kPWords = kBf16 ? G * 8 : G * 16;
+    // A segment's q rows (G heads) reach LDS in kQDma 1 KB LDS-DMA loads.
+    static constexpr int kQBytes = G * kRowBytes;
+    static constexpr int kQDma = (kQBytes + 1023) / 1024;
     static_assert(kCPL >= 1 && kChunks % 8 == 0, "row must be a multiple of 128 bytes");
     static_assert(kDPL >= 1, "head dim must be a multiple of 64");
 };
@@ -144,7 +147,8 @@ struct Cfg {
 template <typename T, int D, int G, int NBUF>
 constexpr int group_waves() {
     using C = Cfg<T, D, G>;
-    constexpr int per_wave = NBUF * 2 * 2 * C::kCPL * kWave * 16 + C::kPWords * 4 + 2 * kWave * 4 + 8 * 4;
+    constexpr int per_wave = NBUF * 2 * 2 * C::kCPL * kWave * 16 + C::kPWords * 4 + 2 * kWave * 4 +
+                             8 * 4 + 2 * C::kQDma * 1024;
     return 4 * per_wave <= 160 * 1024 ? 4 : 2 * per_wave <= 160 * 1024 ? 2 : 1;
 }
 
@@ -204,6 +208,8 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
     __shared__ __attribute__((aligned(16))) uint32_t s_p_all[kGroupWaves][C::kPWords];
     __shared__ __attribute__((aligned(16))) int32_t s_ids_all[kGroupWaves][2][kWave];
     __shared__ float s_alpha_all[kGroupWaves][8];
+    // q rows of the segment being started, for segments k & 1
+    __shared__ __attribute__((aligned(16))) uint4 s_q_all[kGroupWaves][2][C::kQDma * kWave];
     uint4 *s_ring = s_ring_all[wave];
     uint32_t *s_p = s_p_all[wave];
     int32_t(*s_ids)[kWave] = s_ids_all[wave];
@@ -214,13 +220,13 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
     if (!find_share(sid, nshares, num_seqs, nchunks, kBS, context_lens, ws_prefix, lane, sp,
                     window, hw == 0))
         return;
-    const int x1 = sp.x1;
-    int b = sp.b, nbb = sp.nbb, ch = sp.g, blk_start = sp.blk;
+    const int P = sp.x1 - sp.x0;  // blocks of the share, over every segment it touches
 
     const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * C::kRowBytes;
     const int64_t blk_stride = kBS * row_stride;
     const uint32_t ring_lds = lds_offset(s_ring);
     const uint32_t ids_lds[2] = {lds_offset(&s_ids[0][0]), lds_offset(&s_ids[1][0])};
+    const uint32_t q_lds[2] = {lds_offset(&s_q_all[wave][0][0]), lds_offset(&s_q_all[wave][1][0])};
 
     // Where, in a slot's V rows, this lane finds the dword holding its first
     // output dim for token 2 tp' (row j = 0) and 2 tp' + 1 (row j = 1).
@@ -231,235 +237,307 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
     // bf16 with one dim per lane: which half of the dword holds it
     const uint32_t pv_sel = (kEB == 2 && DPL == 1 && (lane & 1)) ? 0x07060302u : 0x05040100u;
 
-    for (int x = sp.x0;;) {
-        // ======== segment (b, ch), head g: blocks [blk_start, blk_start + nblk) ========
-        const int g = ch * team_heads + hw;
-        const int nblk = min(nbb - blk_start, x1 - x);
-        const int ctx = context_lens[b];
-        // the window's first token and block (0 and 0 without a window)
-        const int wstart = window_start(ctx, window);
-        const int wblk = blk_start + wstart / kBS;  // table index of this segment's first block
-        const int32_t *bt_row = block_tables + static_cast<int64_t>(b) * max_blocks;
+    // Byte offsets, inside one physical block and KV head, of this lane's two
+    // rows (the head's offset goes into the scalar base).
+    uint32_t off[2][CPL];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+            off[j][i] = static_cast<uint32_t>((2 * tp + j) * row_stride + (c + 8 * i) * 16);
+    const char *kbase = reinterpret_cast<const char *>(k_cache);
+    const char *vbase = reinterpret_cast<const char *>(v_cache);
 
-        // block ids, 64 per LDS buffer; chunk m holds entries wblk + 64 m + lane
-        auto fetch_ids = [&](int m) {
-            const int e = min(wblk + kWave * m + lane, max_blocks - 1);
-            dma4(bt_row, static_cast<uint32_t>(e) * 4u, ids_lds[m & 1]);
-        };
-        fetch_ids(0);
-        if (nblk > kWave) fetch_ids(1);
-
-        // q slices: chunk (c + 8 i) of each of the G heads of this group.
-        // slot h holds head h ^ hc (the order reduce_scatter_c works in)
-        uint4 qv[G][CPL];
-        {
-            const char *qb = reinterpret_cast<const char *>(q) +
-                             (static_cast<int64_t>(b) * num_q_heads + g * G) * C::kRowBytes;
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int i = 0; i < CPL; ++i)
-                    qv[h][i] = *reinterpret_cast<const uint4 *>(qb + (h ^ hc) * C::kRowBytes +
-                                                                (c + 8 * i) * 16);
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int i = 0; i < CPL; ++i) settle(qv[h][i]);
+    // ---- segments ---------------------------------------------------------------
+    // The share is one stream of P blocks over consecutive (sequence, chunk)
+    // segments.  Segment k of the share: sequence b, head chunk ch (this wave's
+    // KV head g = ch TH + hw), its blocks from window block blk0 on, nblk of
+    // them in this share.  Two cursors walk the stream: the issue side starts
+    // each block's K/V loads NBUF - 1 blocks ahead of the compute side, and
+    // crosses into the next segment as soon as the current one is issued, so a
+    // segment switch costs the compute side no memory round trip.  The next
+    // segment's block ids and q rows are fetched into LDS when the issue side
+    // enters the current segment's last chunk of 64 blocks; the issue side
+    // never runs more than one segment ahead of the compute side, which
+    // bounds the q buffers to two.
+    struct Seg {
+        int b, ch, blk0, nblk, ctx, tbl0;  // tbl0: block-table index of the first block
+    };
+    auto make_seg = [&](int b, int ch, int blk0, int s0) {
+        Seg sg;
+        sg.b = b;
+        sg.ch = ch;
+        sg.blk0 = blk0;
+        sg.ctx = context_lens[b];
+        sg.nblk = min(window_blocks(sg.ctx, window, kBS) - blk0, P - s0);
+        sg.tbl0 = blk0 + window_first_block(sg.ctx, window, kBS);
+        return sg;
+    };
+    // the segment after sg in the global order (there is one: the share goes on)
+    auto successor = [&](const Seg &sg, int s0) {
+        int b = sg.b, ch = sg.ch + 1;
+        if (ch == nchunks) {
+            ch = 0;
+            do {
+                ++b;
+            } while (window_blocks(context_lens[b], window, kBS) == 0);
         }
-        // Byte offsets, inside one physical block, of this lane's two rows.
-        uint32_t off[2][CPL];
+        return make_seg(b, ch, 0, s0);
+    };
+    // block ids: chunk m of segment sg (entries tbl0 + 64 m + lane) into buffer buf
+    auto fetch_ids = [&](const Seg &sg, int m, int buf) {
+        const int32_t *bt_row = block_tables + static_cast<int64_t>(sg.b) * max_blocks;
+        const int e = min(sg.tbl0 + kWave * m + lane, max_blocks - 1);
+        dma4(bt_row, static_cast<uint32_t>(e) * 4u, ids_lds[buf]);
+    };
+    // q rows of segment sg's G heads into q buffer buf (kQDma loads; lanes past
+    // the rows reread the last 16 bytes into the buffer's unused tail)
+    auto fetch_q = [&](const Seg &sg, int buf) {
+        const char *qb = reinterpret_cast<const char *>(q) +
+                         (static_cast<int64_t>(sg.b) * num_q_heads + (sg.ch * team_heads + hw) * G) *
+                             C::kRowBytes;
+#pragma unroll
+        for (int i = 0; i < C::kQDma; ++i)
+            dma16(qb, static_cast<uint32_t>(min(1024 * i + 16 * lane, C::kQBytes - 16)),
+                  q_lds[buf] + 1024 * i);
+    };
+
+    // ---- issue side -------------------------------------------------------------
+    Seg is = make_seg(sp.b, sp.g, sp.blk, 0);
+    int is_k = 0, is_s0 = 0, in = 0, ipar = 0;  // ids chunk m of `is` sits in buffer (ipar + m) & 1
+    Seg nx = is;
+    int nx_ipar = 0;
+    bool nx_ready = false;
+    int gi = 0;  // blocks issued
+    int cs_k = 0;  // the compute side's segment (the issue side stays within one of it)
+
+    // Wait until the successor's id and q fetches have landed, `tail` blocks
+    // (kQDma + tail * PER_BLOCK loads) having been issued after the id fetch.
+    auto wait_since_fetch = [&](int tail) {
+        if constexpr (NBUF >= 4) {
+            if (tail >= 3) { wait_vmem<C::kQDma + 3 * PER_BLOCK>(); return; }
+            if (tail == 2) { wait_vmem<C::kQDma + 2 * PER_BLOCK>(); return; }
+        }
+        wait_vmem<C::kQDma + PER_BLOCK>();
+    };
+
+    // Issues the next block of the stream; false when it must wait for the
+    // compute side to reach the current issue segment first.
+    auto issue_next = [&]() -> bool {
+        if (in == is.nblk) {
+            if (is_k > cs_k) return false;
+            // The successor's first ids were fetched, then its q, then the
+            // loads of the `tail` blocks of the last chunk: with fewer than
+            // NBUF of them the compute side has not waited for the fetch yet,
+            // so wait here for everything issued before those loads.
+            const int tail = is.nblk - ((is.nblk - 1) & ~(kWave - 1));
+            if (tail < NBUF) wait_since_fetch(tail);
+            is_s0 += is.nblk;
+            is = nx;
+            ipar = nx_ipar;
+            ++is_k;
+            in = 0;
+            nx_ready = false;
+        }
+        if ((in & (kWave - 1)) == 0) {  // entering chunk m: fetch what comes 64 blocks later
+            const int m = in >> 6;
+            if (in + kWave < is.nblk) {
+                fetch_ids(is, m + 1, (ipar + m + 1) & 1);
+            } else if (is_s0 + is.nblk < P && !nx_ready) {
+                nx = successor(is, is_s0 + is.nblk);
+                nx_ipar = (ipar + m + 1) & 1;
+                fetch_ids(nx, 0, nx_ipar);
+                fetch_q(nx, (is_k + 1) & 1);
+                nx_ready = true;
+            }
+        }
+        const int pb = __builtin_amdgcn_readfirstlane(s_ids[(ipar + (in >> 6)) & 1][in & (kWave - 1)]);
+        const int64_t head_off = static_cast<int64_t>(is.ch * team_heads + hw) * C::kRowBytes;
+        const char *kb = kbase + static_cast<int64_t>(pb) * blk_stride + head_off;
+        const char *vb = vbase + static_cast<int64_t>(pb) * blk_stride + head_off;
+        const uint32_t slot = ring_lds + (gi & (NBUF - 1)) * (SLOT_U4 * 16);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int i = 0; i < CPL; ++i)
-                off[j][i] = static_cast<uint32_t>((2 * tp + j) * row_stride + g * C::kRowBytes +
-                                                  (c + 8 * i) * 16);
-        // Segment start: the ring is empty; q and the first ids must land
-        // before the ring's vmcnt accounting starts.
-        drain_vmem();
+                dma16(kb, off[j][i], slot + (j * CPL + i) * (kWave * 16));
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < CPL; ++i)
+                dma16(vb, off[j][i], slot + (KV_INSTR + j * CPL + i) * (kWave * 16));
+        ++in;
+        ++gi;
+        return true;
+    };
 
-        const char *kbase = reinterpret_cast<const char *>(k_cache);
-        const char *vbase = reinterpret_cast<const char *>(v_cache);
-
-        float m_run = kNegInf;  // running max of head hc (scaled, log2 units)
-        float l_run = 0.f;      // this lane's share of the running sum of head hc
-        float acc[G][DPL];
+    // ---- compute side -----------------------------------------------------------
+    Seg cs = is;
+    int cn = 0;             // the next block of `cs` to compute
+    float m_run = kNegInf;  // running max of head hc (scaled, log2 units)
+    float l_run = 0.f;      // this lane's share of the running sum of head hc
+    float acc[G][DPL];
+    // q slices: chunk (c + 8 i) of each of the G heads of the segment's group;
+    // slot h holds head h ^ hc (the order reduce_scatter_c works in)
+    uint4 qv[G][CPL];
+    auto load_q = [&](int buf) {
+        const uint4 *qs = reinterpret_cast<const uint4 *>(buf ? &s_q_all[wave][1][0] : &s_q_all[wave][0][0]);
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int i = 0; i < CPL; ++i)
+                qv[h][i] = qs[((h ^ hc) * C::kRowBytes + (c + 8 * i) * 16) >> 4];
+    };
+    auto reset = [&]() {
+        m_run = kNegInf;
+        l_run = 0.f;
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
             for (int d = 0; d < DPL; ++d) acc[h][d] = 0.f;
+    };
 
-        // Start block n's K and V streaming into ring slot n % NBUF.  Entering
-        // id chunk m (block 64 m) also starts the ids of chunk m + 1, which
-        // are needed 64 blocks later.
-        auto issue = [&](int n) {
-            if ((n & (kWave - 1)) == 0 && n > 0 && n + kWave < nblk) fetch_ids((n >> 6) + 1);
-            const int pb = __builtin_amdgcn_readfirstlane(s_ids[(n >> 6) & 1][n & (kWave - 1)]);
-            const char *kb = kbase + static_cast<int64_t>(pb) * blk_stride;
-            const char *vb = vbase + static_cast<int64_t>(pb) * blk_stride;
-            const uint32_t slot = ring_lds + (n & (NBUF - 1)) * (SLOT_U4 * 16);
+    auto compute_block = [&](int n, int g_slot) {
+        const uint4 *slot = s_ring + (g_slot & (NBUF - 1)) * SLOT_U4;
+        const int ctx = cs.ctx;
+        const int wstart = window_start(ctx, window);
+        const int tok0 = (cs.tbl0 + n) * kBS;
+        // only the sequence's last block, and the window's first, hold tokens
+        // outside [wstart, ctx); V rows below wstart are real data and get
+        // weight 0, rows at or past ctx are zeroed below
+        const bool partial = tok0 + kBS > ctx || tok0 < wstart;
+        bool valid[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int i = 0; i < CPL; ++i)
-                    dma16(kb, off[j][i], slot + (j * CPL + i) * (kWave * 16));
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int i = 0; i < CPL; ++i)
-                    dma16(vb, off[j][i], slot + (KV_INSTR + j * CPL + i) * (kWave * 16));
-        };
+        for (int j = 0; j < 2; ++j)
+            valid[j] = !partial || (tok0 + 2 * tp + j < ctx && tok0 + 2 * tp + j >= wstart);
 
-        auto compute_block = [&](int n) {
-            const uint4 *slot = s_ring + (n & (NBUF - 1)) * SLOT_U4;
-            const int tok0 = (wblk + n) * kBS;
-            // only the sequence's last block, and the window's first, hold tokens
-            // outside [wstart, ctx); V rows below wstart are real data and get
-            // weight 0, rows at or past ctx are zeroed below
-            const bool partial = tok0 + kBS > ctx || tok0 < wstart;
-            bool valid[2];
+        // ---- scores for the G heads of both tokens ---------------------
+        uint4 kr[2][CPL];
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                valid[j] = !partial || (tok0 + 2 * tp + j < ctx && tok0 + 2 * tp + j >= wstart);
-
-            // ---- scores for the G heads of both tokens ---------------------
-            uint4 kr[2][CPL];
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int i = 0; i < CPL; ++i) kr[j][i] = slot[(j * CPL + i) * kWave + lane];
+        float part_dot[2][G];
 #pragma unroll
-                for (int i = 0; i < CPL; ++i) kr[j][i] = slot[(j * CPL + i) * kWave + lane];
-            float part_dot[2][G];
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int h = 0; h < G; ++h) {
+                float a = 0.f;
 #pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    float a = 0.f;
-#pragma unroll
-                    for (int i = 0; i < CPL; ++i) {
-                        if constexpr (C::kBf16) {
-                            a = i == 0 ? dot2_bf16_0(qv[h][i].x, kr[j][i].x)
-                                       : dot2_bf16(qv[h][i].x, kr[j][i].x, a);
-                            a = dot2_bf16(qv[h][i].y, kr[j][i].y, a);
-                            a = dot2_bf16(qv[h][i].z, kr[j][i].z, a);
-                            a = dot2_bf16(qv[h][i].w, kr[j][i].w, a);
-                        } else {
-                            a = fmaf(as_f(qv[h][i].x), as_f(kr[j][i].x), a);
-                            a = fmaf(as_f(qv[h][i].y), as_f(kr[j][i].y), a);
-                            a = fmaf(as_f(qv[h][i].z), as_f(kr[j][i].z), a);
-                            a = fmaf(as_f(qv[h][i].w), as_f(kr[j][i].w), a);
-                        }
-                    }
-                    part_dot[j][h] = a;
-                }
-
-            // ---- online softmax for head hc --------------------------------
-            float x2[2];
-            reduce_scatter_c<G>(part_dot, x2);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) x2[j] = valid[j] ? x2[j] * scale_log2 : kNegInf;
-            const float xmax = fmaxf(x2[0], x2[1]);
-            if (__builtin_amdgcn_ballot_w64(xmax > m_run + kSlack) != 0) {
-                const float bmax = max_over_tp(xmax);
-                const float m_new = fmaxf(m_run, bmax);
-                const float alpha = exp2_fast(m_run - m_new);
-                l_run *= alpha;
-                m_run = m_new;
-                if (tp == 0 && head_writer) s_alpha[hc] = alpha;
-                wait_lds();  // the wave's own LDS writes are complete
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const float a = s_alpha[h];
-#pragma unroll
-                    for (int d = 0; d < DPL; ++d) acc[h][d] *= a;
-                }
-            }
-            const float p0 = exp2_fast(x2[0] - m_run);
-            const float p1 = exp2_fast(x2[1] - m_run);
-
-            wait_lds();  // the previous block's reads of s_p are done
-            if constexpr (C::kBf16) {
-                const uint32_t pk = pack_bf16(p0, p1);
-                l_run += bf16_lo(pk) + bf16_hi(pk);
-                if (head_writer) s_p[hc * 8 + tp] = pk;
-            } else {
-                l_run += p0 + p1;
-                if (head_writer)
-                    *reinterpret_cast<float2 *>(&s_p[hc * 16 + 2 * tp]) = make_float2(p0, p1);
-            }
-            wait_lds();  // this wave's probabilities are in LDS
-
-            // ---- P.V for all G heads of this lane's dims -------------------
-            const uint32_t *vw =
-                reinterpret_cast<const uint32_t *>(slot + KV_INSTR * kWave) + pv_word;
-            constexpr int kRowW = CPL * kWave * 4;  // dwords between the j = 0 and j = 1 rows
-            if constexpr (C::kBf16) {
-#pragma unroll
-                for (int quad = 0; quad < 2; ++quad) {
-                    uint4 pq[G];
-#pragma unroll
-                    for (int h = 0; h < G; ++h)
-                        pq[h] = *reinterpret_cast<const uint4 *>(&s_p[h * 8 + quad * 4]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int tq = quad * 4 + e;  // token pair 2 tq, 2 tq + 1
-                        uint32_t a = vw[tq * 32];
-                        uint32_t bb = vw[kRowW + tq * 32];
-                        if (partial) {  // masked rows contribute exactly zero, NaN or not
-                            if (tok0 + 2 * tq >= ctx) a = 0;
-                            if (tok0 + 2 * tq + 1 >= ctx) bb = 0;
-                        }
-                        uint32_t vp[DPL];
-                        if constexpr (DPL == 2) {
-                            vp[0] = __builtin_amdgcn_perm(bb, a, 0x05040100u);
-                            vp[1] = __builtin_amdgcn_perm(bb, a, 0x07060302u);
-                        } else {
-                            vp[0] = __builtin_amdgcn_perm(bb, a, pv_sel);
-                        }
-#pragma unroll
-                        for (int h = 0; h < G; ++h) {
-                            const uint32_t ph = e == 0 ? pq[h].x : e == 1 ? pq[h].y
-                                              : e == 2 ? pq[h].z : pq[h].w;
-#pragma unroll
-                            for (int d = 0; d < DPL; ++d)
-                                acc[h][d] = dot2_bf16(ph, vp[d], acc[h][d]);
-                        }
+                for (int i = 0; i < CPL; ++i) {
+                    if constexpr (C::kBf16) {
+                        a = i == 0 ? dot2_bf16_0(qv[h][i].x, kr[j][i].x)
+                                   : dot2_bf16(qv[h][i].x, kr[j][i].x, a);
+                        a = dot2_bf16(qv[h][i].y, kr[j][i].y, a);
+                        a = dot2_bf16(qv[h][i].z, kr[j][i].z, a);
+                        a = dot2_bf16(qv[h][i].w, kr[j][i].w, a);
+                    } else {
+                        a = fmaf(as_f(qv[h][i].x), as_f(kr[j][i].x), a);
+                        a = fmaf(as_f(qv[h][i].y), as_f(kr[j][i].y), a);
+                        a = fmaf(as_f(qv[h][i].z), as_f(kr[j][i].z), a);
+                        a = fmaf(as_f(qv[h][i].w), as_f(kr[j][i].w), a);
                     }
                 }
-            } else {
+                part_dot[j][h] = a;
+            }
+
+        // ---- online softmax for head hc --------------------------------
+        float x2[2];
+        reduce_scatter_c<G>(part_dot, x2);
 #pragma unroll
-                for (int t = 0; t < kBS; ++t) {
-                    const uint32_t *row = vw + (t & 1) * kRowW + (t >> 1) * 32;
-                    float vv[DPL];
+        for (int j = 0; j < 2; ++j) x2[j] = valid[j] ? x2[j] * scale_log2 : kNegInf;
+        const float xmax = fmaxf(x2[0], x2[1]);
+        if (__builtin_amdgcn_ballot_w64(xmax > m_run + kSlack) != 0) {
+            const float bmax = max_over_tp(xmax);
+            const float m_new = fmaxf(m_run, bmax);
+            const float alpha = exp2_fast(m_run - m_new);
+            l_run *= alpha;
+            m_run = m_new;
+            if (tp == 0 && head_writer) s_alpha[hc] = alpha;
+            wait_lds();  // the wave's own LDS writes are complete
 #pragma unroll
-                    for (int d = 0; d < DPL; ++d)
-                        vv[d] = (partial && tok0 + t >= ctx) ? 0.f : as_f(row[d]);
+            for (int h = 0; h < G; ++h) {
+                const float a = s_alpha[h];
+#pragma unroll
+                for (int d = 0; d < DPL; ++d) acc[h][d] *= a;
+            }
+        }
+        const float p0 = exp2_fast(x2[0] - m_run);
+        const float p1 = exp2_fast(x2[1] - m_run);
+
+        wait_lds();  // the previous block's reads of s_p are done
+        if constexpr (C::kBf16) {
+            const uint32_t pk = pack_bf16(p0, p1);
+            l_run += bf16_lo(pk) + bf16_hi(pk);
+            if (head_writer) s_p[hc * 8 + tp] = pk;
+        } else {
+            l_run += p0 + p1;
+            if (head_writer)
+                *reinterpret_cast<float2 *>(&s_p[hc * 16 + 2 * tp]) = make_float2(p0, p1);
+        }
+        wait_lds();  // this wave's probabilities are in LDS
+
+        // ---- P.V for all G heads of this lane's dims -------------------
+        const uint32_t *vw =
+            reinterpret_cast<const uint32_t *>(slot + KV_INSTR * kWave) + pv_word;
+        constexpr int kRowW = CPL * kWave * 4;  // dwords between the j = 0 and j = 1 rows
+        if constexpr (C::kBf16) {
+#pragma unroll
+            for (int quad = 0; quad < 2; ++quad) {
+                uint4 pq[G];
+#pragma unroll
+                for (int h = 0; h < G; ++h)
+                    pq[h] = *reinterpret_cast<const uint4 *>(&s_p[h * 8 + quad * 4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int tq = quad * 4 + e;  // token pair 2 tq, 2 tq + 1
+                    uint32_t a = vw[tq * 32];
+                    uint32_t bb = vw[kRowW + tq * 32];
+                    if (partial) {  // masked rows contribute exactly zero, NaN or not
+                        if (tok0 + 2 * tq >= ctx) a = 0;
+                        if (tok0 + 2 * tq + 1 >= ctx) bb = 0;
+                    }
+                    uint32_t vp[DPL];
+                    if constexpr (DPL == 2) {
+                        vp[0] = __builtin_amdgcn_perm(bb, a, 0x05040100u);
+                        vp[1] = __builtin_amdgcn_perm(bb, a, 0x07060302u);
+                    } else {
+                        vp[0] = __builtin_amdgcn_perm(bb, a, pv_sel);
+                    }
 #pragma unroll
                     for (int h = 0; h < G; ++h) {
-                        const float ph = as_f(s_p[h * 16 + t]);
+                        const uint32_t ph = e == 0 ? pq[h].x : e == 1 ? pq[h].y
+                                          : e == 2 ? pq[h].z : pq[h].w;
 #pragma unroll
-                        for (int d = 0; d < DPL; ++d) acc[h][d] = fmaf(ph, vv[d], acc[h][d]);
+                        for (int d = 0; d < DPL; ++d)
+                            acc[h][d] = dot2_bf16(ph, vp[d], acc[h][d]);
                     }
                 }
             }
-        };
-
+        } else {
 #pragma unroll
-        for (int n = 0; n < NBUF - 1; ++n)
-            if (n < nblk) issue(n);
-        for (int n = 0; n < nblk; ++n) {
-            if (n + NBUF - 1 < nblk) {
-                wait_lds();  // slot (n - 1) % NBUF and the ids in LDS are read
-                issue(n + NBUF - 1);
+            for (int t = 0; t < kBS; ++t) {
+                const uint32_t *row = vw + (t & 1) * kRowW + (t >> 1) * 32;
+                float vv[DPL];
+#pragma unroll
+                for (int d = 0; d < DPL; ++d)
+                    vv[d] = (partial && tok0 + t >= ctx) ? 0.f : as_f(row[d]);
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const float ph = as_f(s_p[h * 16 + t]);
+#pragma unroll
+                    for (int d = 0; d < DPL; ++d) acc[h][d] = fmaf(ph, vv[d], acc[h][d]);
+                }
             }
-            wait_blocks<PER_BLOCK, NBUF>(min(NBUF - 1, nblk - 1 - n));
-            compute_block(n);
         }
+    };
 
-        // ---- this segment's partial: unnormalised acc, running max and sum ----
+    // this segment's partial: unnormalised acc, running max and sum
+    auto store_partial = [&]() {
         const float l_tot = sum_over_tp(l_run);
         const int64_t slot_row =
-            ((static_cast<int64_t>(sid) + static_cast<int64_t>(b) * nchunks + ch) * team_heads + hw) *
-            G;
+            ((static_cast<int64_t>(sid) + static_cast<int64_t>(cs.b) * nchunks + cs.ch) * team_heads +
+             hw) * G;
         if (tp == 0 && head_writer) ws_ml[slot_row + hc] = make_float2(m_run, l_tot);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -469,19 +547,42 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
             else
                 dst[0] = acc[h][0];
         }
+    };
 
-        x += nblk;
-        if (x >= x1) break;
-        // next segment in the global order; sequences with no blocks hold none
-        blk_start = 0;
-        if (++ch == nchunks) {
-            ch = 0;
-            do {
-                ++b;
-                nbb = window_blocks(context_lens[b], window, kBS);
-            } while (nbb == 0);
+    // ---- prologue: the first segment's ids and q, then the ring -------------------
+    fetch_ids(is, 0, 0);
+    fetch_q(is, 0);
+    drain_vmem();  // (the compiler's own loads too: nothing of it is pending in the loop)
+    load_q(0);
+    reset();
+    for (int n = 0; n < NBUF - 1 && gi < P; ++n) issue_next();
+
+    bool fresh = false;  // `cs` was just entered: its q is still in LDS
+    for (int gcb = 0; gcb < P; ++gcb) {
+        if (fresh) {
+            // The segment's first block has landed, and its q rows (loaded
+            // before it) with them.  They go to registers before the issue
+            // side may refill that q buffer for the segment after next.
+            wait_blocks<PER_BLOCK, NBUF>(min(NBUF - 1, gi - 1 - gcb));
+            load_q(cs_k & 1);
+            reset();
+            fresh = false;
         }
-        wait_lds();  // every LDS read of this segment is done before the next one's DMA
+        while (gi < P && gi <= gcb + NBUF - 1) {
+            wait_lds();  // slot gi % NBUF, the ids and the q buffers in LDS are read
+            if (!issue_next()) break;
+        }
+        wait_blocks<PER_BLOCK, NBUF>(min(NBUF - 1, gi - 1 - gcb));
+        compute_block(cn, gcb);
+        if (++cn == cs.nblk) {
+            store_partial();
+            if (gcb + 1 < P) {  // the issue side is in the next segment already
+                cs = is;
+                ++cs_k;
+                cn = 0;
+                fresh = true;
+            }
+        }
     }
 }
 

@@ -44,10 +44,21 @@ def test_latent_parity_small(dev, hq, ctx):
 
 
 def test_latent_rescale_heavy(dev):
+    """Scale 0.5 on 576 unit-variance dims: scores spread over tens of units,
+    a few tokens carry each head, and |O| reaches the size of single V
+    values.  There the bf16 output's own rounding is the largest error: the
+    exact result rounded to bf16 is already that far from it (the floor
+    printed), and the GPU must stay within 2e-3 of that floor."""
     say("case: latent, scale 0.5 (wide score range)")
     w = make_workload(_spec(64, [900, 333], scale=0.5), seed=3)
     d = to_device(w, dev)
-    say(f"  {compare(d.decode(), oracle.decode_workload(w), 'bf16')}")
+    ref = oracle.decode_workload(w)
+    got = d.decode()
+    stats = compare(got, ref, 'bf16')
+    exact_bf16 = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    floor = float(np.abs(exact_bf16 - ref).max())
+    say(f"  {stats}; bf16 rounding of the exact output alone: {floor:.4f}")
+    assert stats["max_abs"] <= floor + 2e-3
 
 
 def test_latent_context_one_is_v_bitwise(dev):
