@@ -285,6 +285,9 @@ def main() -> int:
                     help="query tokens per sequence (pa_decode_multi when > 1)")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window in tokens (pa_decode_ex; 0 = the whole context)")
+    ap.add_argument("--scores", action="store_true",
+                    help="also time pa_attention_scores (per-token attention mass over the "
+                         "window, from pa_decode_ex's log-sum-exp) on the same workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter scaling)")
@@ -478,6 +481,39 @@ def main() -> int:
         alt = {"kernel": GROUPED_MFMA, "us_decode": round(float(np.mean(t_alt)) * 1e3, 2)}
         decode()  # the default kernel's output for the oracle check below
         torch.cuda.synchronize()
+    scores_leg = None
+    if args.scores:
+        if mx or Q > 1 or spec.mla:
+            log("--scores runs on the single-query grouped workloads' own caches")
+            return 2
+        # lse from the windowed decode, then the scores pass alone, cold
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+        ws_s = pa.alloc_workspace(q, kc, bt)
+        pa.decode_ex(out, q, kc, vc, bt, cl, w.scale, ws_s, window=W, lse=lse)
+        max_ctx = int(bt.shape[1]) * spec.block_size
+        scores_t = torch.empty((spec.num_seqs, spec.num_kv_heads, max_ctx), dtype=torch.float32,
+                               device=dev)
+
+        def scores_call():
+            pa.attention_scores(scores_t, q, kc, bt, cl, lse, w.scale, window=W)
+
+        for _ in range(max(args.warmup, 3)):
+            scores_call()
+        _, t_sc = cold_times(lambda: None, scores_call, K)
+        att = np.minimum(L1, W) if W else L1
+        sc_bytes = (int(att.sum()) * spec.num_kv_heads * spec.head_dim_k * spec.elt +  # K rows once
+                    spec.num_seqs * spec.num_q_heads * (spec.head_dim_k * spec.elt + 4) +  # q, lse
+                    spec.num_seqs * spec.num_kv_heads * max_ctx * 4 +  # scores written
+                    4 * int(((L1 + spec.block_size - 1) // spec.block_size).sum()))  # block ids
+        us_sc = float(np.mean(t_sc)) * 1e3
+        scores_leg = {"kernel": "attention_scores_kernel", "us": round(us_sc, 2),
+                      "algorithmic_bytes": sc_bytes,
+                      "roofline": {"bound": "hbm", "achieved": round(sc_bytes / (us_sc * 1e-6) / 1e9, 2),
+                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": round(sc_bytes / (us_sc * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}}
+        log(f"[bench] attention scores: {us_sc:.1f} us = {scores_leg['roofline']['frac']:.1%} of HBM")
+        decode()  # the timed step's output for the oracle check below
+        torch.cuda.synchronize()
     del flush_buf
 
     # accounting over the context actually attended (ctx + 1)
@@ -575,6 +611,7 @@ def main() -> int:
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": decode_bytes},
         "other_kernel": alt,
+        "attention_scores": scores_leg,
         "cpu_baseline": cpu,
         "max_abs_err_vs_oracle": max_err,
         "wall_s_timed": round(wall, 4),

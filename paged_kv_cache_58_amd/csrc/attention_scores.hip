@@ -16,10 +16,11 @@
 // past the context score 0.  Each head's probabilities sum to 1, so a
 // sequence's scores for a KV head sum to G.
 //
-// One wave per (sequence, KV head, 16-token block): lane (token r = lane / 4,
-// quarter c = lane % 4) holds dims c*D/4 .. of token r's K row and forms the
-// G dot products with q over them; two lane exchanges finish each one.  The
-// pass reads the window's K rows once (half of the decode's cache bytes).
+// One wave per (sequence, KV head, 16-token block), four blocks per
+// work-group: lane (token r = lane / 4, quarter c = lane % 4) loads dims
+// c*D/4 .. of token r's K row with 16-byte loads and forms the G dot
+// products with q over them; two lane exchanges finish each one.  The pass
+// reads the window's K rows once (half of the decode's cache bytes).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -33,26 +34,43 @@ namespace {
 
 constexpr int kSBS = 16;  // tokens per cache block
 
-template <typename T>
-__device__ __forceinline__ float load_as_f32(const T *p, int i) {
-    if constexpr (sizeof(T) == 4) {
-        return reinterpret_cast<const float *>(p)[i];
-    } else {
-        return as_f(static_cast<uint32_t>(reinterpret_cast<const uint16_t *>(p)[i]) << 16);
+constexpr int kScoreWaves = 4;  // waves (blocks of 16 tokens) per work-group
+
+// n 16-byte chunks of a row, converted to fp32 (bf16: 8 values a chunk,
+// fp32: 4).
+template <typename T, int N>
+__device__ __forceinline__ void load_row(const T *p, float *out) {
+    const uint4 *v = reinterpret_cast<const uint4 *>(p);
+    uint4 w[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) w[i] = v[i];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const uint32_t u[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (sizeof(T) == 2) {
+                out[8 * i + 2 * j] = bf16_lo(u[j]);
+                out[8 * i + 2 * j + 1] = bf16_hi(u[j]);
+            } else {
+                out[4 * i + j] = as_f(u[j]);
+            }
+        }
     }
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(kWave) void attention_scores_kernel(
+__global__ __launch_bounds__(kWave *kScoreWaves) void attention_scores_kernel(
     float *__restrict__ scores, const T *__restrict__ q, const T *__restrict__ k_cache,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
-    const float *__restrict__ lse, float scale, int window, int num_kv_heads, int group,
+    const float *__restrict__ lse, float scale_log2, int window, int num_kv_heads, int group,
     int max_blocks, int max_context) {
-    constexpr int DQ = D / 4;  // dims per lane
-    const int blk = blockIdx.x;
+    constexpr int DQ = D / 4;                              // dims per lane
+    constexpr int NCH = DQ * static_cast<int>(sizeof(T)) / 16;  // 16-byte chunks per lane
+    const int lane = threadIdx.x & (kWave - 1);
+    const int blk = blockIdx.x * kScoreWaves + static_cast<int>(threadIdx.x / kWave);
     const int g = blockIdx.y;
     const int b = blockIdx.z;
-    const int lane = threadIdx.x;
     const int r = lane >> 2;
     const int c = lane & 3;
     const int t = blk * kSBS + r;
@@ -67,20 +85,22 @@ __global__ __launch_bounds__(kWave) void attention_scores_kernel(
         return;
     }
     const int pb = block_tables[static_cast<int64_t>(b) * max_blocks + blk];
-    const T *krow = k_cache + ((static_cast<int64_t>(pb) * kSBS + r) * num_kv_heads + g) * D + c * DQ;
     float kv[DQ];
-#pragma unroll
-    for (int i = 0; i < DQ; ++i) kv[i] = load_as_f32(krow, i);
+    load_row<T, NCH>(k_cache + ((static_cast<int64_t>(pb) * kSBS + r) * num_kv_heads + g) * D + c * DQ,
+                     kv);
+    const float *lse_b = lse + static_cast<int64_t>(b) * num_q_heads + g * group;
+    const T *q_g = q + (static_cast<int64_t>(b) * num_q_heads + g * group) * D + c * DQ;
     float sum = 0.f;
     for (int h = 0; h < group; ++h) {
-        const int hq = g * group + h;
-        const T *qrow = q + (static_cast<int64_t>(b) * num_q_heads + hq) * D + c * DQ;
+        float qv[DQ];
+        load_row<T, NCH>(q_g + static_cast<int64_t>(h) * D, qv);
         float dot = 0.f;
 #pragma unroll
-        for (int i = 0; i < DQ; ++i) dot = fmaf(load_as_f32(qrow, i), kv[i], dot);
+        for (int i = 0; i < DQ; ++i) dot = fmaf(qv[i], kv[i], dot);
         dot += __shfl_xor(dot, 1);
         dot += __shfl_xor(dot, 2);
-        sum += expf(dot * scale - lse[static_cast<int64_t>(b) * num_q_heads + hq]);
+        // exp(scale q.k - lse) = 2^(scale log2(e) q.k - lse log2(e))
+        sum += exp2_fast(fmaf(dot, scale_log2, -lse_b[h] * 1.4426950408889634f));
     }
     if (c == 0 && t < max_context) row[t] = in ? sum : 0.f;
 }
@@ -90,10 +110,12 @@ void enqueue_scores(float *scores, const void *q, const void *k_cache, const int
                     const int32_t *cl, const float *lse, float scale, int window, int num_seqs,
                     int num_kv_heads, int group, int max_blocks, int max_context,
                     hipStream_t stream) {
-    const dim3 grid((max_context + kSBS - 1) / kSBS, num_kv_heads, num_seqs);
-    hipLaunchKernelGGL((attention_scores_kernel<T, D>), grid, dim3(kWave), 0, stream, scores,
-                       static_cast<const T *>(q), static_cast<const T *>(k_cache), bt, cl, lse,
-                       scale, window, num_kv_heads, group, max_blocks, max_context);
+    const int nblk = (max_context + kSBS - 1) / kSBS;
+    const dim3 grid((nblk + kScoreWaves - 1) / kScoreWaves, num_kv_heads, num_seqs);
+    const float scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+    hipLaunchKernelGGL((attention_scores_kernel<T, D>), grid, dim3(kWave * kScoreWaves), 0, stream,
+                       scores, static_cast<const T *>(q), static_cast<const T *>(k_cache), bt, cl,
+                       lse, scale_log2, window, num_kv_heads, group, max_blocks, max_context);
 }
 
 }  // namespace

@@ -1,8 +1,8 @@
-"""A continuous-batching decode loop driven by the host block manager, on the
-GPU: sequences are admitted with prompts that share system-prompt blocks,
-decoded step by step (pa_bm_append_token -> pa_copy_blocks for copy-on-write
--> pa_cache_append -> pa_decode), forked (parallel samples of one prompt) and
-retired, while new ones reuse the cached prefixes of live ones.
+"""The continuous-batching decode loop (paged_kv_cache_58_amd.engine.DecodeLoop)
+on the GPU: sequences are admitted with prompts that share system-prompt
+blocks, decoded step by step (pa_bm_append_token -> pa_copy_blocks for
+copy-on-write -> pa_cache_append -> pa_decode), forked (parallel samples of one
+prompt) and retired, while new ones reuse the cached prefixes of live ones.
 
 The K/V of a token is a fixed function of (token id, position), so a shared
 prefix has the same K/V in every sequence, as a model's would.  Every step
@@ -50,73 +50,63 @@ class TokenKV:
         return (f32_to_bf16_bits(self.kt[t] + self.kp[p]), f32_to_bf16_bits(self.vt[t] + self.vp[p]))
 
 
-def test_continuous_batching_with_prefix_sharing_and_copy_on_write(dev):
-    say("case: block-manager driven decode loop, 12 steps")
+def _run_loop(dev, graph_buckets=None, steps=12):
+    """Drive paged_kv_cache_58_amd.engine.DecodeLoop for `steps` steps with
+    admissions (prompts sharing system-prompt blocks), forks and retirements;
+    check the cache and the decode at every step.  Returns the outputs."""
+    from paged_kv_cache_58_amd.engine import DecodeLoop
+
     rng = np.random.default_rng(9)
     tkv = TokenKV()
     nb, max_blocks = 160, MAXPOS // BS
-    m = pa.BlockManager(nb, BS)
-    nan = np.uint16(0x7FC0)
-    kc = device_tensor(np.full((nb, BS, HKV, D), nan, np.uint16), dev)
-    vc = device_tensor(np.full((nb, BS, HKV, D), nan, np.uint16), dev)
+    loop = DecodeLoop(nb, BS, HKV, HQ, D, max_blocks, D ** -0.5, torch.bfloat16, dev,
+                      graph_buckets=graph_buckets)
     sys_prompts = [list(rng.integers(0, VOCAB, 32)), list(rng.integers(0, VOCAB, 40))]
     tokens = {}  # seq id -> token list (the ground truth of what is cached)
     next_id = 0
-    cow_pairs = shared_hits = 0
-
-    def write(slots, toks, poss):
-        k, v = tkv.rows(toks, poss)
-        pa.cache_append(kc, vc, device_tensor(k, dev), device_tensor(v, dev),
-                        torch.from_numpy(np.asarray(slots, np.int32)).to(dev))
+    shared_hits = 0
+    outs = []
 
     def admit():
         nonlocal next_id, shared_hits
         prompt = sys_prompts[rng.integers(0, 2)] + list(rng.integers(0, VOCAB, rng.integers(1, 40)))
-        sid = next_id
+        k, v = tkv.rows(prompt, np.arange(len(prompt)))
+        shared_hits += loop.add(next_id, prompt, device_tensor(k, dev), device_tensor(v, dev))
+        tokens[next_id] = list(prompt)
         next_id += 1
-        cached = m.add_sequence(sid, prompt)
-        shared_hits += cached
-        bt = m.block_table(sid, max_blocks)
-        pos = np.arange(cached, len(prompt))
-        if pos.size:
-            write(bt[pos // BS] * BS + pos % BS, np.asarray(prompt)[pos], pos)
-        tokens[sid] = list(prompt)
 
     for _ in range(5):
         admit()
-    for step in range(12):
+    for step in range(steps):
         live = sorted(tokens)
         if step % 4 == 1:  # parallel sample: fork a sequence
             p = live[rng.integers(0, len(live))]
-            m.fork(p, next_id)
+            loop.fork(p, next_id)
             tokens[next_id] = list(tokens[p])
             next_id += 1
         if step % 5 == 3:  # retire one, admit one
             sid = live[rng.integers(0, len(live))]
-            m.free(sid)
+            loop.free(sid)
             del tokens[sid]
             admit()
         live = sorted(tokens)
-        slots, toks, poss = [], [], []
-        for sid in live:
-            t = int(rng.integers(0, VOCAB))
-            slots.append(m.append_token(sid, t))
-            toks.append(t)
-            poss.append(len(tokens[sid]))
+        assert live == loop.live
+        toks = [int(rng.integers(0, VOCAB)) for _ in live]
+        poss = [len(tokens[sid]) for sid in live]
+        k, v = tkv.rows(toks, poss)
+        q = f32_to_bf16_bits(rng.standard_normal((len(live), HQ, D)).astype(np.float32))
+        out = loop.step(live, toks, device_tensor(q, dev), device_tensor(k, dev),
+                        device_tensor(v, dev))
+        for sid, t in zip(live, toks):
             tokens[sid].append(t)
-        src, dst = m.take_copies()
-        if len(src):
-            cow_pairs += len(src)
-            s_d = torch.from_numpy(src).to(dev)
-            d_d = torch.from_numpy(dst).to(dev)
-            pa.copy_blocks(kc, s_d, d_d)
-            pa.copy_blocks(vc, s_d, d_d)
-        write(slots, toks, poss)
+        torch.cuda.synchronize()
+        outs.append(host_array(out).copy())
 
         # (1) the cache holds exactly each live sequence's K/V
-        bts = np.stack([m.block_table(sid, max_blocks) for sid in live])
+        bts = np.stack([loop.block_table(sid) for sid in live])
         lens = np.array([len(tokens[sid]) for sid in live], np.int32)
-        hk, hv = host_array(kc), host_array(vc)
+        assert [loop.num_tokens(s) for s in live] == lens.tolist()
+        hk, hv = host_array(loop.k_cache), host_array(loop.v_cache)
         for i, sid in enumerate(live):
             pos = np.arange(lens[i])
             ek, ev = tkv.rows(tokens[sid], pos)
@@ -124,20 +114,31 @@ def test_continuous_batching_with_prefix_sharing_and_copy_on_write(dev):
             assert np.array_equal(hk[blk, row], ek) and np.array_equal(hv[blk, row], ev), \
                 f"step {step}: cache of sequence {sid} differs"
 
-        # (2) decode through the manager's tables against the oracle
-        q = f32_to_bf16_bits(rng.standard_normal((len(live), HQ, D)).astype(np.float32))
-        out = torch.empty((len(live), HQ, D), dtype=torch.bfloat16, device=dev)
-        bt_d = torch.from_numpy(bts).to(dev)
-        q_d = device_tensor(q, dev)
-        ws = pa.alloc_workspace(q_d, kc, bt_d)
-        pa.decode(out, q_d, kc, vc, bt_d, torch.from_numpy(lens).to(dev), D ** -0.5, ws)
+        # (2) the decode against the oracle on a pool packed independently
         seqs_k, seqs_v = zip(*[tkv.rows(tokens[sid], np.arange(len(tokens[sid]))) for sid in live])
         pk, pbt = pack_paged(list(seqs_k), BS, rng=np.random.default_rng(step), dtype=np.uint16)
         pv, _ = pack_paged(list(seqs_v), BS, rng=np.random.default_rng(step), dtype=np.uint16)
         ref = oracle.decode(q, pk, pv, pbt, lens, D ** -0.5)
         compare(out, ref, "bf16")
-    say(f"  {next_id} sequences, {shared_hits} prompt tokens found cached, {cow_pairs} copy-on-write blocks")
-    assert shared_hits > 0 and cow_pairs > 0
+    say(f"  {next_id} sequences, {shared_hits} prompt tokens found cached, "
+        f"{loop.copied_blocks} copy-on-write blocks")
+    assert shared_hits > 0 and loop.copied_blocks > 0
+    return outs
+
+
+def test_continuous_batching_with_prefix_sharing_and_copy_on_write(dev):
+    say("case: DecodeLoop (block manager, copy-on-write, append, decode), 12 steps")
+    _run_loop(dev)
+
+
+def test_continuous_batching_from_graph_buckets(dev):
+    """The same loop with each step's append + decode replayed from graph
+    buckets: identical to the eager loop bit for bit."""
+    say("case: DecodeLoop on graph buckets (4, 8) vs eager")
+    eager = _run_loop(dev)
+    graphed = _run_loop(dev, graph_buckets=(4, 8))
+    for a, b in zip(eager, graphed):
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
 
 
 def test_copy_blocks_mxfp8_pools(dev):
