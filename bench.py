@@ -411,7 +411,7 @@ def main() -> int:
         torch.sum(flush_buf, 0, dtype=torch.int64, out=flush_sink)
 
     # Clock ramp: the GPU runs its first few hundred ms of work at lower
-    # clocks, so flush writes (not steps of the hot path) run for ~0.5 s first.
+    # clocks, so flush reads (not steps of the hot path) run for ~0.5 s first.
     t_ramp = time.perf_counter()
     while time.perf_counter() - t_ramp < 0.5:
         for _ in range(20):

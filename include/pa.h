@@ -110,7 +110,10 @@ pa_status pa_cache_append(void *k_cache, void *v_cache,
  * these sizes (the split-context partial results: an fp32 accumulator of
  * head_dim_v values plus a running max and a running sum per sequence, query
  * head and context partition).  Returns 0 when the sizes are not valid.
- * pa_decode must be called with the same sizes.
+ * pa_decode must be called with the same sizes.  The sizes carry no v_cache
+ * pointer, so head_dim_k != head_dim_v is what names latent mode here; the
+ * only unequal pair accepted is the latent shape (576, 512, one KV head,
+ * block size 64), and any other returns 0.
  */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                 int32_t num_kv_heads, int32_t head_dim_k,

@@ -75,7 +75,8 @@ PA_EXPORT size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                           int32_t num_kv_heads, int32_t head_dim_k,
                                           int32_t head_dim_v, int32_t block_size,
                                           int32_t max_blocks_per_seq) {
-    // Latent mode is the only shape with head_dim_v != head_dim_k.
+    // Latent mode is the only shape with head_dim_v != head_dim_k (the plan
+    // rejects any unequal pair but 576 / 512, so nothing else is planned as latent).
     const bool latent = head_dim_k != head_dim_v;
     const pa::DecodeShape s = make_shape(latent, num_seqs, num_q_heads, num_kv_heads,
                                          head_dim_k, head_dim_v, block_size,
