@@ -43,6 +43,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "device_common.h"
 #include "hip_util.h"
@@ -223,7 +224,9 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
     const int P = sp.x1 - sp.x0;  // blocks of the share, over every segment it touches
 
     const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * C::kRowBytes;
-    const int64_t blk_stride = kBS * row_stride;
+    // bytes per physical block: below 2^32 (at most 65535 KV heads of 512-byte rows), so a
+    // block's offset is one 32 x 32 -> 64-bit product
+    const uint32_t blk_stride = static_cast<uint32_t>(kBS * row_stride);
     const uint32_t ring_lds = lds_offset(s_ring);
     const uint32_t ids_lds[2] = {lds_offset(&s_ids[0][0]), lds_offset(&s_ids[1][0])};
     const uint32_t q_lds[2] = {lds_offset(&s_q_all[wave][0][0]), lds_offset(&s_q_all[wave][1][0])};
@@ -353,8 +356,9 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
         }
         const int pb = __builtin_amdgcn_readfirstlane(s_ids[(ipar + (in >> 6)) & 1][in & (kWave - 1)]);
         const int64_t head_off = static_cast<int64_t>(is.ch * team_heads + hw) * C::kRowBytes;
-        const char *kb = kbase + static_cast<int64_t>(pb) * blk_stride + head_off;
-        const char *vb = vbase + static_cast<int64_t>(pb) * blk_stride + head_off;
+        const uint64_t blk_off = static_cast<uint64_t>(static_cast<uint32_t>(pb)) * blk_stride;
+        const char *kb = kbase + blk_off + head_off;
+        const char *vb = vbase + blk_off + head_off;
         const uint32_t slot = ring_lds + (gi & (NBUF - 1)) * (SLOT_U4 * 16);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
@@ -478,22 +482,36 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
         wait_lds();  // this wave's probabilities are in LDS
 
         // ---- P.V for all G heads of this lane's dims -------------------
+        // Two copies of the loop: only a partial block compares tokens with
+        // the context length (the compiler would otherwise evaluate the 16
+        // uniform compares of the masked copy for every block).
         const uint32_t *vw =
             reinterpret_cast<const uint32_t *>(slot + KV_INSTR * kWave) + pv_word;
         constexpr int kRowW = CPL * kWave * 4;  // dwords between the j = 0 and j = 1 rows
-        if constexpr (C::kBf16) {
+        auto value_product = [&](auto masked_tag) {
+            constexpr bool kMasked = decltype(masked_tag)::value;
+            if constexpr (C::kBf16) {
+                // Every LDS read of the product first (probabilities of both
+                // halves, the V words of all 8 token pairs), then the
+                // arithmetic: a lone wave on its SIMD hides the reads' latency
+                // only behind its own later instructions.
+                uint4 pq[2][G];
+                uint32_t va[8], vb[8];
 #pragma unroll
-            for (int quad = 0; quad < 2; ++quad) {
-                uint4 pq[G];
+                for (int quad = 0; quad < 2; ++quad)
 #pragma unroll
-                for (int h = 0; h < G; ++h)
-                    pq[h] = *reinterpret_cast<const uint4 *>(&s_p[h * 8 + quad * 4]);
+                    for (int h = 0; h < G; ++h)
+                        pq[quad][h] = *reinterpret_cast<const uint4 *>(&s_p[h * 8 + quad * 4]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int tq = quad * 4 + e;  // token pair 2 tq, 2 tq + 1
-                    uint32_t a = vw[tq * 32];
-                    uint32_t bb = vw[kRowW + tq * 32];
-                    if (partial) {  // masked rows contribute exactly zero, NaN or not
+                for (int tq = 0; tq < 8; ++tq) {
+                    va[tq] = vw[tq * 32];
+                    vb[tq] = vw[kRowW + tq * 32];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int tq = 0; tq < 8; ++tq) {  // token pair 2 tq, 2 tq + 1
+                    uint32_t a = va[tq], bb = vb[tq];
+                    if constexpr (kMasked) {  // masked rows contribute exactly zero, NaN or not
                         if (tok0 + 2 * tq >= ctx) a = 0;
                         if (tok0 + 2 * tq + 1 >= ctx) bb = 0;
                     }
@@ -504,32 +522,37 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
                     } else {
                         vp[0] = __builtin_amdgcn_perm(bb, a, pv_sel);
                     }
+                    const int e = tq & 3;
 #pragma unroll
                     for (int h = 0; h < G; ++h) {
-                        const uint32_t ph = e == 0 ? pq[h].x : e == 1 ? pq[h].y
-                                          : e == 2 ? pq[h].z : pq[h].w;
+                        const uint4 &pw = pq[tq >> 2][h];
+                        const uint32_t ph = e == 0 ? pw.x : e == 1 ? pw.y : e == 2 ? pw.z : pw.w;
 #pragma unroll
                         for (int d = 0; d < DPL; ++d)
                             acc[h][d] = dot2_bf16(ph, vp[d], acc[h][d]);
                     }
                 }
-            }
-        } else {
+            } else {
 #pragma unroll
-            for (int t = 0; t < kBS; ++t) {
-                const uint32_t *row = vw + (t & 1) * kRowW + (t >> 1) * 32;
-                float vv[DPL];
+                for (int t = 0; t < kBS; ++t) {
+                    const uint32_t *row = vw + (t & 1) * kRowW + (t >> 1) * 32;
+                    float vv[DPL];
 #pragma unroll
-                for (int d = 0; d < DPL; ++d)
-                    vv[d] = (partial && tok0 + t >= ctx) ? 0.f : as_f(row[d]);
+                    for (int d = 0; d < DPL; ++d)
+                        vv[d] = (kMasked && tok0 + t >= ctx) ? 0.f : as_f(row[d]);
 #pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const float ph = as_f(s_p[h * 16 + t]);
+                    for (int h = 0; h < G; ++h) {
+                        const float ph = as_f(s_p[h * 16 + t]);
 #pragma unroll
-                    for (int d = 0; d < DPL; ++d) acc[h][d] = fmaf(ph, vv[d], acc[h][d]);
+                        for (int d = 0; d < DPL; ++d) acc[h][d] = fmaf(ph, vv[d], acc[h][d]);
+                    }
                 }
             }
-        }
+        };
+        if (partial)
+            value_product(std::true_type{});
+        else
+            value_product(std::false_type{});
     };
 
     // this segment's partial: unnormalised acc, running max and sum
