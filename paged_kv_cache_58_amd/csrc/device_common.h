@@ -71,6 +71,16 @@ __device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t
                  : "memory");
 }
 
+// Five wait states after `base` is formed and before the first dma16 that
+// reads it: a vector memory instruction may read an SGPR only 5 wait states
+// after a VALU instruction wrote it, and a base built from a block id goes
+// v_readfirstlane -> a few SALU instructions -> the load (the compiler does
+// not look inside the asm for the hazard).  Taking `base` as an operand
+// keeps the nop after the instructions that form it.
+__device__ __forceinline__ void sgpr_settle(const void *base) {
+    asm volatile("s_nop 4" ::"s"(base) : "memory");
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight
 // (they retire in issue order).
 template <int N>
@@ -88,8 +98,8 @@ __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)"
 // may read an SGPR only 5 wait states after a VALU instruction wrote it (as
 // v_readlane does when a spilled base pointer is reloaded right before):
 // hence the s_nop 4.  This load runs once per 64 blocks; the hot-loop loads
-// (dma16) go without it, and a static test checks the compiled kernels for
-// the pattern instead.
+// (dma16) take sgpr_settle once per block where their base comes from a
+// block id, and a static test checks the compiled kernels for the pattern.
 __device__ __forceinline__ void dma4(const void *sbase, uint32_t voff, uint32_t lds) {
     asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds)
                  : "memory");

@@ -43,7 +43,6 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
-#include <type_traits>
 
 #include "device_common.h"
 #include "hip_util.h"
@@ -299,6 +298,7 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
         const char *qb = reinterpret_cast<const char *>(q) +
                          (static_cast<int64_t>(sg.b) * num_q_heads + (sg.ch * team_heads + hw) * G) *
                              C::kRowBytes;
+        sgpr_settle(qb);
 #pragma unroll
         for (int i = 0; i < C::kQDma; ++i)
             dma16(qb, static_cast<uint32_t>(min(1024 * i + 16 * lane, C::kQBytes - 16)),
@@ -308,6 +308,16 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
     // ---- issue side -------------------------------------------------------------
     Seg is = make_seg(sp.b, sp.g, sp.blk, 0);
     int is_k = 0, is_s0 = 0, in = 0, ipar = 0;  // ids chunk m of `is` sits in buffer (ipar + m) & 1
+    // this wave's KV head inside the pools, for segment `is`
+    auto head_base = [&](const char *pool, const Seg &sg) {
+        return pool + static_cast<int64_t>(sg.ch * team_heads + hw) * C::kRowBytes;
+    };
+    const char *k_seg = head_base(kbase, is);
+    const char *v_seg = head_base(vbase, is);
+    // The id of block `in`, read from LDS one issue ahead (valid when id_ready):
+    // the LDS round trip then overlaps the compute instead of the issue.
+    int id_next = 0;
+    bool id_ready = false;
     Seg nx = is;
     int nx_ipar = 0;
     bool nx_ready = false;
@@ -341,6 +351,9 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
             ++is_k;
             in = 0;
             nx_ready = false;
+            id_ready = false;
+            k_seg = head_base(kbase, is);
+            v_seg = head_base(vbase, is);
         }
         if ((in & (kWave - 1)) == 0) {  // entering chunk m: fetch what comes 64 blocks later
             const int m = in >> 6;
@@ -354,12 +367,16 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
                 nx_ready = true;
             }
         }
-        const int pb = __builtin_amdgcn_readfirstlane(s_ids[(ipar + (in >> 6)) & 1][in & (kWave - 1)]);
-        const int64_t head_off = static_cast<int64_t>(is.ch * team_heads + hw) * C::kRowBytes;
+        int pb;
+        if (id_ready)
+            pb = __builtin_amdgcn_readfirstlane(id_next);
+        else
+            pb = __builtin_amdgcn_readfirstlane(s_ids[(ipar + (in >> 6)) & 1][in & (kWave - 1)]);
         const uint64_t blk_off = static_cast<uint64_t>(static_cast<uint32_t>(pb)) * blk_stride;
-        const char *kb = kbase + blk_off + head_off;
-        const char *vb = vbase + blk_off + head_off;
+        const char *kb = k_seg + blk_off;
+        const char *vb = v_seg + blk_off;
         const uint32_t slot = ring_lds + (gi & (NBUF - 1)) * (SLOT_U4 * 16);
+        sgpr_settle(kb);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -372,12 +389,18 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
                 dma16(vb, off[j][i], slot + (KV_INSTR + j * CPL + i) * (kWave * 16));
         ++in;
         ++gi;
+        // Read the next id of this segment now.  Its chunk was fetched 64
+        // blocks before its first block (the compute side has waited for
+        // everything issued before that), and the next fetch writes the other
+        // buffer.  A successor segment's first id is read at the switch, after
+        // the wait for its fetch.
+        id_ready = in < is.nblk;
+        if (id_ready) id_next = s_ids[(ipar + (in >> 6)) & 1][in & (kWave - 1)];
         return true;
     };
 
     // ---- compute side -----------------------------------------------------------
     Seg cs = is;
-    int cn = 0;             // the next block of `cs` to compute
     float m_run = kNegInf;  // running max of head hc (scaled, log2 units)
     float l_run = 0.f;      // this lane's share of the running sum of head hc
     float acc[G][DPL];
@@ -482,77 +505,73 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
         wait_lds();  // this wave's probabilities are in LDS
 
         // ---- P.V for all G heads of this lane's dims -------------------
-        // Two copies of the loop: only a partial block compares tokens with
-        // the context length (the compiler would otherwise evaluate the 16
-        // uniform compares of the masked copy for every block).
         const uint32_t *vw =
             reinterpret_cast<const uint32_t *>(slot + KV_INSTR * kWave) + pv_word;
         constexpr int kRowW = CPL * kWave * 4;  // dwords between the j = 0 and j = 1 rows
-        auto value_product = [&](auto masked_tag) {
-            constexpr bool kMasked = decltype(masked_tag)::value;
-            if constexpr (C::kBf16) {
-                // Every LDS read of the product first (probabilities of both
-                // halves, the V words of all 8 token pairs), then the
-                // arithmetic: a lone wave on its SIMD hides the reads' latency
-                // only behind its own later instructions.
-                uint4 pq[2][G];
-                uint32_t va[8], vb[8];
+        if constexpr (C::kBf16) {
+            // Every LDS read of the product first (probabilities of both
+            // halves, the V words of all 8 token pairs), then the arithmetic:
+            // a lone wave on its SIMD hides the reads' latency only behind its
+            // own later instructions.
+            uint4 pq[2][G];
+            uint32_t va[8], vb[8];
 #pragma unroll
-                for (int quad = 0; quad < 2; ++quad)
+            for (int quad = 0; quad < 2; ++quad)
 #pragma unroll
-                    for (int h = 0; h < G; ++h)
-                        pq[quad][h] = *reinterpret_cast<const uint4 *>(&s_p[h * 8 + quad * 4]);
+                for (int h = 0; h < G; ++h)
+                    pq[quad][h] = *reinterpret_cast<const uint4 *>(&s_p[h * 8 + quad * 4]);
+#pragma unroll
+            for (int tq = 0; tq < 8; ++tq) {
+                va[tq] = vw[tq * 32];
+                vb[tq] = vw[kRowW + tq * 32];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // Rows at or past the context contribute exactly zero, NaN or
+            // not.  Only a partial block compares tokens with the context
+            // length, in place on the loaded words, so that one copy of the
+            // arithmetic serves every block.
+            if (partial) {
 #pragma unroll
                 for (int tq = 0; tq < 8; ++tq) {
-                    va[tq] = vw[tq * 32];
-                    vb[tq] = vw[kRowW + tq * 32];
-                }
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int tq = 0; tq < 8; ++tq) {  // token pair 2 tq, 2 tq + 1
-                    uint32_t a = va[tq], bb = vb[tq];
-                    if constexpr (kMasked) {  // masked rows contribute exactly zero, NaN or not
-                        if (tok0 + 2 * tq >= ctx) a = 0;
-                        if (tok0 + 2 * tq + 1 >= ctx) bb = 0;
-                    }
-                    uint32_t vp[DPL];
-                    if constexpr (DPL == 2) {
-                        vp[0] = __builtin_amdgcn_perm(bb, a, 0x05040100u);
-                        vp[1] = __builtin_amdgcn_perm(bb, a, 0x07060302u);
-                    } else {
-                        vp[0] = __builtin_amdgcn_perm(bb, a, pv_sel);
-                    }
-                    const int e = tq & 3;
-#pragma unroll
-                    for (int h = 0; h < G; ++h) {
-                        const uint4 &pw = pq[tq >> 2][h];
-                        const uint32_t ph = e == 0 ? pw.x : e == 1 ? pw.y : e == 2 ? pw.z : pw.w;
-#pragma unroll
-                        for (int d = 0; d < DPL; ++d)
-                            acc[h][d] = dot2_bf16(ph, vp[d], acc[h][d]);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int t = 0; t < kBS; ++t) {
-                    const uint32_t *row = vw + (t & 1) * kRowW + (t >> 1) * 32;
-                    float vv[DPL];
-#pragma unroll
-                    for (int d = 0; d < DPL; ++d)
-                        vv[d] = (kMasked && tok0 + t >= ctx) ? 0.f : as_f(row[d]);
-#pragma unroll
-                    for (int h = 0; h < G; ++h) {
-                        const float ph = as_f(s_p[h * 16 + t]);
-#pragma unroll
-                        for (int d = 0; d < DPL; ++d) acc[h][d] = fmaf(ph, vv[d], acc[h][d]);
-                    }
+                    if (tok0 + 2 * tq >= ctx) va[tq] = 0;
+                    if (tok0 + 2 * tq + 1 >= ctx) vb[tq] = 0;
                 }
             }
-        };
-        if (partial)
-            value_product(std::true_type{});
-        else
-            value_product(std::false_type{});
+#pragma unroll
+            for (int tq = 0; tq < 8; ++tq) {  // token pair 2 tq, 2 tq + 1
+                uint32_t vp[DPL];
+                if constexpr (DPL == 2) {
+                    vp[0] = __builtin_amdgcn_perm(vb[tq], va[tq], 0x05040100u);
+                    vp[1] = __builtin_amdgcn_perm(vb[tq], va[tq], 0x07060302u);
+                } else {
+                    vp[0] = __builtin_amdgcn_perm(vb[tq], va[tq], pv_sel);
+                }
+                const int e = tq & 3;
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const uint4 &pw = pq[tq >> 2][h];
+                    const uint32_t ph = e == 0 ? pw.x : e == 1 ? pw.y : e == 2 ? pw.z : pw.w;
+#pragma unroll
+                    for (int d = 0; d < DPL; ++d)
+                        acc[h][d] = dot2_bf16(ph, vp[d], acc[h][d]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < kBS; ++t) {
+                const uint32_t *row = vw + (t & 1) * kRowW + (t >> 1) * 32;
+                float vv[DPL];
+#pragma unroll
+                for (int d = 0; d < DPL; ++d)
+                    vv[d] = (partial && tok0 + t >= ctx) ? 0.f : as_f(row[d]);
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const float ph = as_f(s_p[h * 16 + t]);
+#pragma unroll
+                    for (int d = 0; d < DPL; ++d) acc[h][d] = fmaf(ph, vv[d], acc[h][d]);
+                }
+            }
+        }
     };
 
     // this segment's partial: unnormalised acc, running max and sum
@@ -580,32 +599,30 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
     reset();
     for (int n = 0; n < NBUF - 1 && gi < P; ++n) issue_next();
 
-    bool fresh = false;  // `cs` was just entered: its q is still in LDS
-    for (int gcb = 0; gcb < P; ++gcb) {
-        if (fresh) {
-            // The segment's first block has landed, and its q rows (loaded
-            // before it) with them.  They go to registers before the issue
-            // side may refill that q buffer for the segment after next.
-            wait_blocks<PER_BLOCK, NBUF>(min(NBUF - 1, gi - 1 - gcb));
-            load_q(cs_k & 1);
-            reset();
-            fresh = false;
-        }
-        while (gi < P && gi <= gcb + NBUF - 1) {
-            wait_lds();  // slot gi % NBUF, the ids and the q buffers in LDS are read
-            if (!issue_next()) break;
-        }
-        wait_blocks<PER_BLOCK, NBUF>(min(NBUF - 1, gi - 1 - gcb));
-        compute_block(cn, gcb);
-        if (++cn == cs.nblk) {
-            store_partial();
-            if (gcb + 1 < P) {  // the issue side is in the next segment already
-                cs = is;
-                ++cs_k;
-                cn = 0;
-                fresh = true;
+    // Segments of the share, then their blocks (block gcb of the share is
+    // block n of segment cs).
+    int gcb = 0;
+    for (;;) {
+        for (int n = 0; n < cs.nblk; ++n, ++gcb) {
+            while (gi < P && gi <= gcb + NBUF - 1) {
+                wait_lds();  // slot gi % NBUF, the ids and the q buffers in LDS are read
+                if (!issue_next()) break;
             }
+            wait_blocks<PER_BLOCK, NBUF>(min(NBUF - 1, gi - 1 - gcb));
+            compute_block(n, gcb);
         }
+        store_partial();
+        if (gcb == P) break;
+        // The issue side is in the next segment already (it issued the
+        // segment's first block before this segment's last was computed).
+        cs = is;
+        ++cs_k;
+        // That first block has landed, and the segment's q rows (loaded
+        // before it) with it.  They go to registers before the issue side
+        // may refill that q buffer for the segment after next.
+        wait_blocks<PER_BLOCK, NBUF>(min(NBUF - 1, gi - 1 - gcb));
+        load_q(cs_k & 1);
+        reset();
     }
 }
 
