@@ -443,13 +443,14 @@ hipError_t enqueue_stream_reduce(T *out, const float *ws_acc, const float2 *ws_m
 // on the current device, so that every share streams from start to end.
 // Work-groups per CU = the smaller of the register limit (occupancy query)
 // and the LDS limit (CU LDS / the kernel's static LDS), rounded down to a
-// multiple of per_cu_multiple; shares = work-groups x waves_per_group
-// (each wave of a work-group streams its own share), capped by the
-// workspace's slot count.  The value is cached per device and kernel
-// instantiation; PA_STREAM_WAVES overrides it (tuning and tests).  Launch
-// ceil(shares / waves_per_group) work-groups.
+// multiple of per_cu_multiple and at most max_per_cu (0: no limit);
+// shares = work-groups x waves_per_group (each wave of a work-group streams
+// its own share), capped by the workspace's slot count.  The value is cached
+// per device and kernel instantiation; PA_STREAM_WAVES overrides it (tuning
+// and tests).  Launch ceil(shares / waves_per_group) work-groups.
 template <typename K>
-int stream_waves(K kernel, int threads, int per_cu_multiple, int cap, int waves_per_group = 1) {
+int stream_waves(K kernel, int threads, int per_cu_multiple, int cap, int waves_per_group = 1,
+                 int max_per_cu = 0) {
     static std::atomic<int> cache[kMaxDevices];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
@@ -468,6 +469,7 @@ int stream_waves(K kernel, int threads, int per_cu_multiple, int cap, int waves_
             const int by_lds = lds_cu / static_cast<int>(attr.sharedSizeBytes);
             if (by_lds < per_cu) per_cu = by_lds;
         }
+        if (max_per_cu > 0 && per_cu > max_per_cu) per_cu = max_per_cu;
         if (per_cu >= per_cu_multiple) per_cu -= per_cu % per_cu_multiple;
         w = cus * per_cu * waves_per_group;
         if (w <= 0) w = 256;

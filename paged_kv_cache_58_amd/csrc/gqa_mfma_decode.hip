@@ -317,6 +317,7 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
                 const int64_t blk_b = static_cast<int64_t>(kMBS) * num_kv_heads * TL::kRowB;
                 const char *kb = kbase + static_cast<int64_t>(pb) * blk_b;
                 const char *vb = vbase + static_cast<int64_t>(pb) * blk_b;
+                sgpr_settle(kb);
 #pragma unroll
                 for (int i = 0; i < TL::kDma; ++i) dma16(kb, dma_off[i], slot + i * 1024);
 #pragma unroll
@@ -325,6 +326,7 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
                 const int64_t tile = static_cast<int64_t>(pb) * num_kv_heads + g;
                 const char *kb = kbase + tile * TL::kKB;
                 const char *vb = vbase + tile * TL::kKB;
+                sgpr_settle(kb);
 #pragma unroll
                 for (int i = 0; i < TL::kDma; ++i) dma16(kb, dma_off[i], slot + i * 1024);
 #pragma unroll
@@ -520,7 +522,11 @@ pa_status enqueue_gqa_mfma(const DecodeShape &s, const DecodeArgs &a, const Deco
     float2 *ml = reinterpret_cast<float2 *>(ws + p.ml_offset);
     int32_t *prefix = reinterpret_cast<int32_t *>(ws + p.prefix_offset);
     const auto kernel = gqa_mfma_partition_kernel<MX, NBUF, NT>;
-    const int waves = stream_waves(kernel, kWave * kMGroupWaves, 1, kStreamWavesMax, kMGroupWaves);
+    // MXFP8: two work-groups (8 waves) per CU although LDS holds four: on the
+    // 70B-shape batch 179 us against 189 us with 16 waves (and 1024 fewer
+    // partial slots to merge), 187 against 199 us at 128K contexts.
+    const int waves = stream_waves(kernel, kWave * kMGroupWaves, 1, kStreamWavesMax, kMGroupWaves,
+                                   MX ? 2 : 0);
     const int th = team_heads(s.num_kv_heads, kMGroupWaves, p.group);
     const int nshares = waves / th > 0 ? waves / th : 1;
     const int groups = (nshares * th + kMGroupWaves - 1) / kMGroupWaves;
