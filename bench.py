@@ -80,11 +80,23 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
+def code_tokens(text: str) -> str:
+    """C++ source without comments and with whitespace runs collapsed: what
+    the compiler sees, so that a comment edit keeps a measurement valid.
+    (String literals in these sources hold no comment markers.)"""
+    import re
+
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code (comments and layout excluded)."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "paged_kv_cache_58_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "paged_kv_cache_58_amd", "csrc", name), encoding="utf-8") as f:
+            h.update(code_tokens(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -22,15 +22,16 @@
 //    c, c+8, ...: every load is 16 bytes wide and each group of 8 lanes reads
 //    one 128-byte line.
 //  * K and V travel HBM -> LDS with global_load_lds_dwordx4 (no VGPRs on the
-//    way) into a ring of kRingDepth blocks, so several blocks are in flight
-//    while the wave computes on an earlier one; explicit vmcnt waits retire
-//    exactly one block per step.
+//    way) into a ring of NBUF blocks, so several blocks are in flight while
+//    the wave computes on an earlier one; explicit vmcnt waits retire exactly
+//    one block per step, and the ring runs on across a share's segments (the
+//    next segment's block ids and q are fetched ahead, see "segments").
 //  * The block is fetched once for all G query heads of the group: each lane
 //    holds its slice of q for all G heads and forms G partial dot products
 //    per token with v_dot2_f32_bf16 (fp32 FMA for fp32 inputs).  The 8 lanes
 //    of a token pair finish the dot products with three DPP adds
 //    (quad_perm 1032, quad_perm 2301, row_half_mirror).
-//  * Softmax: lane c owns head c.  The running max is raised only when a
+//  * Softmax: lane c carries head c / (8 / G).  The running max is raised only when a
 //    score exceeds it by more than kSlack (log2 units), which keeps every
 //    weight below 2^kSlack; otherwise no cross-lane max and no rescale run.
 //    The result is the same exact softmax: any reference value works as
