@@ -55,6 +55,28 @@ __device__ __forceinline__ float dpp(float x) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// x[l] and x[l ^ 16] (r16) or x[l] and x[l ^ 32] (r32) in every lane l, by
+// gfx950's row swaps (a swap of a register with itself hands each lane its
+// partner's value) rather than __shfl_xor, which goes through the LDS
+// crossbar and waits for it.  max and + are symmetric, so both lanes of a
+// pair get the same bits.
+__device__ __forceinline__ float max_r16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(as_u(x), as_u(x), false, false);
+    return fmaxf(as_f(r[0]), as_f(r[1]));
+}
+__device__ __forceinline__ float max_r32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(as_u(x), as_u(x), false, false);
+    return fmaxf(as_f(r[0]), as_f(r[1]));
+}
+__device__ __forceinline__ float sum_r16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(as_u(x), as_u(x), false, false);
+    return as_f(r[0]) + as_f(r[1]);
+}
+__device__ __forceinline__ float sum_r32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(as_u(x), as_u(x), false, false);
+    return as_f(r[0]) + as_f(r[1]);
+}
+
 // LDS address of a __shared__ object (what M0 takes for an LDS-DMA load).
 __device__ __forceinline__ uint32_t lds_offset(const void *p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(

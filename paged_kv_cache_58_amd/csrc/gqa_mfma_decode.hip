@@ -34,7 +34,7 @@
 //    the softmax to the matrix core without leaving the lane; V^T comes from
 //    LDS by ds_read_b64_tr_b16.
 //  * Softmax per head (column): max over the lane's 4 scores and the 4 quads
-//    (two lane exchanges); the running max moves only when a score passes it
+//    (two row swaps, v_permlane16_swap and v_permlane32_swap); the running max moves only when a score passes it
 //    by more than kSlack (log2 units), so the rescale of the 32 accumulators
 //    is rare; probabilities are rounded to bf16 for the product and the
 //    running sum adds the rounded values.
@@ -412,8 +412,7 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
                                    : kNegInf;
                 }
                 float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-                bm = fmaxf(bm, __shfl_xor(bm, 16));
-                bm = fmaxf(bm, __shfl_xor(bm, 32));
+                bm = max_r32(max_r16(bm));
                 if (__builtin_amdgcn_ballot_w64(bm > m_run[ct] + kMSlack) != 0) {
                     const float m_new = fmaxf(m_run[ct], bm);
                     const float alpha =
@@ -487,8 +486,7 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
             ncols;
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
-            float l_tot = l_run[ct] + __shfl_xor(l_run[ct], 16);
-            l_tot += __shfl_xor(l_tot, 32);
+            const float l_tot = sum_r32(sum_r16(l_run[ct]));
             if (live[ct]) {
                 const int64_t row = slot_row + 16 * ct + col;
                 // a column with no visible token in the segment reports max -inf
