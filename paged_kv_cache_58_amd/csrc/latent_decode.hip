@@ -40,10 +40,13 @@
 //    matrix core consumes (a wave reading every dim itself would issue four
 //    times the transposed reads, which run at about a quarter of the rate of
 //    16-byte reads).
-//  * Software pipeline, one barrier per unit: the value products of unit u
-//    run beside the score products of unit u + 1, and the softmax of unit
-//    u + 1 beside the rest of them, so the matrix core has work while the
-//    vector unit takes the exponentials.
+//  * Software pipeline, one barrier per unit: the score products of unit
+//    u + 1 run as one chain with the unit's DMA rows and bookkeeping between
+//    them, then the value products of unit u one at a time, each after an
+//    even share of the softmax of unit u + 1.  A wave overlaps its own
+//    matrix-core and vector work only when other instructions follow a
+//    product: a product issued right after another stalls the wave until the
+//    first one leaves the matrix core.
 //  * LDS layout of a unit: the first 64 16-byte chunks of every row (dims
 //    0..511) in a 32 KB region of 1 KB rows, the 8 RoPE chunks in a 4 KB
 //    region of 128-byte rows.  Chunk c of main row t sits at c ^ swm(t),
@@ -197,9 +200,7 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
     constexpr int kVR = 3;              // V^T operands read ahead
     constexpr int kRA = 3;              // score A operands read ahead
     constexpr int kNV = 2 * DT;         // value steps (of HT products) per unit
-    // of them beside the score chain, the rest beside the softmax: none
-    // (measured 1-2% faster than half beside the chain)
-    constexpr int kVA = 0;
+    constexpr int kVP = kNV * HT;       // value products per unit
 
     // Ring: main regions (dims 0..511 of 32 rows) for units u % 4, RoPE
     // regions (dims 512..575) for units u % 3: while step u runs, unit u's
@@ -210,7 +211,7 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
     __shared__ __attribute__((aligned(16))) uint4 s_rope[3][(kUnitB - kUnitMainB) / 16];
     __shared__ __attribute__((aligned(16))) u32x4_t s_p[2][HT][2][kWave];  // P^T fragments of unit u in [u & 1]
     __shared__ float s_alpha[2][HT * kHeads];  // rescale factor of each head, unit u in [u & 1]
-    __shared__ __attribute__((aligned(16))) int32_t s_flag[2][4];  // head tile ht rescaled in unit u
+    __shared__ __attribute__((aligned(4))) uint8_t s_flag[2][4];  // byte ht: head tile ht rescaled in unit u
     __shared__ __attribute__((aligned(16))) int32_t s_ids[2][kWave];
     __shared__ __attribute__((aligned(16))) uint4 s_sink[kWave];  // target of padding loads
     __shared__ float s_l[HT * kHeads];  // each head's running sum, for the partial
@@ -426,6 +427,9 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
         // swm(NW k): one lane term serves every row of the wave, and the
         // wave's row offset goes into the unit's source and destination.
         constexpr int kPer = (kDmaPerUnit + NW - 1) / NW;
+        // rows issued beside the score chain, one before every third product
+        // from the third; the rest (with a short chain) right after it
+        constexpr int kChainRows = kKW / 3 < kPer ? kKW / 3 : kPer;
         const uint32_t ln_w = static_cast<uint32_t>(lane) ^ (static_cast<uint32_t>(wave) << 2);
         struct UnitDma {
             const char *src;  // the unit's first row + wave rows
@@ -436,10 +440,14 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
         const char *pool = reinterpret_cast<const char *>(latent);
         auto unit_dma = [&](int u, bool live, int pb) {
             UnitDma d;
-            d.src = (live ? pool + static_cast<int64_t>(pb) * kBlockB + ((h0 + u) & 1) * kUnitTok * kRowB
-                          : pool) + wave * kRowB;
+            // (operands are selected rather than results, which keeps this
+            // free of branches)
+            const int pbl = live ? pb : 0;
+            const int half = live ? ((h0 + u) & 1) : 0;
+            d.src = pool + static_cast<int64_t>(pbl) * kBlockB + half * (kUnitTok * kRowB) + wave * kRowB;
             d.dst = main_slot(u) + wave * kMainRowB;
-            d.nfetch = (live ? min(kUnitTok, ctx - (seg_tok0 + u * kUnitTok)) : 0) - wave;
+            const int rows = min(kUnitTok, ctx - (seg_tok0 + u * kUnitTok));
+            d.nfetch = (live ? rows : 0) - wave;
             d.live = live;
             return d;
         };
@@ -459,9 +467,11 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
         // Block ids come in chunks of 64 through s_ids; wave 0 fetches chunk
         // c + 1 when the first unit of chunk c is issued.
         auto refill_ids = [&](int u) {
-            const int n = (h0 + u) >> 1;
-            if (wave == 0 && ((h0 + u) & 1) == 0 && (n & (kWave - 1)) == 0 && n > 0 && n + kWave < nblk)
-                fetch_ids((n >> 6) + 1);
+            // unit u is the first half of block n = (h0 + u) / 2, n a positive
+            // multiple of 64 with a further chunk after this one
+            const int hu = h0 + u;
+            if (wave == 0 && (hu & (2 * kWave - 1)) == 0 && hu > 0 && (hu >> 1) + kWave < nblk)
+                fetch_ids((hu >> 7) + 1);
         };
         auto unit_id = [&](int u) {
             const int n = (h0 + u) >> 1;  // block of unit u, from blk_start
@@ -474,13 +484,21 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
         // budget)
         // (local step k of this wave's split; its main steps start at a
         // multiple of 8, so their chunk term stays a constant)
+        // The 8 main and kRopePer RoPE lane addresses of a unit are formed once
+        // (qk_bases); each read then adds only an immediate offset.
         const uint32_t qmain = static_cast<uint32_t>(ksplit * kMainPer / 8) * 256u;
-        auto qk_read = [&](int u, int k) {
-            const uint32_t addr =
-                k < kMainPer ? main_slot(u) + qmain + qrow + 256 * (k >> 3) + ((32u * (k & 7)) ^ qx)
-                             : rope_slot(u) + rrow +
-                                   ((32u * static_cast<uint32_t>(ksplit * kRopePer + k - kMainPer)) ^ rx);
-            return ds_read_b128(addr);
+        constexpr int kQB = kMainPer < 8 ? kMainPer : 8;
+        uint32_t qb_main[kQB], qb_rope[kRopePer];
+        auto qk_bases = [&](int u) {
+#pragma unroll
+            for (int j = 0; j < kQB; ++j) qb_main[j] = (main_slot(u) + qmain + qrow) + ((32u * j) ^ qx);
+#pragma unroll
+            for (int j = 0; j < kRopePer; ++j)
+                qb_rope[j] = (rope_slot(u) + rrow) +
+                             ((32u * static_cast<uint32_t>(ksplit * kRopePer + j)) ^ rx);
+        };
+        auto qk_read = [&](int k) {
+            return ds_read_b128(k < kMainPer ? qb_main[k & 7] + 256 * (k >> 3) : qb_rope[k - kMainPer]);
         };
         // V^T operand (k-step s, this wave's dim tile dt, half qq) of unit u
         auto pv_read = [&](int u, int s, int dt, int qq) {
@@ -491,11 +509,12 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
                               ((64u * (dg & 3)) ^ y));
         };
 
-        // The score chain of unit u over k-steps [k0, k1) into s (A operands
-        // read kRA steps ahead); before each product f(ks) runs, pinned there
-        // by the products' memory clobber.
+        // The score chain over k-steps [k0, k1) into s, of the unit whose
+        // addresses score_prefetch formed (A operands read kRA steps ahead);
+        // before each product f(ks) runs, pinned there by the products'
+        // memory clobber.
         bf16x8_t xa[kRA];
-        auto score_steps = [&](f32x16_t &s, int u, int k0, int k1, auto &&f) {
+        auto score_steps = [&](f32x16_t &s, int k0, int k1, auto &&f) {
 #pragma unroll
             for (int ks = k0; ks < k1; ++ks) {
                 f(ks);
@@ -503,46 +522,57 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
                 if (ks == 0) mfma_v0(s, xa[r], qf[ks]);
                 else if (ks + 1 < kKW) mfma_v(s, xa[r], qf[ks]);
                 else mfma_v_fence(s, xa[r], qf[ks]);
-                if (ks + kRA < kKW) xa[r] = qk_read(u, ks + kRA);
+                if (ks + kRA < kKW) xa[r] = qk_read(ks + kRA);
             }
         };
         auto score_prefetch = [&](int u) {
+            qk_bases(u);
 #pragma unroll
-            for (int ks = 0; ks < kRA; ++ks) xa[ks] = qk_read(u, ks);
+            for (int ks = 0; ks < kRA; ++ks) xa[ks] = qk_read(ks);
         };
 
-        // Softmax of unit u from its raw scores s, in pieces 0..11: the running
-        // max and sum of this lane's head and the P^T fragments of this wave's
-        // head tile into buffer u & 1, with the rescale factor when the max
-        // moved.  Register j of s: token 8 (j >> 2) + 4 hk + (j & 3) of the
-        // unit; tokens at or past seg_lim are masked, so the score chain that
-        // runs past a segment's last unit changes nothing here.
+        // Softmax of unit u from its raw scores s, in kSub pieces so that it
+        // spreads evenly between the value products: the running max and sum
+        // of this lane's head and the P^T fragments of this wave's head tile
+        // into buffer u & 1, with the rescale factor when the max moved.
+        // Register j of s: token 8 (j >> 2) + 4 hk + (j & 3) of the unit;
+        // tokens at or past seg_lim are masked, so the score chain that runs
+        // past a segment's last unit changes nothing here.  Pieces: 0..3
+        // scale registers 4k .. 4k + 3; 4 masks (only a unit that reaches the
+        // segment's limit, its last or one past it, holds tokens to mask); 5..8
+        // the running max over registers 4(k - 5) .. + 3; 9 the other 16
+        // tokens of the head, in lane ^ 32; 10 the running max and the rescale
+        // decision; 11..26 one probability each (register k - 11), the second
+        // of a pair packing the pair, adding both rounded values to the running
+        // sum and, every fourth pair, writing a P^T fragment.
+        constexpr int kSub = 27;
         bool moved = false;
         float bmax = kNegInf;
+        float pe = 0.f;  // the first probability of a pair
         uint32_t w4[4];
-        auto softmax_piece = [&](f32x16_t &s, int u, int piece) {
+        auto softmax_sub = [&](f32x16_t &s, int u, int k) {
             const int tok0 = seg_tok0 + u * kUnitTok;
-            if (piece < 2) {
-                float lmax = piece == 0 ? kNegInf : bmax;
+            if (k < 4) {
 #pragma unroll
-                for (int j = 8 * piece; j < 8 * piece + 8; ++j) s[j] *= scale_log2;
-                // only a unit that reaches the segment's limit (its last, or
-                // one past it) holds tokens to mask (uniform)
-                if (__builtin_expect(tok0 + kUnitTok > seg_lim, 0)) {
+                for (int j = 4 * k; j < 4 * k + 4; ++j) s[j] *= scale_log2;
+            } else if (k == 4) {
+                if (__builtin_expect(tok0 + kUnitTok > seg_lim, 0)) {  // (uniform)
 #pragma unroll
-                    for (int j = 8 * piece; j < 8 * piece + 8; ++j) {
+                    for (int j = 0; j < 16; ++j) {
                         const int tk = tok0 + 8 * (j >> 2) + 4 * hk + (j & 3);
                         s[j] = tk < seg_lim ? s[j] : kNegInf;
                     }
                 }
+            } else if (k < 9) {
+                const int b = k - 5;
+                float lmax = b == 0 ? kNegInf : bmax;
 #pragma unroll
-                for (int j = 8 * piece; j < 8 * piece + 8; ++j) lmax = fmaxf(lmax, s[j]);
+                for (int j = 4 * b; j < 4 * b + 4; ++j) lmax = fmaxf(lmax, s[j]);
                 bmax = lmax;
-            } else if (piece == 2) {
-                // the other 16 tokens of this head sit in lane ^ 32
+            } else if (k == 9) {
                 const auto r = __builtin_amdgcn_permlane32_swap(as_u(bmax), as_u(bmax), false, false);
                 bmax = fmaxf(as_f(r[0]), as_f(r[1]));
-            } else if (piece == 3) {
+            } else if (k == 10) {
                 moved = __builtin_amdgcn_ballot_w64(bmax > m_run + kLSlack) != 0;
                 if (moved) {
                     const float m_new = fmaxf(m_run, bmax);
@@ -551,23 +581,32 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
                     m_run = m_new;
                     if (hk == 0) s_alpha[u & 1][head] = alpha;
                 }
-                if (lane == 0) s_flag[u & 1][ht_w] = moved && u > 0;  // u = 0: nothing to rescale
+                if (lane == 0) s_flag[u & 1][ht_w] = (moved && u > 0) ? 1 : 0;  // u = 0: nothing to rescale
             } else {
-                // pieces 4..11: probabilities 2 v, 2 v + 1 of k-step v >> 2
-                const int v = piece - 4, sv = v >> 2, e = v & 3;
-                w4[e] = pack_bf16(exp2_fast(s[2 * v] - m_run), exp2_fast(s[2 * v + 1] - m_run));
-                l_run = dot2_bf16(w4[e], 0x3F803F80u, l_run);  // + both rounded values (bf16 1, 1)
-                if (e == 3)
-                    *(__attribute__((address_space(3))) u32x4_t *)(uintptr_t)(
-                        p_lds + (u & 1) * kPBuf + (ht_w * 2 + sv) * kWave * 16) =
-                        u32x4_t{w4[0], w4[1], w4[2], w4[3]};
+                const int jj = k - 11, v = jj >> 1, sv = v >> 2, e = v & 3;
+                if ((jj & 1) == 0) {
+                    pe = exp2_fast(s[jj] - m_run);
+                } else {
+                    w4[e] = pack_bf16(pe, exp2_fast(s[jj] - m_run));
+                    l_run = dot2_bf16(w4[e], 0x3F803F80u, l_run);  // + both rounded values (bf16 1, 1)
+                    if (e == 3)
+                        *(__attribute__((address_space(3))) u32x4_t *)(uintptr_t)(
+                            p_lds + (u & 1) * kPBuf + (ht_w * 2 + sv) * kWave * 16) =
+                            u32x4_t{w4[0], w4[1], w4[2], w4[3]};
+                }
             }
         };
 
-        // O^T += V^T P^T for this wave's dims, every head, unit u, in 2 DT value
-        // steps of HT products (V^T operand i = DT s + dt sits in slot i % kVR).
+        // O^T += V^T P^T for this wave's dims, every head, unit u: 2 DT value
+        // steps i (k-step i / DT, dim tile i % DT) of HT products each, issued
+        // one at a time.  value_begin(u, i) takes step i's V^T operand (read
+        // kVR steps ahead into slot i % kVR) and issues the reads of step
+        // i + kVR; value_product(i, ht) is the product of head tile ht.  The
+        // P^T fragments of k-step 0 are read during the score chain (p_read),
+        // each of k-step 1 right after its k-step 0 fragment's last product.
         s16x4_t vlo[kVR], vhi[kVR];
         bf16x8_t pb[HT];
+        bf16x8_t va;
         auto value_prefetch = [&](int u) {
 #pragma unroll
             for (int i = 0; i < kVR; ++i) {
@@ -575,37 +614,40 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
                 vhi[i] = pv_read(u, i / DT, i % DT, 1);
             }
         };
-        auto value_step = [&](int u, int i) {
-            const int s = i / DT, dt = i % DT;
-            if (dt == 0) {
-#pragma unroll
-                for (int ht = 0; ht < HT; ++ht)
-                    pb[ht] = ds_read_b128(p_lds + (u & 1) * kPBuf + (ht * 2 + s) * kWave * 16);
-            }
+        auto p_read = [&](int u, int s, int ht) {
+            pb[ht] = ds_read_b128(p_lds + (u & 1) * kPBuf + (ht * 2 + s) * kWave * 16);
+        };
+        auto value_begin = [&](int u, int i) {
             const int r = i % kVR;
-            const bf16x8_t va = __builtin_bit_cast(
-                bf16x8_t, __builtin_shufflevector(vlo[r], vhi[r], 0, 1, 2, 3, 4, 5, 6, 7));
-            if (i + kVR < 2 * DT) {
+            va = __builtin_bit_cast(bf16x8_t,
+                                    __builtin_shufflevector(vlo[r], vhi[r], 0, 1, 2, 3, 4, 5, 6, 7));
+            if (i + kVR < kNV) {
                 vlo[r] = pv_read(u, (i + kVR) / DT, (i + kVR) % DT, 0);
                 vhi[r] = pv_read(u, (i + kVR) / DT, (i + kVR) % DT, 1);
             }
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht) mfma_a(acc[dt * HT + ht], va, pb[ht]);
+        };
+        auto value_product = [&](int u, int i, int ht) {
+            mfma_a(acc[(i % DT) * HT + ht], va, pb[ht]);
+            if (i == DT - 1) p_read(u, 1, ht);
         };
         // rescale of the accumulators for unit u when a running max moved (rare);
         // tile by tile through VGPRs so that at most one tile is out of the
         // accumulation registers at a time
-        auto rescale = [&](int u) {
-            const u32x4_t fl = *(const __attribute__((address_space(3))) u32x4_t *)(
-                uintptr_t)lds_offset(&s_flag[u & 1][0]);
-            int any = 0;  // (flags of head tiles past HT are never written)
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht) any |= fl[ht];
+        // The flags of unit u (byte ht for head tile ht) are read right after
+        // the step's barrier and applied after the score chain, so that their
+        // LDS round trip is not waited for.
+        auto read_flags = [&](int u) {
+            return *(const __attribute__((address_space(3))) uint32_t *)(uintptr_t)lds_offset(
+                &s_flag[u & 1][0]);
+        };
+        auto rescale = [&](int u, uint32_t flw) {
+            uint32_t any = flw;
+            if constexpr (HT < 4) any &= (1u << (8 * HT)) - 1u;  // (bytes past HT are never written)
             if (__builtin_expect(any != 0, 0)) {
                 float alpha[HT];
 #pragma unroll
                 for (int ht = 0; ht < HT; ++ht)
-                    alpha[ht] = fl[ht] != 0 ? s_alpha[u & 1][ht * kHeads + l31] : 1.0f;
+                    alpha[ht] = ((flw >> (8 * ht)) & 0xFFu) != 0 ? s_alpha[u & 1][ht * kHeads + l31] : 1.0f;
                 acc_fence(acc);
 #pragma unroll
                 for (int t = 0; t < NA; ++t) {
@@ -649,15 +691,16 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
         };
 
         // ---- the software pipeline --------------------------------------------
-        // Step u: the value products of unit u beside the score products of
-        // unit u + 1, then the softmax of unit u + 1 beside the rest of unit
-        // u's value products.  Unit u + 3 streams into the regions units
-        // u - 1 (main) and u (RoPE) used.  One barrier per step: every wave's
-        // rows of unit u + 1 have landed, every wave's probabilities of unit u
-        // are in buffer u & 1, and every wave is done with step u - 1.  Past
-        // the segment's last unit the score chain runs over stale LDS and its
-        // tokens are all masked (one code path for every step keeps the
-        // register allocation in budget).
+        // Step u: the score products of unit u + 1 (one dependent chain, with
+        // this wave's DMA rows of unit u + 3 and the bookkeeping between its
+        // products), then the value products of unit u one at a time, each
+        // after an even share of the softmax of unit u + 1.  Unit u + 3
+        // streams into the regions units u - 1 (main) and u (RoPE) used.  One
+        // barrier per step: every wave's rows of unit u + 1 have landed, every
+        // wave's probabilities of unit u are in buffer u & 1, and every wave is
+        // done with step u - 1.  Past the segment's last unit the score chain
+        // runs over stale LDS and its tokens are all masked (one code path for
+        // every step keeps the register allocation in budget).
         for (int u = 0; u < 3; ++u) {
             const bool live = u < nunits;
             if (live) refill_ids(u);
@@ -671,11 +714,11 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
             __syncthreads();
             f32x16_t s;
             score_prefetch(0);
-            score_steps(s, 0, 0, kKW, [](int) {});
+            score_steps(s, 0, kKW, [](int) {});
             exchange(s);
             if (ksplit == 0) {
 #pragma unroll
-                for (int piece = 0; piece < 12; ++piece) softmax_piece(s, 0, piece);
+                for (int k = 0; k < kSub; ++k) softmax_sub(s, 0, k);
             }
         }
 
@@ -685,35 +728,44 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
             wait_vmem<kPer>();  // this wave's rows of unit u + 1 have landed (unit u + 2's may not)
             const int id3 = has_u3 ? unit_id(u3) : 0;
             __syncthreads();
-            if (has_u3) refill_ids(u3);
-            const UnitDma d3 = unit_dma(u3, has_u3, __builtin_amdgcn_readfirstlane(id3));
-            rescale(u);
+            // the step's LDS reads first, so that their latency passes under
+            // the bookkeeping
+            const uint32_t flw = read_flags(u);
             score_prefetch(u1);
             value_prefetch(u);
-            // value steps j < kVA beside the 36 score products of unit u + 1
-            // (step j before product ks with j * 36 / kVA in [ks, ks + 1)), then
-            // the softmax of unit u + 1 in 12 pieces beside the other kNV - kVA
-            // and this wave's DMA rows of unit u + 3
+            UnitDma d3;
             f32x16_t s;
-            score_steps(s, u1, 0, kKW, [&](int ks) {
+            score_steps(s, 0, kKW, [&](int ks) {
+                if (ks == 1) {
+                    if (has_u3) refill_ids(u3);
+                    d3 = unit_dma(u3, has_u3, __builtin_amdgcn_readfirstlane(id3));
+                }
+                if (ks >= 2 && (ks - 2) % 3 == 0 && (ks - 2) / 3 < kChainRows) issue_row(u3, d3, (ks - 2) / 3);
+                if (ks == kKW - 4) {  // unit u's P^T fragments of k-step 0
 #pragma unroll
-                for (int j = (ks * kVA + kKW - 1) / kKW; j < ((ks + 1) * kVA + kKW - 1) / kKW; ++j)
-                    value_step(u, j);
+                    for (int ht = 0; ht < HT; ++ht) p_read(u, 0, ht);
+                }
             });
+#pragma unroll
+            for (int k = kChainRows; k < kPer; ++k) issue_row(u3, d3, k);
+            rescale(u, flw);
             exchange(s);
-            // (the DMA rows of unit u + 3 go beside the softmax: rows k with
-            // k * 12 / kPer in [piece, piece + 1), each exactly once; beside the
-            // score products they overflowed the register budget)
-            constexpr int kVB = kNV - kVA;
+            // kVP value products, one per slot t; before product t the softmax
+            // pieces k with k kVP / kSub in [t, t + 1).  A scheduling fence
+            // after each product keeps the products apart: back to back, a
+            // product waits for the one before it to leave the matrix core and
+            // the wave issues nothing else meanwhile.
 #pragma unroll
-            for (int piece = 0; piece < 12; ++piece) {
-                if (ksplit == 0) softmax_piece(s, u1, piece);
+            for (int t = 0; t < kVP; ++t) {
+                const int i = t / HT, ht = t % HT;
+                if (ksplit == 0) {
 #pragma unroll
-                for (int k = (piece * kPer + 11) / 12; k < ((piece + 1) * kPer + 11) / 12; ++k)
-                    issue_row(u3, d3, k);
-#pragma unroll
-                for (int j = (piece * kVB + 11) / 12; j < ((piece + 1) * kVB + 11) / 12; ++j)
-                    value_step(u, kVA + j);
+                    for (int k = (t * kSub + kVP - 1) / kVP; k < ((t + 1) * kSub + kVP - 1) / kVP; ++k)
+                        softmax_sub(s, u1, k);
+                }
+                if (ht == 0) value_begin(u, i);
+                value_product(u, i, ht);
+                __builtin_amdgcn_sched_barrier(0);
             }
             // This unit's value products drain before the step ends: the
             // compiler may move the accumulators between registers on the
