@@ -42,8 +42,16 @@ WORKLOAD_TEXT = {
     "c5": "MLA-style latent decode bf16: batch 64, 128 heads over one 576-dim latent "
           "(V = first 512), block 64, ctx U[2048,8192]",
 }
-KERNEL_SOURCES = ["grouped_decode.hip", "gqa_mfma_decode.hip", "latent_decode.hip", "append.hip",
-                  "mxfp8_append.hip", "device_common.h", "plan.cpp", "plan.h"]
+# The sources each decode path is built from (its kernels, the append before
+# it, the shared device code and the host planning that sets its launch): a
+# measurement of one path stays valid while these hash the same.
+_SHARED_SOURCES = ["device_common.h", "plan.cpp", "plan.h"]
+KERNEL_SOURCES = {
+    "grouped": ["grouped_decode.hip", "append.hip"] + _SHARED_SOURCES,
+    "mfma": ["gqa_mfma_decode.hip", "append.hip"] + _SHARED_SOURCES,
+    "mxfp8": ["gqa_mfma_decode.hip", "mxfp8_append.hip"] + _SHARED_SOURCES,
+    "latent": ["latent_decode.hip", "append.hip"] + _SHARED_SOURCES,
+}
 
 
 FLUSH_BYTES = 512 << 20
@@ -91,24 +99,36 @@ def code_tokens(text: str) -> str:
     return " ".join(text.split())
 
 
-def kernel_source_hash() -> str:
-    """Hash of the kernel sources' code (comments and layout excluded)."""
+def traffic_family(key: str) -> str:
+    """The decode path a traffic_<key>.json describes: <config>, <config>_mfma
+    (the matrix-core variant of a native bf16 config) or <config>_mxfp8."""
+    if key.endswith("_mxfp8"):
+        return "mxfp8"
+    if key.endswith("_mfma"):
+        return "mfma"
+    import workloads
+
+    return "latent" if workloads.CONFIGS[key].mla else "grouped"
+
+
+def kernel_source_hash(family: str) -> str:
+    """Hash of the code (comments and layout excluded) of one path's sources."""
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, "paged_kv_cache_58_amd", "csrc", name), encoding="utf-8") as f:
             h.update(code_tokens(f.read()).encode())
     return h.hexdigest()[:16]
 
 
-def load_traffic(cfg: str, decode_bytes: int):
+def load_traffic(key: str, decode_bytes: int):
     """HBM traffic per decode from committed rocprofv3 --pmc summaries, or None
-    when they are missing or were taken on different kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{cfg}.json")
+    when they are missing or were taken on different sources of that path."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{key}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash(traffic_family(key)):
         return None
     return t.get("hbm_bytes_per_decode")
 
@@ -585,8 +605,8 @@ def main() -> int:
         d, cpu = native_oracle_check(w, L1, got, decode_bytes, args, oracle)
     max_err = float(d.max())
 
-    traffic = (load_traffic(args.config + ("_mxfp8" if mx else ""), decode_bytes)
-               if Q == 1 and not W and not H else None)
+    key = args.config + ("_mxfp8" if mx else "_mfma" if kernel_name(spec, mx, Q, W) == GROUPED_MFMA else "")
+    traffic = load_traffic(key, decode_bytes) if Q == 1 and not W and not H else None
     result = {
         "metric": METRIC,
         "value": round(value, 2),
