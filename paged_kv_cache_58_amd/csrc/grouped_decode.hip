@@ -575,20 +575,51 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
         }
     };
 
-    // this segment's partial: unnormalised acc, running max and sum
-    auto store_partial = [&]() {
-        const float l_tot = sum_over_tp(l_run);
-        const int64_t slot_row =
-            ((static_cast<int64_t>(sid) + static_cast<int64_t>(cs.b) * nchunks + cs.ch) * team_heads +
-             hw) * G;
-        if (tp == 0 && head_writer) ws_ml[slot_row + hc] = make_float2(m_run, l_tot);
+    // A segment's partial (unnormalised acc, running max and sum) is kept in
+    // registers and written when the share ends, or when more than kPend
+    // wait: vmcnt counts stores with the loads, in issue order, so a block
+    // loaded after a store cannot be waited for before the store completes,
+    // and under the read stream that takes longer than the ring's slack (on
+    // c3 the stores at every segment switch cost about 10 us of 315).
+    struct Part {
+        float acc[G][DPL];
+        float m, l;
+        int64_t row;  // first row of the segment's slot (uniform)
+    };
+    constexpr int kPend = 2;
+    Part pend[kPend];
+    int npend = 0;  // (uniform)
+    auto write_part = [&](const Part &pp) {
+        if (tp == 0 && head_writer) ws_ml[pp.row + hc] = make_float2(pp.m, pp.l);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            float *dst = ws_acc + (slot_row + h) * D + lane * DPL;
+            float *dst = ws_acc + (pp.row + h) * D + lane * DPL;
             if constexpr (DPL == 2)
-                *reinterpret_cast<float2 *>(dst) = make_float2(acc[h][0], acc[h][1]);
+                *reinterpret_cast<float2 *>(dst) = make_float2(pp.acc[h][0], pp.acc[h][1]);
             else
-                dst[0] = acc[h][0];
+                dst[0] = pp.acc[h][0];
+        }
+    };
+    auto finish_segment = [&]() {
+        Part cur;
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int d = 0; d < DPL; ++d) cur.acc[h][d] = acc[h][d];
+        cur.m = m_run;
+        cur.l = sum_over_tp(l_run);
+        cur.row = ((static_cast<int64_t>(sid) + static_cast<int64_t>(cs.b) * nchunks + cs.ch) * team_heads +
+                   hw) * G;
+        if (npend == kPend) {  // the oldest goes out now
+            write_part(pend[0]);
+#pragma unroll
+            for (int i = 0; i + 1 < kPend; ++i) pend[i] = pend[i + 1];
+            pend[kPend - 1] = cur;
+        } else {
+#pragma unroll
+            for (int i = 0; i < kPend; ++i)
+                if (i == npend) pend[i] = cur;
+            ++npend;
         }
     };
 
@@ -612,7 +643,7 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
             wait_blocks<PER_BLOCK, NBUF>(min(NBUF - 1, gi - 1 - gcb));
             compute_block(n, gcb);
         }
-        store_partial();
+        finish_segment();
         if (gcb == P) break;
         // The issue side is in the next segment already (it issued the
         // segment's first block before this segment's last was computed).
@@ -625,6 +656,9 @@ __global__ __launch_bounds__(kWave *kGroupWaves) void grouped_partition_kernel(
         load_q(cs_k & 1);
         reset();
     }
+#pragma unroll
+    for (int i = 0; i < kPend; ++i)
+        if (i < npend) write_part(pend[i]);
 }
 
 template <typename T, int D, int G, int NBUF>
