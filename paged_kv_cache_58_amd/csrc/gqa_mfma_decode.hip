@@ -497,106 +497,6 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
             }
         };
 
-        // The same block with several column tiles (bf16): one wave issues its
-        // products and its vector work from one instruction stream, and a
-        // product issued right after another stalls it until the first leaves
-        // the matrix core.  So the tiles are pipelined: while the scores of
-        // tile ct + 1 are taken, the softmax of tile ct finds its maximum; while
-        // the value products of tile ct - 1 run, the weights of tile ct are
-        // formed; one product at a time between the pieces (a scheduling
-        // fence after each).  Per value the arithmetic and its order are those
-        // of compute_block.
-        auto compute_block_tiles = [&](int n) {
-            const uint32_t kslot = ring_lds + (n & (NBUF - 1)) * TL::kSlotB;
-            const int tok0 = (wblk + n) * kMBS;
-            const int valid = ctx - tok0;
-            bf16x8_t ka[kMKSteps];
-#pragma unroll
-            for (int j = 0; j < kMKSteps; ++j) ka[j] = lds_b128(kslot + k_rd[j]);
-            s16x4_t va[kMDimTiles];
-#pragma unroll
-            for (int t = 0; t < kMDimTiles; ++t) va[t] = lds_tr_b64(kslot + TL::kKB + v_rd[t]);
-            const bool full = tok0 + kMBS <= all_visible && tok0 >= wstart;
-            f32x4_t s[NT];
-            uint32_t p01[NT], p23[NT];
-            float x[4], bm = 0.f, p[4];
-            auto score = [&](int ct, int j) {
-                s[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    ka[j], qb[ct][j], j == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : s[ct], 0, 0, 0);
-            };
-            auto value = [&](int ct, int t) {
-                const s16x4_t pb = __builtin_bit_cast(s16x4_t, u32x2_t{p01[ct], p23[ct]});
-                acc[ct][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[t], pb, acc[ct][t], 0, 0, 0);
-            };
-            // softmax of tile ct up to its maximum, in 4 pieces
-            auto soft_max = [&](int ct, int j) {
-                if (j == 0) {
-                    if (full) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) x[i] = s[ct][i] * scale_log2;
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            x[i] = (tok0 + 4 * quad + i < lim[ct] && tok0 + 4 * quad + i >= wstart)
-                                       ? s[ct][i] * scale_log2
-                                       : kNegInf;
-                    }
-                } else if (j == 1) {
-                    bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-                } else if (j == 2) {
-                    bm = max_r16(bm);
-                } else {
-                    bm = max_r32(bm);
-                }
-            };
-            // the weights of tile ct, in 8 pieces
-            auto soft_weights = [&](int ct, int t) {
-                if (t < 4) {
-                    p[t] = exp2_fast(x[t] - m_run[ct]);
-                } else if (t == 4) {
-                    p01[ct] = pack_bf16(p[0], p[1]);
-                    p23[ct] = pack_bf16(p[2], p[3]);
-                } else if (t == 5) {
-                    l_run[ct] += (bf16_lo(p01[ct]) + bf16_hi(p01[ct])) + (bf16_lo(p23[ct]) + bf16_hi(p23[ct]));
-                }
-            };
-#pragma unroll
-            for (int j = 0; j < kMKSteps; ++j) score(0, j);
-#pragma unroll
-            for (int ct = 0; ct < NT; ++ct) {
-#pragma unroll
-                for (int j = 0; j < kMKSteps; ++j) {
-                    if (ct + 1 < NT) score(ct + 1, j);
-                    soft_max(ct, j);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                if (__builtin_amdgcn_ballot_w64(bm > m_run[ct] + kMSlack) != 0) {
-                    const float m_new = fmaxf(m_run[ct], bm);
-                    const float alpha = exp2_fast(m_run[ct] - m_new);
-                    l_run[ct] *= alpha;
-                    m_run[ct] = m_new;
-#pragma unroll
-                    for (int t = 0; t < kMDimTiles; ++t) acc[ct][t] *= alpha;
-                }
-                if (ct == 1 && valid < kMBS) {  // before the first value product
-                    // rows past the context contribute exactly zero, NaN or not
-#pragma unroll
-                    for (int t = 0; t < kMDimTiles; ++t)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (4 * quad + e >= valid) va[t][e] = 0;
-                }
-#pragma unroll
-                for (int t = 0; t < kMDimTiles; ++t) {
-                    if (ct > 0) value(ct - 1, t);
-                    soft_weights(ct, t);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-#pragma unroll
-            for (int t = 0; t < kMDimTiles; ++t) value(NT - 1, t);
-        };
-
 #pragma unroll
         for (int n = 0; n < NBUF - 1; ++n)
             if (n < nblk) issue(n);
@@ -606,8 +506,7 @@ __global__ __launch_bounds__(kWave *kMGroupWaves) void gqa_mfma_partition_kernel
                 issue(n + NBUF - 1);
             }
             wait_mblocks<TL::kPerBlock, NBUF>(min(NBUF - 1, nblk - 1 - n));
-            if constexpr (!MX && NT > 1) compute_block_tiles(n);
-            else compute_block(n);
+            compute_block(n);
         }
 
         // ---- this segment's partial: unnormalised acc, running max and sum ----
