@@ -468,10 +468,13 @@ hipError_t enqueue_stream_reduce(T *out, const float *ws_acc, const float2 *ws_m
 // multiple of per_cu_multiple and at most max_per_cu (0: no limit);
 // shares = work-groups x waves_per_group (each wave of a work-group streams
 // its own share), capped by the workspace's slot count.  The value is cached
-// per device and kernel instantiation; PA_STREAM_WAVES overrides it (tuning
-// and tests).  Launch ceil(shares / waves_per_group) work-groups.
-template <typename K>
-int stream_waves(K kernel, int threads, int per_cu_multiple, int cap, int waves_per_group = 1,
+// per device and kernel: the kernel is a template argument, since the
+// instantiations of one kernel template share a function type (a cache keyed
+// by the type would hand one instantiation's count to another).
+// PA_STREAM_WAVES overrides it (tuning and tests).  Launch
+// ceil(shares / waves_per_group) work-groups.
+template <auto kernel>
+int stream_waves(int threads, int per_cu_multiple, int cap, int waves_per_group = 1,
                  int max_per_cu = 0) {
     static std::atomic<int> cache[kMaxDevices];
     int dev = 0;

@@ -561,9 +561,11 @@ pa_status enqueue_gqa_mfma(const DecodeShape &s, const DecodeArgs &a, const Deco
     const auto kernel = gqa_mfma_partition_kernel<MX, NBUF, NT>;
     // MXFP8: two work-groups (8 waves) per CU although LDS holds four: on the
     // 70B-shape batch 179 us against 189 us with 16 waves (and 1024 fewer
-    // partial slots to merge), 187 against 199 us at 128K contexts.
-    const int waves = stream_waves(kernel, kWave * kMGroupWaves, 1, kStreamWavesMax, kMGroupWaves,
-                                   MX ? 2 : 0);
+    // partial slots to merge), 187 against 199 us at 128K contexts.  bf16:
+    // one work-group per CU, which a 4-deep ring fills; with the 2-deep ring
+    // LDS would hold two, and that measures slower (c3 301.6 against 294.5 us).
+    const int waves = stream_waves<gqa_mfma_partition_kernel<MX, NBUF, NT>>(
+        kWave * kMGroupWaves, 1, kStreamWavesMax, kMGroupWaves, MX ? 2 : 1);
     const int th = team_heads(s.num_kv_heads, kMGroupWaves, p.group);
     const int nshares = waves / th > 0 ? waves / th : 1;
     const int groups = (nshares * th + kMGroupWaves - 1) / kMGroupWaves;

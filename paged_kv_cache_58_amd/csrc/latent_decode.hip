@@ -900,8 +900,8 @@ pa_status enqueue_latent(const DecodeShape &s, const DecodeArgs &a, const Decode
     const auto kernel = latent_partition_kernel<HT>;
     // one work-group per resident slot, and at least one per sequence (each
     // work-group streams a part of one sequence)
-    const int waves =
-        std::max(stream_waves(kernel, kLatentNW * kWave, 1, kLatentWavesMax), s.num_seqs);
+    const int waves = std::max(
+        stream_waves<latent_partition_kernel<HT>>(kLatentNW * kWave, 1, kLatentWavesMax), s.num_seqs);
     hipLaunchKernelGGL(kernel, dim3(waves), dim3(kLatentNW * kWave), 0, stream, acc, ml, prefix,
                        static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k_cache),
                        a.block_tables, a.context_lens, scale_log2, s.num_seqs, s.num_q_heads,

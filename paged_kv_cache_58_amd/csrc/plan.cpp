@@ -37,13 +37,16 @@ bool grouped_mfma_default(const DecodeShape &s) {
 }
 
 // Cache blocks each wave of the grouped paths streams into LDS (ring depth):
-// four 8 KB bf16 slots per wave (four waves per CU) measure faster than two
-// with eight waves; MXFP8 slots are half the size and take two.
-// PA_RING_DEPTH (2 or 4) overrides either default.
-int grouped_ring_depth(int default_depth = 4) {
+// two slots per wave, one block in flight while the wave computes on the
+// other.  With the partials written at the share's end, two 8 KB bf16 slots
+// per wave measure faster than four at the same four waves per CU (c3 299.6
+// against 304.5 us, c4 328.7 against 334.8, c2 and the several-query shapes
+// equal or faster), and MXFP8 slots, half the size, run two per wave at eight
+// waves per CU.  PA_RING_DEPTH (2 or 4) overrides the default.
+int grouped_ring_depth() {
     const char *env = std::getenv("PA_RING_DEPTH");
-    if (env && *env) return std::atoi(env) == 2 ? 2 : 4;
-    return default_depth;
+    if (env && *env) return std::atoi(env) == 4 ? 4 : 2;
+    return 2;
 }
 
 }  // namespace
@@ -159,8 +162,8 @@ pa_status plan_decode(const DecodeShape &s, DecodePlan *plan, std::string *why) 
                         "decode: num_seqs * max_blocks_per_seq * num_kv_heads exceeds 2^31-1");
         p.path = DecodePath::kMxfp8;
         // half-size MXFP8 slots: two per wave, at 8 waves per CU (the launch
-        // caps it there), measure faster than four (c3: 179 against 184 us)
-        p.ring_depth = grouped_ring_depth(2);
+        // caps it there), measure faster than four (c3: 171.8 against 175.7 us)
+        p.ring_depth = grouped_ring_depth();
     } else if (s.latent) {
         if (s.head_dim_k != 576 || s.head_dim_v != 512 || s.num_kv_heads != 1 ||
             s.block_size != 64 || s.dtype != PA_BF16 || s.num_q_heads % 16 != 0 ||
