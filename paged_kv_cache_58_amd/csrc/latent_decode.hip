@@ -13,8 +13,8 @@
 //
 // Here all query heads share one K/V row, so each block is a dense
 // contraction and runs on the matrix cores (v_mfma_f32_32x32x16_bf16).
-//  * A work-group has NW = 1, 2 or 4 waves, one per SIMD, and covers 32 NW
-//    heads (the query heads, padded).  Each sequence is cut into parts of
+//  * A work-group has four waves, one per SIMD, and covers every query head
+//    (padded to 32, 64 or 128).  Each sequence is cut into parts of
 //    near-equal size, one work-group per part, so a work-group streams one
 //    stretch of one sequence (split-KV partitions; the log-sum-exp reduce
 //    merges a sequence's parts).  The latent is streamed in units of 32
@@ -75,7 +75,6 @@ constexpr int kBlockB = kLBS * kRowB;         // 72 KB per block in HBM
 constexpr int kUnitTok = 32;                  // tokens per ring slot (half a block)
 constexpr int kUnitMainB = kUnitTok * kMainRowB;  // 32 KB main region
 constexpr int kUnitB = kUnitTok * kRowB;      // 36 KB per slot
-constexpr int kAhead = 2;                     // units in flight while one is computed
 constexpr int kSlots = 4;                     // ring slots (a power of two keeps the
                                               // slot arithmetic in shifts and immediates)
 constexpr int kDmaPerUnit = kUnitB / 1024;    // 36: 32 main rows + 4 groups of 8 RoPE rows
@@ -85,7 +84,6 @@ constexpr int kKSteps = kDK / 16;             // 36 k-steps of q . L
 constexpr int kMainKSteps = kDV / 16;         // the first 32 of them read the main region
 constexpr int kDimTiles = kDV / 32;           // 16 tiles of the output
 constexpr float kLSlack = 8.0f;               // lazy-rescale threshold, log2 units
-constexpr int kQD = 6;                        // S^T k-steps of A operands read ahead
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -134,15 +132,6 @@ __device__ __forceinline__ void mfma_v0(f32x16_t &c, bf16x8_t a, bf16x8_t b) {
 __device__ __forceinline__ void mfma_v(f32x16_t &c, bf16x8_t a, bf16x8_t b) {
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b) : "memory");
 }
-// The last product of each of the two score chains, then the fence.
-__device__ __forceinline__ void mfma_v_last(f32x16_t &c0, f32x16_t &c1, bf16x8_t a0, bf16x8_t a1,
-                                            bf16x8_t b0, bf16x8_t b1) {
-    asm volatile(
-        "v_mfma_f32_32x32x16_bf16 %0, %2, %4, %0\n\t"
-        "v_mfma_f32_32x32x16_bf16 %1, %3, %5, %1\n\t"
-        "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
-        : "+v"(c0), "+v"(c1) : "v"(a0), "v"(a1), "v"(b0), "v"(b1) : "memory");
-}
 // The last product of a score chain, then the fence.
 __device__ __forceinline__ void mfma_v_fence(f32x16_t &c, bf16x8_t a, bf16x8_t b) {
     asm volatile(
@@ -152,6 +141,17 @@ __device__ __forceinline__ void mfma_v_fence(f32x16_t &c, bf16x8_t a, bf16x8_t b
 }
 __device__ __forceinline__ void mfma_a(f32x16_t &c, bf16x8_t a, bf16x8_t b) {
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b) : "memory");
+}
+// A tile of the output accumulators read into VGPRs element by element by
+// inline asm that takes each value from the accumulation registers: code
+// after the unit loop reads the tiles only through this, so the compiler
+// keeps them where the loop left them instead of copying all 256 into VGPRs
+// at the loop's exit (which spills).  Only after acc_fence.
+__device__ __forceinline__ f32x16_t acc_tile(const f32x16_t &a) {
+    f32x16_t x;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x[e]) : "a"(a[e]));
+    return x;
 }
 // Fence over the output tiles (before the rescale and the final store).
 template <int N>
@@ -178,7 +178,8 @@ __device__ __forceinline__ void acc_fence(f32x16_t (&acc)[N]) {
 
 template <int HT>
 __global__ __launch_bounds__(kLatentNW *kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws_ml,
+void latent_partition_kernel(uint16_t *__restrict__ out, float *__restrict__ ws_acc,
+                             float2 *__restrict__ ws_ml,
                              int32_t *__restrict__ ws_prefix, const uint16_t *__restrict__ q,
                              const uint16_t *__restrict__ latent,
                              const int32_t *__restrict__ block_tables,
@@ -239,8 +240,9 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
     // one stretch of one sequence: a change of segment inside a work-group
     // (partial store, q reload, refilling the ring) costs about as much as a
     // dozen units, and units rather than 64-token blocks keep the parts
-    // within one unit of each other.  Its partial goes to slot j; work-group
-    // 0 stores K_b (num_seqs + 1 entries) for the reduce.  The unit counts of
+    // within one unit of each other.  Part j (below) stores its partial in
+    // slot j, and part 0 stores K_b (num_seqs + 1 entries) for the reduce; a
+    // sequence of one part writes its output itself.  The unit counts of
     // the first 256 sequences stay in registers for the search.
     auto seq_units = [&](int bb) {
         return bb < num_seqs ? (context_lens[bb] + kUnitTok - 1) / kUnitTok : 0;
@@ -275,6 +277,12 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
     });
     if (total == 0) return;  // every context empty: the reduce writes zeros
     const int grid = static_cast<int>(gridDim.x);
+    // Part index j runs over the work-groups so that the parts of a sequence
+    // sit on one XCD (work-groups are dealt to the 8 XCDs in turn, so j takes
+    // every 8th one; they then share that XCD's L2 for q and the block table).
+    const int j = grid % 8 == 0 ? static_cast<int>(blockIdx.x % 8u) * (grid / 8) +
+                                      static_cast<int>(blockIdx.x / 8u)
+                                : static_cast<int>(blockIdx.x);
     auto parts = [&](int P) {  // sum over the sequences of ceil(nu_b / P)
         int k_all = 0;
         each_chunk([&](int, int nu) { k_all += wave_sum((nu + P - 1) / P); });
@@ -297,19 +305,19 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
         const int bb = base + lane;
         const int k = (nu + P - 1) / P;
         const int incl = wave_incl_scan(k, lane);
-        if (blockIdx.x == 0 && wave == 0 && bb < num_seqs) ws_prefix[bb] = carry + incl - k;
+        if (j == 0 && wave == 0 && bb < num_seqs) ws_prefix[bb] = carry + incl - k;
         const uint64_t hit =
-            __builtin_amdgcn_ballot_w64(bb < num_seqs && carry + incl > static_cast<int>(blockIdx.x));
+            __builtin_amdgcn_ballot_w64(bb < num_seqs && carry + incl > j);
         if (b < 0 && hit != 0) {
             const int f = __builtin_ctzll(hit);
             b = base + f;
             k_b = __builtin_amdgcn_readlane(k, f);
             nu_b = __builtin_amdgcn_readlane(nu, f);
-            part = static_cast<int>(blockIdx.x) - (carry + __builtin_amdgcn_readlane(incl, f) - k_b);
+            part = j - (carry + __builtin_amdgcn_readlane(incl, f) - k_b);
         }
         carry += __builtin_amdgcn_readlane(incl, kWave - 1);
     });
-    if (blockIdx.x == 0 && tid == 0) ws_prefix[num_seqs] = carry;
+    if (j == 0 && tid == 0) ws_prefix[num_seqs] = carry;
     if (b < 0) return;  // a work-group past the last part (uniform)
     // this part: units [seg_u0, seg_u1) of sequence b; unit u of the segment
     // is half (h0 + u) & 1 of block blk_start + ((h0 + u) >> 1)
@@ -773,37 +781,52 @@ void latent_partition_kernel(float *__restrict__ ws_acc, float2 *__restrict__ ws
             acc_fence(acc);
         }
 
-        // ---- this part's partial ---------------------------------------------
-        // Slot blockIdx.x: (max, sum) per head in fp32 from the score waves,
-        // and the part's output normalised by its own sum, acc / l, in fp32.
-        // The tiles of this wave go out in register order, so every store
-        // writes 1 KB of consecutive bytes.
+        // ---- this part's result ----------------------------------------------
+        // A sequence of one part writes its output, acc / l in bf16.  Otherwise
+        // slot j gets (max, sum) per head in fp32 from the score waves, and
+        // the part's output normalised by its own sum, acc / l, in fp32; the
+        // tiles of a wave go out in register order, so every store writes
+        // 1 KB of consecutive bytes.
         const float l_tot = l_run + __shfl_xor(l_run, 32);
         if (ksplit == 0 && hk == 0) s_l[head] = l_tot;
         __syncthreads();  // every head's sum is in s_l
-        {
-            const int64_t slot = blockIdx.x;
+        float inv[HT];
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            const float l = s_l[ht * kHeads + l31];
+            inv[ht] = l > 0.f ? 1.0f / l : 0.f;
+        }
+        if (k_b == 1) {
+            // out[b, h, dims 32 (DT wave + dt) + 8 qd + 4 hk .. + 3] of tile
+            // t = dt HT + ht (h = 32 ht + lane % 32)
+#pragma unroll
+            for (int t = 0; t < NA; ++t) {
+                const int dt = t / HT, h = (t % HT) * kHeads + l31;
+                if (h >= num_heads) continue;
+                const f32x16_t x = acc_tile(acc[t]);
+                const float r = inv[t % HT];
+                uint16_t *o = out + (static_cast<int64_t>(b) * num_heads + h) * kDV +
+                              32 * (DT * wave + dt) + 4 * hk;
+#pragma unroll
+                for (int qd = 0; qd < 4; ++qd)
+                    *reinterpret_cast<uint2 *>(o + 8 * qd) =
+                        make_uint2(pack_bf16(x[4 * qd] * r, x[4 * qd + 1] * r),
+                                   pack_bf16(x[4 * qd + 2] * r, x[4 * qd + 3] * r));
+            }
+        } else {
+            const int64_t slot = j;
             if (ksplit == 0 && hk == 0) ws_ml[slot * (HT * kHeads) + head] = make_float2(m_run, l_tot);
             f32x4_t *dst = reinterpret_cast<f32x4_t *>(ws_acc) + slot * (kDimTiles * HT * 4 * kWave) +
                            (DT * wave) * (HT * 4 * kWave) + lane;
-            float inv[HT];
 #pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
-                const float l = s_l[ht * kHeads + l31];
-                inv[ht] = l > 0.f ? 1.0f / l : 0.f;
+            for (int t = 0; t < NA; ++t) {
+                const f32x16_t x = acc_tile(acc[t]);
+                const float r = inv[t % HT];
+#pragma unroll
+                for (int qd = 0; qd < 4; ++qd)
+                    dst[(t * 4 + qd) * kWave] =
+                        f32x4_t{x[4 * qd] * r, x[4 * qd + 1] * r, x[4 * qd + 2] * r, x[4 * qd + 3] * r};
             }
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-                    for (int qd = 0; qd < 4; ++qd) {
-                        const f32x16_t &t = acc[dt * HT + ht];
-                        const float r = inv[ht];
-                        dst[((dt * HT + ht) * 4 + qd) * kWave] =
-                            f32x4_t{t[4 * qd] * r, t[4 * qd + 1] * r, t[4 * qd + 2] * r,
-                                    t[4 * qd + 3] * r};
-                    }
         }
     }
 }
@@ -843,6 +866,7 @@ __global__ __launch_bounds__(HT *kWave) void latent_reduce_kernel(
         for (int qd = 0; qd < 4; ++qd) *reinterpret_cast<uint2 *>(o + 8 * qd) = make_uint2(0, 0);
         return;
     }
+    if (n == 1) return;  // a sequence of one part: the partition wrote its output
 
     // part p holds its normalised output O_p (fp32) and (m_p, l_p): the merge
     // weight is 2^(m_p - M) l_p
@@ -902,7 +926,8 @@ pa_status enqueue_latent(const DecodeShape &s, const DecodeArgs &a, const Decode
     // work-group streams a part of one sequence)
     const int waves = std::max(
         stream_waves<latent_partition_kernel<HT>>(kLatentNW * kWave, 1, kLatentWavesMax), s.num_seqs);
-    hipLaunchKernelGGL(kernel, dim3(waves), dim3(kLatentNW * kWave), 0, stream, acc, ml, prefix,
+    hipLaunchKernelGGL(kernel, dim3(waves), dim3(kLatentNW * kWave), 0, stream,
+                       static_cast<uint16_t *>(a.out), acc, ml, prefix,
                        static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k_cache),
                        a.block_tables, a.context_lens, scale_log2, s.num_seqs, s.num_q_heads,
                        s.max_blocks_per_seq);
