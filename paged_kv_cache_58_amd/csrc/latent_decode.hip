@@ -838,8 +838,8 @@ void latent_partition_kernel(uint16_t *__restrict__ out, float *__restrict__ ws_
 // thread t = 64 ht + lane always sees head 32 ht + (lane & 31), and 16-byte
 // piece qd of its tile holds dims 32 dg + 8 qd + 4 (lane >> 5) .. + 3.  The
 // kernel is a few memory round trips long, so every load of a batch of
-// kBatch parts is issued before any is used (parts past the last re-read the
-// last one and weigh 0), and batches merge by the running max.
+// kBatch parts is issued before any is used, and batches merge by the
+// running max.
 template <int HT>
 __global__ __launch_bounds__(HT *kWave) void latent_reduce_kernel(
     uint16_t *__restrict__ out, const float *__restrict__ ws_acc, const float2 *__restrict__ ws_ml,
@@ -877,7 +877,8 @@ __global__ __launch_bounds__(HT *kWave) void latent_reduce_kernel(
         f32x4_t v[kBatch][4];
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-            const int64_t slot = first + min(p0 + j, n - 1);
+            if (p0 + j >= n) break;  // (uniform)
+            const int64_t slot = first + p0 + j;
             mp[j] = ws_ml[slot * (HT * kHeads) + head];
             const f32x4_t *a = reinterpret_cast<const f32x4_t *>(ws_acc) +
                                slot * (kDimTiles * HT * 4 * kWave) + ((dg * HT + ht) * 4) * kWave +
@@ -898,7 +899,8 @@ __global__ __launch_bounds__(HT *kWave) void latent_reduce_kernel(
         }
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-            const float wgt = p0 + j < n && mp[j].y > 0.f ? exp2_fast(mp[j].x - M) * mp[j].y : 0.f;
+            if (p0 + j >= n) break;  // (uniform; those entries were not loaded)
+            const float wgt = mp[j].y > 0.f ? exp2_fast(mp[j].x - M) * mp[j].y : 0.f;
             den += wgt;
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd)
