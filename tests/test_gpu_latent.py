@@ -82,8 +82,11 @@ def test_latent_poison_and_determinism(dev):
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("waves", ["1", "3", "7", "512"])
+@pytest.mark.parametrize("waves", ["1", "3", "7", "24", "64", "512"])
 def test_latent_stream_split(dev, waves, monkeypatch):
+    """Grids of 1, 3 and 7 work-groups give each sequence one or two parts;
+    24, 64 and 512 (multiples of 8) place a sequence's parts on one XCD
+    (part j is work-group 8 (j mod grid/8) + j / (grid/8))."""
     say(f"case: latent, {waves} stream work-groups")
     monkeypatch.setenv("PA_STREAM_WAVES", waves)
     w = make_workload(_spec(128, [1, 1300, 0, 4100, 64]), seed=6)
