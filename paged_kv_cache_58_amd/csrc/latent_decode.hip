@@ -240,9 +240,10 @@ void latent_partition_kernel(uint16_t *__restrict__ out, float *__restrict__ ws_
     // one stretch of one sequence: a change of segment inside a work-group
     // (partial store, q reload, refilling the ring) costs about as much as a
     // dozen units, and units rather than 64-token blocks keep the parts
-    // within one unit of each other.  Part j (below) stores its partial in
-    // slot j, and part 0 stores K_b (num_seqs + 1 entries) for the reduce; a
-    // sequence of one part writes its output itself.  The unit counts of
+    // within one unit of each other.  The work-group of part index j (below)
+    // stores its partial in slot j, and the one of index 0 stores K_b
+    // (num_seqs + 1 entries) for the reduce; a sequence of one part writes
+    // its output itself.  The unit counts of
     // the first 256 sequences stay in registers for the search.
     auto seq_units = [&](int bb) {
         return bb < num_seqs ? (context_lens[bb] + kUnitTok - 1) / kUnitTok : 0;
