@@ -195,6 +195,16 @@ def test_reduce_one_wave_rows_many_slots(dev, ctx0, monkeypatch):
     say(f"  {compare(d.decode(), oracle.decode_workload(w), 'bf16')}")
 
 
+def test_many_sequences(dev, grouped_path):
+    """300 short ragged sequences, some empty: more than the 256 whose block
+    counts the stream shares keep in registers."""
+    say(f"case: 300 sequences, {grouped_path} kernel")
+    ctx = [(53 * i) % 311 for i in range(300)]
+    w = make_workload(custom_spec(300, 64, 8, 128, 16, "bf16", ctx=ctx), seed=41)
+    d = to_device(w, dev)
+    say(f"  {compare(d.decode(), oracle.decode_workload(w), 'bf16')}")
+
+
 @pytest.mark.parametrize("dtype,D,hq,hkv", [("bf16", 128, 64, 8), ("f32", 64, 4, 2),
                                             ("bf16", 64, 16, 4)])
 def test_long_segments_refill_block_ids(dev, dtype, D, hq, hkv, monkeypatch):

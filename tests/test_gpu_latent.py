@@ -94,6 +94,23 @@ def test_latent_stream_split(dev, waves, monkeypatch):
     say(f"  {compare(d.decode(), oracle.decode_workload(w), 'bf16')}")
 
 
+@pytest.mark.parametrize("waves", ["0", "512"])
+def test_latent_many_sequences(dev, waves, monkeypatch):
+    """300 short ragged sequences, some empty: more than the 256 whose unit
+    counts the part search keeps in registers, and more than one work-group
+    per CU.  With the default width the grid is one work-group per sequence
+    (every sequence one part, written by the partition itself); with 512
+    work-groups the longer sequences get two parts and their parts share an
+    XCD."""
+    say(f"case: latent, 300 sequences, PA_STREAM_WAVES={waves}")
+    if waves != "0":
+        monkeypatch.setenv("PA_STREAM_WAVES", waves)
+    ctx = [(37 * i) % 229 for i in range(300)]
+    w = make_workload(_spec(16, ctx), seed=31)
+    d = to_device(w, dev)
+    say(f"  {compare(d.decode(), oracle.decode_workload(w), 'bf16')}")
+
+
 @pytest.mark.parametrize("grid", ["8", "9", "17"])
 def test_latent_reduce_part_batches(dev, grid, monkeypatch):
     """One sequence of 72 units cut into 8, 9 or 15 parts by 8, 9 or 17
