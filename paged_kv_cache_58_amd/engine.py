@@ -111,6 +111,9 @@ class DecodeLoop:
         import torch
 
         b = len(seq_ids)
+        if b == 0:  # nothing to decode this step
+            return torch.empty((0, self.num_q_heads, self.head_dim), dtype=self.dtype,
+                               device=self.device)
         slots = np.empty(b, np.int32)
         for i, (sid, tok) in enumerate(zip(seq_ids, new_tokens)):
             slots[i] = self.manager.append_token(sid, int(tok))
