@@ -403,6 +403,16 @@ void latent_partition_kernel(uint16_t *__restrict__ out, float *__restrict__ ws_
         }
         drain_vmem();
         __syncthreads();  // ids landed for every wave; the previous segment is done
+        // The scale goes into each exponential (one fused multiply-add per
+        // score) and the running max is taken over the raw q . c, which needs
+        // a positive scale: a negative one negates q instead, and zero becomes
+        // the smallest normal float (every weight then rounds to 1, as at 0).
+        if (scale_log2 < 0.f) {  // (uniform)
+#pragma unroll
+            for (int k = 0; k < kKW; ++k)
+                qf[k] = __builtin_bit_cast(bf16x8_t, __builtin_bit_cast(u32x4_t, qf[k]) ^ 0x80008000u);
+        }
+        const float sc = fmaxf(fabsf(scale_log2), 1.17549435e-38f);
 
         float m_run = kNegInf;  // running max of this lane's head (log2 units)
         float l_run = 0.f;      // this lane's share of its running sum
@@ -547,13 +557,14 @@ void latent_partition_kernel(uint16_t *__restrict__ out, float *__restrict__ ws_
         // Register j of s: token 8 (j >> 2) + 4 hk + (j & 3) of the unit;
         // tokens at or past seg_lim are masked, so the score chain that runs
         // past a segment's last unit changes nothing here.  Pieces: 0..3
-        // scale registers 4k .. 4k + 3; 4 masks (only a unit that reaches the
-        // segment's limit, its last or one past it, holds tokens to mask); 5..8
-        // the running max over registers 4(k - 5) .. + 3; 9 the other 16
-        // tokens of the head, in lane ^ 32; 10 the running max and the rescale
-        // decision; 11..26 one probability each (register k - 11), the second
-        // of a pair packing the pair, adding both rounded values to the running
-        // sum and, every fourth pair, writing a P^T fragment.
+        // empty (they keep the pieces' spacing among the value products); 4
+        // masks (only a unit that reaches the segment's limit, its last or one
+        // past it, holds tokens to mask); 5..8 the max of the raw scores over
+        // registers 4(k - 5) .. + 3; 9 the other 16 tokens of the head, in
+        // lane ^ 32; 10 the scaled block max, the running max and the rescale
+        // decision; 11..26 one probability 2^(sc s - m) each (register k - 11),
+        // the second of a pair packing the pair, adding both rounded values to
+        // the running sum and, every fourth pair, writing a P^T fragment.
         constexpr int kSub = 27;
         bool moved = false;
         float bmax = kNegInf;
@@ -562,8 +573,7 @@ void latent_partition_kernel(uint16_t *__restrict__ out, float *__restrict__ ws_
         auto softmax_sub = [&](f32x16_t &s, int u, int k) {
             const int tok0 = seg_tok0 + u * kUnitTok;
             if (k < 4) {
-#pragma unroll
-                for (int j = 4 * k; j < 4 * k + 4; ++j) s[j] *= scale_log2;
+                // (nothing: the scale is applied inside the exponentials)
             } else if (k == 4) {
                 if (__builtin_expect(tok0 + kUnitTok > seg_lim, 0)) {  // (uniform)
 #pragma unroll
@@ -582,9 +592,10 @@ void latent_partition_kernel(uint16_t *__restrict__ out, float *__restrict__ ws_
                 const auto r = __builtin_amdgcn_permlane32_swap(as_u(bmax), as_u(bmax), false, false);
                 bmax = fmaxf(as_f(r[0]), as_f(r[1]));
             } else if (k == 10) {
-                moved = __builtin_amdgcn_ballot_w64(bmax > m_run + kLSlack) != 0;
+                const float bs = bmax * sc;  // the block max, scaled
+                moved = __builtin_amdgcn_ballot_w64(bs > m_run + kLSlack) != 0;
                 if (moved) {
-                    const float m_new = fmaxf(m_run, bmax);
+                    const float m_new = fmaxf(m_run, bs);
                     const float alpha = exp2_fast(m_run - m_new);
                     l_run *= alpha;
                     m_run = m_new;
@@ -594,9 +605,9 @@ void latent_partition_kernel(uint16_t *__restrict__ out, float *__restrict__ ws_
             } else {
                 const int jj = k - 11, v = jj >> 1, sv = v >> 2, e = v & 3;
                 if ((jj & 1) == 0) {
-                    pe = exp2_fast(s[jj] - m_run);
+                    pe = exp2_fast(fmaf(s[jj], sc, -m_run));
                 } else {
-                    w4[e] = pack_bf16(pe, exp2_fast(s[jj] - m_run));
+                    w4[e] = pack_bf16(pe, exp2_fast(fmaf(s[jj], sc, -m_run)));
                     l_run = dot2_bf16(w4[e], 0x3F803F80u, l_run);  // + both rounded values (bf16 1, 1)
                     if (e == 3)
                         *(__attribute__((address_space(3))) u32x4_t *)(uintptr_t)(

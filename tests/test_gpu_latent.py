@@ -61,6 +61,18 @@ def test_latent_rescale_heavy(dev):
     assert stats["max_abs"] <= floor + 2e-3
 
 
+@pytest.mark.parametrize("scale", [0.0, -SCALE])
+def test_latent_zero_and_negative_scale(dev, scale):
+    """The scale is applied inside the exponentials with the max taken over
+    the raw scores: a negative scale negates q instead (here the mirror of
+    the usual 1/sqrt(576)), and zero gives the plain mean of the values
+    (uniform weights)."""
+    say(f"case: latent, scale {scale}")
+    w = make_workload(_spec(128, [1, 100, 333, 64], scale=scale), seed=13)
+    d = to_device(w, dev)
+    say(f"  {compare(d.decode(), oracle.decode_workload(w), 'bf16')}")
+
+
 def test_latent_context_one_is_v_bitwise(dev):
     say("case: latent ctx=1")
     w = make_workload(_spec(128, [1, 1, 1]), seed=4)
