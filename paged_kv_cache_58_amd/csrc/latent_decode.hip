@@ -353,15 +353,22 @@ void latent_partition_kernel(uint16_t *__restrict__ out, float *__restrict__ ws_
     // (qq, hk, i >> 2) only; the chunk is 16 (dt >> 2) + 4 (dt & 3) + c0 with
     // c0 = 2 (g & 1) + ((i & 3) >> 1) < 4, so the offset in a row is
     // 256 (dt >> 2) + (64 (dt & 3) ^ vy[qq]) with vy = 16 (c0 ^ swm(row)).
-    uint32_t vrow[2], vy[2];
+    // With DT = 4 dim tiles per wave, dt = dg & 3 and dg >> 2 = wave, so the
+    // lane's part of the address of (qq, dt) is one of 8 values, formed once:
+    // vofs[qq][dt] = row offset + ((64 dt) ^ vy[qq]); a read then adds the
+    // unit's slot and 256 wave (uniform) and takes 16 s rows as an immediate.
+    static_assert(kDimTiles / kLatentNW == 4, "four dim tiles per wave");
+    uint32_t vofs[2][4];
     {
         const int i = lane & 15;
         const int c0 = 2 * ((lane >> 4) & 1) + ((i & 3) >> 1);
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq) {
             const int trow = 8 * qq + 4 * hk + (i >> 2);
-            vrow[qq] = trow * kMainRowB + 8 * (i & 1);
-            vy[qq] = 16u * static_cast<uint32_t>(c0 ^ swm(trow));
+            const uint32_t vrow = trow * kMainRowB + 8 * (i & 1);
+            const uint32_t vy = 16u * static_cast<uint32_t>(c0 ^ swm(trow));
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) vofs[qq][dt] = vrow + ((64u * dt) ^ vy);
         }
     }
     // P^T fragment (buffer, head tile ht, k-step s) of this lane: 16 bytes
@@ -497,10 +504,8 @@ void latent_partition_kernel(uint16_t *__restrict__ out, float *__restrict__ ws_
             return s_ids[(n >> 6) & 1][n & (kWave - 1)];
         };
 
-        // A operand of score k-step ks of unit u (the compiler keeps the lane's
-        // 12 row offsets live; the V^T reads below recompute theirs at each use,
-        // where an empty asm hides the lane's terms, to stay in the register
-        // budget)
+        // A operand of score k-step ks of unit u (the lane's 12 row offsets
+        // stay live, as do the 8 of the V^T reads below)
         // (local step k of this wave's split; its main steps start at a
         // multiple of 8, so their chunk term stays a constant)
         // The 8 main and kRopePer RoPE lane addresses of a unit are formed once
@@ -521,11 +526,7 @@ void latent_partition_kernel(uint16_t *__restrict__ out, float *__restrict__ ws_
         };
         // V^T operand (k-step s, this wave's dim tile dt, half qq) of unit u
         auto pv_read = [&](int u, int s, int dt, int qq) {
-            const int dg = DT * wave + dt;  // global dim tile
-            uint32_t y = vy[qq];
-            asm volatile("" : "+v"(y));
-            return ds_read_tr(main_slot(u) + (16 * s) * kMainRowB + 256 * (dg >> 2) + vrow[qq] +
-                              ((64u * (dg & 3)) ^ y));
+            return ds_read_tr(main_slot(u) + 256 * wave + vofs[qq][dt] + (16 * s) * kMainRowB);
         };
 
         // The score chain over k-steps [k0, k1) into s, of the unit whose
