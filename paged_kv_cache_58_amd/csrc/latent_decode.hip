@@ -525,8 +525,10 @@ void latent_partition_kernel(uint16_t *__restrict__ out, float *__restrict__ ws_
             return ds_read_b128(k < kMainPer ? qb_main[k & 7] + 256 * (k >> 3) : qb_rope[k - kMainPer]);
         };
         // V^T operand (k-step s, this wave's dim tile dt, half qq) of unit u
+        uint32_t vbase[2][4];  // this unit's V^T read bases (set by value_prefetch)
         auto pv_read = [&](int u, int s, int dt, int qq) {
-            return ds_read_tr(main_slot(u) + 256 * wave + vofs[qq][dt] + (16 * s) * kMainRowB);
+            (void)u;
+            return ds_read_tr(vbase[qq][dt] + (16 * s) * kMainRowB);
         };
 
         // The score chain over k-steps [k0, k1) into s, of the unit whose
@@ -629,6 +631,10 @@ void latent_partition_kernel(uint16_t *__restrict__ out, float *__restrict__ ws_
         bf16x8_t pb[HT];
         bf16x8_t va;
         auto value_prefetch = [&](int u) {
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) vbase[qq][dt] = main_slot(u) + 256 * wave + vofs[qq][dt];
 #pragma unroll
             for (int i = 0; i < kVR; ++i) {
                 vlo[i] = pv_read(u, i / DT, i % DT, 0);
